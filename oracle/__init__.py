@@ -1,0 +1,199 @@
+"""fp64 CPU oracle of the Gated Residual read/write path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (``write_gr_read_amd``)
+never does.  The arithmetic lives in ``gr_oracle.c`` (plain loops, fp64,
+built with ``-O2 -ffp-contract=off``); this file only marshals numpy arrays.
+
+Functions take and return float64 numpy arrays holding the exact stored values
+(a bfloat16 or float32 input widened to float64 is exact).  Storage dtypes:
+"f32", "bf16", or "f64" (no rounding at store points, for closed-form checks).
+
+Every function follows a passage of the pages:
+  read / write / fused  -- "Paper reading: Qwen3.8 Flash Next", part 2
+                           (Residual), sec. 4 Gated Residual, eq:rms, eq:gate,
+                           eq:use_gate, eq:s, eq:write; sec. 7 for the fusion.
+  add_rmsnorm           -- "Residual" (LLM inference), sec. 3.3.
+  chain                 -- the same page of the paper reading, sec. 4 (one GR
+                           module around each sublayer) and sec. 6 (each branch
+                           accumulates the writes, eq:rcv).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gr_oracle.c")
+_LIB = os.path.join(_HERE, "libgr_oracle.so")
+_DT = {"f32": 0, "bf16": 1, "f64": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64, I, D = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.gro_read.argtypes = [I64, I, I, I, D, I, P, P, P, P, P, P, P, P, P]
+        lib.gro_write.argtypes = [I64, I, I, I, P, P, P]
+        lib.gro_fused.argtypes = [I64, I, I, I, D, I, P, P, P, P, P, P, P, P, P]
+        lib.gro_add_rmsnorm.argtypes = [I64, I, D, I, P, P, P, P]
+        lib.gro_tanh_standin.argtypes = [I64, I, P, P]
+        lib.orc_round_bf16.argtypes = [D]
+        lib.orc_round_bf16.restype = D
+        for f in (lib.gro_read, lib.gro_write, lib.gro_fused, lib.gro_add_rmsnorm,
+                  lib.gro_tanh_standin):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None) -> np.ndarray:
+    """float64, C-contiguous copy of a numpy array or CPU torch tensor."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu").double().numpy()
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None:
+        a = a.reshape(shape)
+    return a
+
+
+def _p(a) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc: int, name: str):
+    if rc != 0:
+        raise ValueError(f"oracle {name} rejected its arguments")
+
+
+def round_bf16(x: float) -> float:
+    return _load().orc_round_bf16(float(x))
+
+
+def read(R, gamma, w_down, w_up, w_write, eps: float = 1e-6, dtype: str = "bf16",
+         detail: bool = False):
+    """GR read: returns (u [N,d], s [N,n]) and, with ``detail``, (rho, G)."""
+    R = _f64(R)
+    N, n, d = R.shape
+    gamma = _f64(gamma, (n, d))
+    r = 0 if w_down is None else int(np.shape(w_down)[0])
+    wd = _f64(w_down, (r, n * d)) if r else None
+    wu = _f64(w_up, (n * d, r)) if r else None
+    ww = _f64(w_write, (n, n * d))
+    u = np.empty((N, d))
+    s = np.empty((N, n))
+    rho = np.empty((N, n)) if detail else None
+    G = np.empty((N, n, d)) if detail else None
+    _check(_load().gro_read(N, n, d, r, eps, _DT[dtype], _p(R), _p(gamma), _p(wd), _p(wu),
+                            _p(ww), _p(u), _p(s), _p(rho), _p(G)), "read")
+    return (u, s, rho, G) if detail else (u, s)
+
+
+def write(R, y, s, dtype: str = "bf16") -> np.ndarray:
+    """GR write: returns R' = R + s_i y per branch (a new array)."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    s = _f64(s, (N, n))
+    _check(_load().gro_write(N, n, d, _DT[dtype], _p(R), _p(y), _p(s)), "write")
+    return R
+
+
+def fused(R, y, s_in, gamma, w_down, w_up, w_write, eps: float = 1e-6,
+          dtype: str = "bf16"):
+    """Write of sublayer l then read of sublayer l+1: returns (R', u, s_out)."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    s_in = _f64(s_in, (N, n))
+    gamma = _f64(gamma, (n, d))
+    r = 0 if w_down is None else int(np.shape(w_down)[0])
+    wd = _f64(w_down, (r, n * d)) if r else None
+    wu = _f64(w_up, (n * d, r)) if r else None
+    ww = _f64(w_write, (n, n * d))
+    u = np.empty((N, d))
+    s = np.empty((N, n))
+    _check(_load().gro_fused(N, n, d, r, eps, _DT[dtype], _p(R), _p(y), _p(s_in), _p(gamma),
+                             _p(wd), _p(wu), _p(ww), _p(u), _p(s)), "fused")
+    return R, u, s
+
+
+def add_rmsnorm(x, y, w, eps: float = 1e-6, dtype: str = "bf16"):
+    """n = 1 fused residual add + RMSNorm: returns (h, out)."""
+    x = _f64(x).copy()
+    N, d = x.shape
+    y = _f64(y, (N, d))
+    w = _f64(w, (d,))
+    out = np.empty((N, d))
+    _check(_load().gro_add_rmsnorm(N, d, eps, _DT[dtype], _p(x), _p(y), _p(w), _p(out)),
+           "add_rmsnorm")
+    return x, out
+
+
+def tanh_standin(u, dtype: str = "bf16") -> np.ndarray:
+    """The chained workload's elementwise sublayer: y = 0.1 tanh(u)."""
+    u = _f64(u)
+    y = np.empty_like(u)
+    _check(_load().gro_tanh_standin(u.size, _DT[dtype], _p(u), _p(y)), "tanh_standin")
+    return y
+
+
+def chain(X0, params: Sequence, eps: float = 1e-6, dtype: str = "bf16",
+          record: bool = False):
+    """A stack of len(params) sublayers, each read -> F -> write, where F is the
+    stand-in y = 0.1 tanh(u) and consecutive write/read pairs are fused.
+
+    ``params`` holds objects with gamma / w_down / w_up / w_write.  Returns the
+    final state and, with ``record``, the lists of (s, y) that were written.
+    """
+    R = _f64(X0).copy()
+    ss: List[np.ndarray] = []
+    ys: List[np.ndarray] = []
+    p0 = params[0]
+    u, s = read(R, p0.gamma, p0.w_down, p0.w_up, p0.w_write, eps, dtype)
+    y = tanh_standin(u, dtype)
+    for p in params[1:]:
+        if record:
+            ss.append(s); ys.append(y)
+        R, u, s = fused(R, y, s, p.gamma, p.w_down, p.w_up, p.w_write, eps, dtype)
+        y = tanh_standin(u, dtype)
+    if record:
+        ss.append(s); ys.append(y)
+    R = write(R, y, s, dtype)
+    return (R, ss, ys) if record else R
+
+
+def parallel_tokens(fn, arrays_by_token: Sequence[np.ndarray], threads: int, **kw):
+    """Run ``fn`` over disjoint token ranges in ``threads`` threads (ctypes
+    releases the GIL).  Tokens are independent, so results equal one call."""
+    N = arrays_by_token[0].shape[0]
+    threads = max(1, min(threads, N))
+    bounds = np.linspace(0, N, threads + 1).astype(int)
+    def run(k):
+        lo, hi = bounds[k], bounds[k + 1]
+        return fn(*[a[lo:hi] for a in arrays_by_token], **kw)
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(run, range(threads)))

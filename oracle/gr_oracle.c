@@ -1,0 +1,209 @@
+/*
+ * gr_oracle.c -- TEST INFRASTRUCTURE, not part of the product.
+ *
+ * A plain, slow, single-threaded fp64 evaluation of the Gated Residual (GR)
+ * read and write, of the fused write+read, and of the n = 1 fused residual
+ * add + RMSNorm.  It exists to judge the HIP path; only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * Sources (cited by page title and section / equation):
+ *   [QFN]  "Paper reading: Qwen3.8 Flash Next" (wkq9411.github.io), part 2
+ *          "Residual", section 4 "Gated Residual (GR)": eq:rms, eq:gate,
+ *          eq:use_gate, eq:s, eq:write.
+ *   [NOTES] "Qwen3.8-Flash-Next architecture notes, 06 Residual"
+ *          (cbphcr.github.io), section 2 (GR read) and section 3 (GR write):
+ *          the same equations restated with n_r = 4.
+ *   [RES]  "Residual" (rainlin-net.pages.dev, LLM inference), section 2.2
+ *          (Pre-Norm) and section 3.3 (fused residual add + RMSNorm).
+ *
+ * Conventions adopted where the pages leave a point open:
+ *   - RMSNorm(x; g)_c = g_c * x_c / sqrt(mean(x^2) + eps), eps inside the root;
+ *     g is the effective gain (a zero-centred model passes 1 + g).
+ *   - vec() stacks branches: vec index of (branch i, channel c) is i*d + c;
+ *     W_down is [r][n*d], W_up is [n*d][r], W_write is [n][n*d], row-major.
+ *   - r == 0 means a unit gate (G == 1); W_write == NULL means s == 1.
+ *   - All arithmetic is fp64.  Results are rounded to the storage dtype only
+ *     where the path stores them: the state, u, and (for the chain) F's y;
+ *     s is rounded to fp32.  Storage dtype 2 ("f64") skips that rounding, for
+ *     exact closed-form checks.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+
+/* Largest finite bfloat16: (2 - 2^-7) * 2^127. */
+#define ORC_BF16_MAX 3.3895313892515355e38
+
+/* Round x to the nearest bfloat16 (8 significant bits, fp32 exponent range),
+ * ties to even.  Below 2^-126 the spacing is the fixed subnormal step 2^-133. */
+double orc_round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);                  /* |x| in [2^(e-1), 2^e) */
+    int q = e - 8;                 /* spacing of 8-bit significands there */
+    if (q < -133) q = -133;
+    double y = ldexp(nearbyint(ldexp(x, -q)), q);   /* nearbyint: ties-to-even */
+    if (fabs(y) > ORC_BF16_MAX) return copysign(INFINITY, x);
+    return y;
+}
+
+/* Round x to the nearest fp32 (C conversion under the default rounding mode). */
+double orc_round_f32(double x) { return (double)(float)x; }
+
+static double store_round(double x, int dtype)
+{
+    if (dtype == ORC_BF16) return orc_round_bf16(x);
+    if (dtype == ORC_F32) return orc_round_f32(x);
+    return x;
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+static double silu(double x) { return x * sigmoid(x); }
+
+/*
+ * GR read for N tokens  [QFN eq:rms, eq:gate, eq:use_gate, eq:s; NOTES sec. 2-3].
+ *
+ *   R      [N][n][d]   state (exact stored values)
+ *   gamma  [n][d]      per-branch RMSNorm gains
+ *   wd     [r][n*d]    down projection (NULL iff r == 0)
+ *   wu     [n*d][r]    up projection   (NULL iff r == 0)
+ *   ww     [n][n*d]    write projection, or NULL for unit write strengths
+ *   u      [N][d]      out: sublayer input x (rounded to the storage dtype)
+ *   s      [N][n]      out: write strengths (rounded to fp32); may be NULL
+ *   rho    [N][n]      out (optional): 1/rms of each branch
+ *   gate   [N][n][d]   out (optional): G
+ * Returns 0, or -1 on bad sizes / allocation failure.
+ */
+int gro_read(int64_t N, int n, int d, int r, double eps, int dtype,
+             const double *R, const double *gamma, const double *wd,
+             const double *wu, const double *ww, double *u, double *s,
+             double *rho, double *gate)
+{
+    if (N < 0 || n < 1 || d < 1 || r < 0) return -1;
+    if (r > 0 && (!wd || !wu)) return -1;
+    const int64_t nd = (int64_t)n * d;
+    double *vhat = malloc(sizeof(double) * nd);      /* vec(R-hat) */
+    double *g = malloc(sizeof(double) * nd);         /* G, vec order */
+    double *a = malloc(sizeof(double) * (r > 0 ? r : 1));
+    double *rh = malloc(sizeof(double) * n);
+    if (!vhat || !g || !a || !rh) { free(vhat); free(g); free(a); free(rh); return -1; }
+
+    for (int64_t t = 0; t < N; ++t) {
+        const double *Rt = R + t * nd;
+        /* eq:rms -- each branch normalised on its own, with its own gain. */
+        for (int i = 0; i < n; ++i) {
+            double ss = 0.0;
+            for (int c = 0; c < d; ++c) ss += Rt[i * d + c] * Rt[i * d + c];
+            rh[i] = 1.0 / sqrt(ss / d + eps);
+            for (int c = 0; c < d; ++c)
+                vhat[i * d + c] = gamma[i * d + c] * Rt[i * d + c] * rh[i];
+        }
+        /* eq:gate -- G = unvec sigmoid(W_up SiLU((1/n) W_down vec(R-hat))). */
+        if (r > 0) {
+            for (int k = 0; k < r; ++k) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < nd; ++j) acc += wd[k * nd + j] * vhat[j];
+                a[k] = silu(acc / n);
+            }
+            for (int64_t j = 0; j < nd; ++j) {
+                double acc = 0.0;
+                for (int k = 0; k < r; ++k) acc += wu[j * r + k] * a[k];
+                g[j] = sigmoid(acc);
+            }
+        } else {
+            for (int64_t j = 0; j < nd; ++j) g[j] = 1.0;
+        }
+        /* eq:use_gate -- x = (1/n) sum_i G_i (.) R-hat_i. */
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i) acc += g[i * d + c] * vhat[i * d + c];
+            u[t * d + c] = store_round(acc / n, dtype);
+        }
+        /* eq:s -- s = 2 sigmoid((1/n) W_write vec(R-hat)). */
+        if (s) {
+            for (int i = 0; i < n; ++i) {
+                double val = 1.0;
+                if (ww) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < nd; ++j) acc += ww[i * nd + j] * vhat[j];
+                    val = 2.0 * sigmoid(acc / n);
+                }
+                s[t * n + i] = dtype == ORC_F64 ? val : orc_round_f32(val);
+            }
+        }
+        if (rho) for (int i = 0; i < n; ++i) rho[t * n + i] = rh[i];
+        if (gate) memcpy(gate + t * nd, g, sizeof(double) * nd);
+    }
+    free(vhat); free(g); free(a); free(rh);
+    return 0;
+}
+
+/*
+ * GR write for N tokens  [QFN eq:write; NOTES sec. 3]:
+ *   R'_i = R_i + s_i * y, the same y into every branch, stored in place.
+ *   R [N][n][d] in/out, y [N][d], s [N][n].
+ */
+int gro_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
+              const double *s)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    for (int64_t t = 0; t < N; ++t)
+        for (int i = 0; i < n; ++i)
+            for (int c = 0; c < d; ++c) {
+                double *p = R + (t * n + i) * (int64_t)d + c;
+                *p = store_round(*p + s[t * n + i] * y[t * d + c], dtype);
+            }
+    return 0;
+}
+
+/*
+ * Fused write of one sublayer followed by the read of the next
+ * [QFN sec. 2.7 (one traversal per direction), eq:write then eq:rms..eq:s]:
+ * the write is completed and stored first; the read then sees the stored R'.
+ */
+int gro_fused(int64_t N, int n, int d, int r, double eps, int dtype, double *R,
+              const double *y, const double *s_in, const double *gamma,
+              const double *wd, const double *wu, const double *ww, double *u,
+              double *s_out)
+{
+    int rc = gro_write(N, n, d, dtype, R, y, s_in);
+    if (rc) return rc;
+    return gro_read(N, n, d, r, eps, dtype, R, gamma, wd, wu, ww, u, s_out, NULL, NULL);
+}
+
+/*
+ * n = 1 fused residual add + RMSNorm  [RES sec. 3.3]:
+ *   h = x + y (stored in place of x), out = w (.) h / sqrt(mean(h^2) + eps),
+ *   the norm taken over the stored h.  x, y, out [N][d], w [d].
+ */
+int gro_add_rmsnorm(int64_t N, int d, double eps, int dtype, double *x,
+                    const double *y, const double *w, double *out)
+{
+    if (N < 0 || d < 1) return -1;
+    for (int64_t t = 0; t < N; ++t) {
+        double *h = x + t * d;
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) {
+            h[c] = store_round(h[c] + y[t * d + c], dtype);
+            ss += h[c] * h[c];
+        }
+        double inv = 1.0 / sqrt(ss / d + eps);
+        for (int c = 0; c < d; ++c) out[t * d + c] = store_round(w[c] * h[c] * inv, dtype);
+    }
+    return 0;
+}
+
+/* Elementwise sublayer stand-in of the chained workload: y = 0.1 tanh(u). */
+int gro_tanh_standin(int64_t count, int dtype, const double *u, double *y)
+{
+    if (count < 0) return -1;
+    for (int64_t k = 0; k < count; ++k) y[k] = store_round(0.1 * tanh(u[k]), dtype);
+    return 0;
+}
