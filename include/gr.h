@@ -1,0 +1,152 @@
+/*
+ * gr.h -- C ABI of the MI355X (gfx950) Gated Residual read/write library.
+ *
+ * Gated Residual (GR) keeps n branch states per token, R in R^{n x d}.  Around
+ * each sublayer F it performs
+ *   read : R-hat_i = RMSNorm(R_i; gamma_i)                              eq:rms
+ *          G = unvec sigmoid(W_up SiLU((1/n) W_down vec(R-hat)))        eq:gate
+ *          u = (1/n) sum_i G_i (.) R-hat_i      (the sublayer input)     eq:use_gate
+ *          s = 2 sigmoid((1/n) W_write vec(R-hat))  (write strengths)    eq:s
+ *   F    : y = F(u), once, outside this library
+ *   write: R'_i = R_i + s_i y                                             eq:write
+ * ("Paper reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4 Gated
+ * Residual; restated in "Qwen3.8-Flash-Next architecture notes, 06 Residual",
+ * sec. 2 and 3).  The pages fuse the read into one kernel and the write into
+ * another (same paper reading, sec. 7).  This library computes s inside the
+ * read (it depends only on R-hat, which the read holds) and hands it to the
+ * write, and adds a fused write(l)+read(l+1) call so the widened state makes
+ * one HBM round trip per sublayer.  The n = 1 degenerate case is the fused
+ * residual add + RMSNorm of "Residual" (LLM inference), sec. 3.3.
+ *
+ * Conventions shared by every call
+ *   Memory     All tensor pointers are DEVICE pointers owned by the caller;
+ *              the library keeps no reference after a call returns.  Scratch
+ *              memory comes only from the caller's workspace argument.
+ *   Layout     Contiguous, row-major: state [N][n][d] (token, branch,
+ *              channel); y, u [N][d]; s [N][n] (always fp32); gamma [n][d];
+ *              W_down [r][n*d]; W_up [n*d][r]; W_write [n][n*d].  The vec()
+ *              index of (branch i, channel c) is i*d + c.  Weights and gamma
+ *              have the state dtype.
+ *   Alignment  Every pointer 16-byte aligned; d a multiple of 8 (bf16) or 4
+ *              (fp32).
+ *   Sizes      1 <= n <= 8, d >= 1, 0 <= r <= 512, N >= 0.  r == 0 means a
+ *              unit gate (G == 1).  W_write == NULL means s == 1 (the value
+ *              of 2 sigmoid(0)).  eps is added inside the square root.
+ *   N == 0     A no-op returning GR_SUCCESS (pointers are not inspected).
+ *   Aliasing   No two arguments may overlap, except out == y in
+ *              residual_add_rmsnorm.
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *              are asynchronous; a fault inside a kernel surfaces at the
+ *              caller's next synchronisation.
+ *   Errors     Argument errors are detected on the host before any HIP call
+ *              and return GR_ERROR_INVALID_VALUE / GR_ERROR_NOT_SUPPORTED /
+ *              GR_ERROR_WORKSPACE; a failed launch returns GR_ERROR_LAUNCH.
+ *              gr_last_error() gives a message for the calling thread.
+ *              No call aborts the process.
+ *   Threads    Calls are stateless and may be made from several threads.
+ */
+#ifndef GR_H
+#define GR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gr_dtype {
+    GR_F32 = 0,   /* fp32 state and weights, fp32 arithmetic */
+    GR_BF16 = 1   /* bf16 state and weights, fp32 accumulation */
+} gr_dtype;
+
+typedef enum gr_status {
+    GR_SUCCESS = 0,
+    GR_ERROR_INVALID_VALUE = 1,  /* bad pointer, size, dtype or alignment */
+    GR_ERROR_NOT_SUPPORTED = 2,  /* valid but outside what the kernels handle */
+    GR_ERROR_LAUNCH = 3,         /* the HIP runtime refused a launch */
+    GR_ERROR_WORKSPACE = 4       /* workspace smaller than gr_workspace_size() */
+} gr_status;
+
+/* One GR module's parameters (device pointers, state dtype). */
+typedef struct gr_layer {
+    int32_t n;             /* branches, 1..8 */
+    int32_t d;             /* width of each branch and of the sublayer */
+    int32_t r;             /* gate rank, 0..512 (0 = unit gate) */
+    float eps;             /* RMSNorm epsilon (>= 0, finite) */
+    const void *gamma;     /* [n][d]    effective per-branch gains */
+    const void *w_down;    /* [r][n*d]  NULL iff r == 0 */
+    const void *w_up;      /* [n*d][r]  NULL iff r == 0 */
+    const void *w_write;   /* [n][n*d]  or NULL (s == 1) */
+} gr_layer;
+
+/* Operation ids for gr_workspace_size. */
+enum { GR_OP_READ = 0, GR_OP_FUSED_WRITE_READ = 1 };
+
+/*
+ * gr_read -- the GR read (eq:rms, eq:gate, eq:use_gate) plus the write
+ * strengths of the same module (eq:s), which depend only on R-hat.
+ *   state  in  [N][n][d]  (not modified)
+ *   u      out [N][d]     sublayer input, state dtype
+ *   s      out [N][n]     fp32 write strengths for the later gr_write
+ *   workspace / ws_bytes  device scratch of at least
+ *                         gr_workspace_size(GR_OP_READ, ...) bytes
+ */
+gr_status gr_read(const void *state, gr_dtype dt, int64_t N, const gr_layer *L,
+                  void *u, float *s, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gr_write -- eq:write, in place: state[t][i][c] += s[t][i] * y[t][c],
+ * computed as one fp32 fused multiply-add and stored in the state dtype
+ * (round to nearest even).
+ *   state  in/out [N][n][d];  y in [N][d];  s in [N][n] fp32
+ */
+gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int64_t N,
+                   int32_t n, int32_t d, void *stream);
+
+/*
+ * gr_fused_write_read -- gr_write of sublayer l, then gr_read of sublayer
+ * l+1 with `next`, on the STORED (rounded) state, in one pass over it.
+ * Results equal gr_write followed by gr_read (state bit for bit).
+ *   state  in/out [N][n][d];  y in [N][d];  s_in in [N][n] fp32
+ *   u_next out [N][d];  s_next out [N][n] fp32
+ *   workspace >= gr_workspace_size(GR_OP_FUSED_WRITE_READ, ...) bytes
+ */
+gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_dtype dt,
+                              int64_t N, const gr_layer *next, void *u_next, float *s_next,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * residual_add_rmsnorm -- n = 1 fused residual add + RMSNorm ("Residual",
+ * LLM inference, sec. 3.3): h = x + y stored in place of x, then
+ * out = w (.) h / sqrt(mean(h^2) + eps), the mean taken over the stored h.
+ *   x in/out [N][d];  y in [N][d];  w in [d];  out out [N][d] (may equal y)
+ */
+gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
+                               gr_dtype dt, int64_t N, int32_t d, void *stream);
+
+/* Bytes of workspace `op` needs for N tokens of layer L (may be 0). */
+gr_status gr_workspace_size(int op, gr_dtype dt, int64_t N, const gr_layer *L, size_t *bytes);
+
+/* Static description of a status code. */
+const char *gr_status_string(gr_status status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *gr_last_error(void);
+
+/* ---- measurement support (not part of the GR method) ------------------ */
+
+/* The chained workload's elementwise sublayer stand-in: y = 0.1 tanh(u),
+ * computed in fp32 and stored in the state dtype.  u, y [count]. */
+gr_status gr_bench_tanh_standin(const void *u, void *y, gr_dtype dt, int64_t count,
+                                void *stream);
+
+/* Streaming copy probe: dst[0..bytes) = src[0..bytes), 16-byte vectors.
+ * bytes must be a multiple of 16.  Measures attainable HBM bandwidth. */
+gr_status gr_bench_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GR_H */

@@ -1,0 +1,92 @@
+"""Parity helpers: compare GPU results with the fp64 oracle's.
+
+Tolerances (written here, used by every GPU parity test):
+  * fp32 state:  max |g - o| <= 1e-5 * RMS(o), per output tensor.
+  * bf16 state:  |g - o| <= 2e-2 * max(|o|, A, RMS(o)/16) element by element,
+    fp32 accumulation on the GPU.  A is the condition scale of the element:
+    for u, the sum of the absolute values of the terms of the n-branch
+    combine, (1/n) sum_i |G_i R-hat_i| (eq:use_gate); for a chained state,
+    |R^(0)| + sum_u |s^(u) y^(u)| (eq:rcv).  A comes from the oracle's own
+    intermediates.  Reason: a stored bf16 branch value may differ by one ulp
+    between the GPU (fp32 FMA, then round to bf16) and the oracle (exact
+    value rounded once), and a one-ulp change of a term moves a cancelling
+    sum by up to 2^-7 of that term.  Where no A is given the RMS(o)/16 floor
+    applies.  Also reported: max|g-o|/RMS(o) and the relative L2 error.
+  * chained bf16 state after L sublayers (check_chain): each stored value is
+    rounded L times, and a rounding decision that differs between the two
+    sides (a pre-rounding difference of 1e-7 lands on a bf16 rounding
+    boundary) moves that element by one ulp for good; such flips cascade
+    through y = F(u).  So: every element within 6e-2 * max(|o|, A), at least
+    99.9 % of elements within 2e-2 * max(|o|, A), relative L2 error <= 2e-3.
+"""
+import numpy as np
+import torch
+
+
+def to64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu").double().numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def check(name: str, got, ref, dtype: str, rms=None, scale=None):
+    """Assert ``got`` (GPU) matches ``ref`` (oracle) at the stated tolerance.
+
+    ``rms`` overrides the RMS used for the floor (e.g. the RMS of the whole
+    output when only sampled tokens are compared); ``scale`` is the per-element
+    condition scale A (same shape as ``ref``)."""
+    g, o = to64(got), to64(ref)
+    assert g.shape == o.shape, f"{name}: shape {g.shape} vs {o.shape}"
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
+    if g.size == 0:
+        return {}
+    rms = float(np.sqrt(np.mean(o * o))) if rms is None else float(rms)
+    err = np.abs(g - o)
+    stats = {"max_abs": float(err.max()), "max_over_rms": float(err.max() / max(rms, 1e-300)),
+             "rel_l2": float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-300))}
+    if dtype == "f32":
+        assert err.max() <= 1e-5 * rms, f"{name}: fp32 max err {err.max():.3e} > 1e-5*RMS {rms:.3e}"
+    else:
+        mag = np.maximum(np.abs(o), rms / 16)
+        if scale is not None:
+            mag = np.maximum(mag, to64(scale))
+        bound = 2e-2 * mag
+        bad = err > bound
+        if bad.any():
+            k = int(np.argmax(err / bound))
+            idx = np.unravel_index(k, err.shape)
+            raise AssertionError(f"{name}: {int(bad.sum())} elements outside 2e-2 rel (worst at "
+                                 f"{idx}: gpu {g[idx]!r} oracle {o[idx]!r}); stats {stats}")
+    return stats
+
+
+def sample_tokens(N: int, k: int, seed: int = 0) -> np.ndarray:
+    """A sorted sample of k token indices including the first and last ones."""
+    if N <= k:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(2, N - 2), size=k - 4, replace=False)
+    return np.unique(np.concatenate([[0, 1, N - 2, N - 1], mid]))
+
+
+def combine_scale(R, gamma, rho, G) -> np.ndarray:
+    """A for u: (1/n) sum_i |G_i (.) gamma_i (.) R_i| rho_i, from the oracle's
+    stored state R [N,n,d], gains, 1/rms per branch and gate G."""
+    R, gamma, rho, G = to64(R), to64(gamma), to64(rho), to64(G)
+    n = R.shape[1]
+    return np.abs(G * gamma[None] * R * rho[:, :, None]).sum(1) / n
+
+
+def check_chain(name: str, got, ref, scale):
+    """The chained-state criterion stated in the module docstring."""
+    g, o, A = to64(got), to64(ref), to64(scale)
+    assert g.shape == o.shape == A.shape
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
+    q = np.abs(g - o) / np.maximum(np.abs(o), A)
+    rel_l2 = float(np.linalg.norm(g - o) / np.linalg.norm(o))
+    frac = float((q > 2e-2).mean())
+    stats = {"max_err_over_scale": float(q.max()), "frac_over_2e-2": frac, "rel_l2": rel_l2}
+    assert q.max() <= 6e-2, f"{name}: element off by {q.max():.3e} of its scale; {stats}"
+    assert frac <= 1e-3, f"{name}: {frac:.2e} of elements beyond 2e-2; {stats}"
+    assert rel_l2 <= 2e-3, f"{name}: relative L2 error {rel_l2:.2e}; {stats}"
+    return stats

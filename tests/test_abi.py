@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/gr.h declares, and rejects bad arguments on the host before any
+HIP call (so none of these tests launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import write_gr_read_amd as gr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gr.h")
+
+INVALID, NOT_SUPPORTED, LAUNCH, WORKSPACE = 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gr.library_path()):
+        pytest.skip("libgr.so not built")
+    return gr.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("gr_read", "gr_write", "gr_fused_write_read", "residual_add_rmsnorm",
+              "gr_workspace_size", "gr_status_string", "gr_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for f in declared_functions():
+        assert hasattr(L, f), f"libgr.so does not export {f}"
+
+
+def test_status_strings(L):
+    assert L.gr_status_string(0) == b"success"
+    assert L.gr_status_string(WORKSPACE) == b"workspace too small"
+    assert L.gr_status_string(99) == b"unknown status"
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced here
+MISALIGNED = FAKE + 2
+
+
+def layer(n=4, d=64, r=8, eps=1e-6, gamma=FAKE, wd=FAKE, wu=FAKE, ww=FAKE):
+    return gr._Layer(n, d, r, eps, gamma, wd, wu, ww)
+
+
+def call_read(L, N=4, lay=None, state=FAKE, u=FAKE, s=FAKE, dt=1, ws=None, ws_bytes=0):
+    lay = layer() if lay is None else lay
+    return L.gr_read(state, dt, N, ctypes.byref(lay), u, s, ws, ws_bytes, None)
+
+
+def test_zero_tokens_is_a_noop(L):
+    assert call_read(L, N=0, state=None, u=None, s=None) == 0
+    assert L.gr_write(None, None, None, 1, 0, 4, 64, None) == 0
+    assert L.residual_add_rmsnorm(None, None, None, 1e-6, None, 1, 0, 64, None) == 0
+    assert L.gr_fused_write_read(None, None, None, 1, 0, None, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), INVALID),
+    (dict(dt=7), INVALID),
+    (dict(state=None), INVALID),
+    (dict(state=MISALIGNED), INVALID),
+    (dict(u=None), INVALID),
+    (dict(s=MISALIGNED), INVALID),
+    (dict(lay=layer(n=0)), INVALID),
+    (dict(lay=layer(n=9)), INVALID),
+    (dict(lay=layer(d=0)), INVALID),
+    (dict(lay=layer(d=12)), NOT_SUPPORTED),      # bf16 needs d % 8 == 0
+    (dict(lay=layer(r=-1)), INVALID),
+    (dict(lay=layer(r=513)), INVALID),
+    (dict(lay=layer(eps=-1.0)), INVALID),
+    (dict(lay=layer(eps=float("nan"))), INVALID),
+    (dict(lay=layer(gamma=None)), INVALID),
+    (dict(lay=layer(wd=None)), INVALID),
+    (dict(lay=layer(wu=MISALIGNED)), INVALID),
+    (dict(lay=layer(r=0)), INVALID),             # r == 0 requires no gate weights
+    (dict(lay=layer(ww=MISALIGNED)), INVALID),
+    (dict(N=1 << 31), NOT_SUPPORTED),
+])
+def test_read_rejects_bad_arguments(L, kw, code):
+    assert call_read(L, **kw) == code
+    assert L.gr_last_error() != b""
+
+
+def test_fp32_width_rule(L):
+    assert call_read(L, dt=0, lay=layer(d=6)) == NOT_SUPPORTED
+
+
+def test_write_and_addnorm_reject_bad_arguments(L):
+    assert L.gr_write(FAKE, FAKE, FAKE, 1, 4, 0, 64, None) == INVALID
+    assert L.gr_write(FAKE, FAKE, FAKE, 1, 4, 4, 60, None) == NOT_SUPPORTED
+    assert L.gr_write(FAKE, None, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.residual_add_rmsnorm(FAKE, FAKE, FAKE, -1.0, FAKE, 1, 4, 64, None) == INVALID
+    assert L.residual_add_rmsnorm(FAKE, FAKE, FAKE, 1e-6, FAKE, 1, 4, 64, None) == INVALID  # out == x
+    assert L.residual_add_rmsnorm(FAKE, FAKE, None, 1e-6, FAKE + 16, 1, 4, 64, None) == INVALID
+    assert L.gr_bench_copy(FAKE, FAKE, 17, None) == INVALID
+
+
+def test_workspace_query_and_check(L):
+    lay = layer(n=4, d=4096, r=64)
+    nbytes = ctypes.c_size_t(123)
+    assert L.gr_workspace_size(0, 1, 16384, ctypes.byref(lay), ctypes.byref(nbytes)) == 0
+    assert L.gr_workspace_size(5, 1, 16384, ctypes.byref(lay), ctypes.byref(nbytes)) == INVALID
+    assert L.gr_workspace_size(0, 1, 0, ctypes.byref(lay), ctypes.byref(nbytes)) == 0
+    assert nbytes.value == 0
+    need = ctypes.c_size_t(0)
+    L.gr_workspace_size(1, 1, 16384, ctypes.byref(lay), ctypes.byref(need))
+    if need.value > 0:
+        assert call_read(L, N=16384, lay=lay, ws=FAKE, ws_bytes=need.value - 16) == WORKSPACE
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_launch_failure_is_reported_without_a_gpu(L):
+    """With valid arguments but no GPU, the launch itself fails and is mapped
+    to GR_ERROR_LAUNCH with the runtime's message (host-forced error path)."""
+    st = L.gr_write(FAKE, FAKE + 4096, FAKE + 8192, 1, 4, 4, 64, None)
+    assert st == LAUNCH
+    assert b"launch failed" in L.gr_last_error()
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gr.residual_add_rmsnorm(x, x.clone(), torch.ones(64, dtype=torch.bfloat16))

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Same seeded inputs on both sides; sizes the oracle finishes in seconds that
+span several tiles plus ragged tails, and the full workload sizes on sampled
+tokens.  Tolerances are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import write_gr_read_amd as gr
+from write_gr_read_amd import inputs
+from parity import check, check_chain, combine_scale, sample_tokens, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_and_library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gr.lib()  # raises if the HIP library is missing: no silent fallback
+
+
+def dev_params(p):
+    return p.to(DEV)
+
+
+def orc_read(X, p, dtype, eps=1e-6):
+    """Oracle read; returns (u, s, A) with A the combine's condition scale."""
+    u, s, rho, G = oracle.read(X, p.gamma, p.w_down, p.w_up, p.w_write, eps, dtype, detail=True)
+    return u, s, combine_scale(X, p.gamma, rho, G)
+
+
+def orc_fused(X, y, s, p, dtype, eps=1e-6):
+    """Oracle fused write+read; returns (R', u, s, A)."""
+    R, u, s_out = oracle.fused(X, y, s, p.gamma, p.w_down, p.w_up, p.w_write, eps, dtype)
+    u2, s2, A = orc_read(R, p, dtype, eps)
+    assert np.array_equal(u, u2) and np.array_equal(s_out, s2)
+    return R, u, s_out, A
+
+
+def run_read_write_fused(Xin: inputs.GRInputs, label: str):
+    """read(P0), write, fused(P1) on the GPU vs the oracle, whole tensors."""
+    dt = Xin.dtype
+    p0, p1 = Xin.params[0], Xin.params[1]
+    X = Xin.X.to(DEV)
+    y = Xin.y.to(DEV)
+    # read
+    u0, s0 = gr.read(X, dev_params(p0))
+    ou0, os0, A0 = orc_read(Xin.X, p0, dt)
+    check(f"{label} read u", u0, ou0, dt, scale=A0)
+    check(f"{label} read s", s0, os0, dt)
+    # write with the oracle's strengths (same input on both sides)
+    s_in = torch.from_numpy(os0).float()
+    Xw = X.clone()
+    gr.write(Xw, y, s_in.to(DEV))
+    oRw = oracle.write(Xin.X, Xin.y, s_in.double().numpy(), dt)
+    check(f"{label} write state", Xw, oRw, dt)
+    # fused write + read of the next sublayer
+    Xf = X.clone()
+    u1, s1 = gr.fused_write_read(Xf, y, s_in.to(DEV), dev_params(p1))
+    oR, ou1, os1, A1 = orc_fused(Xin.X, Xin.y, s_in.double().numpy(), p1, dt)
+    check(f"{label} fused state", Xf, oR, dt)
+    check(f"{label} fused u", u1, ou1, dt, scale=A1)
+    check(f"{label} fused s", s1, os1, dt)
+    # the fused state is exactly the standalone write's
+    assert torch.equal(Xf, Xw), f"{label}: fused state differs from gr_write's"
+    torch.cuda.synchronize()
+
+
+def test_tiny_fp32_workload():
+    """Workload 1: N=64, d=256, n=4, r=16, fp32: read, write and fused."""
+    run_read_write_fused(inputs.workload(1), "tiny-f32")
+
+
+@pytest.mark.parametrize("N,n,d,r", [
+    (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (9, 2, 128, 1), (17, 3, 64, 5),
+    (3, 8, 32, 2), (70, 4, 512, 32), (130, 4, 1024, 48), (33, 4, 2048, 32), (64, 4, 256, 0),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_shapes(N, n, d, r, dtype):
+    """Off-workload shapes: several tiles, ragged token tails, n in 1..8,
+    r in {0, 1, 2, 5, ...}; both storage dtypes."""
+    X = inputs.make_gr_inputs(N, n, d, r, dtype, seed=N * 131 + n * 17 + d + r, w_std=0.05,
+                              branch_scale=None)
+    run_read_write_fused(X, f"N{N}-n{n}-d{d}-r{r}-{dtype}")
+
+
+def test_no_write_projection_gives_unit_strength():
+    X = inputs.make_gr_inputs(40, 4, 256, 16, "bf16", seed=41, with_write=False)
+    u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))
+    assert torch.all(s == 1.0)
+    ou, _, A = orc_read(X.X, X.params[0], "bf16")
+    check("no-write u", u, ou, "bf16", scale=A)
+
+
+def test_zero_write_projection_gives_exactly_one():
+    X = inputs.make_gr_inputs(40, 4, 512, 16, "bf16", seed=42)
+    p = X.params[0]
+    p.w_write = torch.zeros_like(p.w_write)
+    _, s = gr.read(X.X.to(DEV), dev_params(p))
+    assert torch.all(s == 1.0)
+
+
+def test_zero_strength_and_zero_output_are_identities():
+    X = inputs.make_gr_inputs(50, 4, 512, 16, "bf16", seed=43)
+    R = X.X.to(DEV)
+    y = X.y.to(DEV)
+    R1 = R.clone()
+    gr.write(R1, y, torch.zeros(50, 4, device=DEV))
+    assert torch.equal(R1, R)
+    R2 = R.clone()
+    gr.write(R2, torch.zeros_like(y), torch.rand(50, 4, device=DEV) * 2)
+    assert torch.equal(R2, R)
+    R3 = R.clone()
+    gr.fused_write_read(R3, y, torch.zeros(50, 4, device=DEV), dev_params(X.params[1]))
+    assert torch.equal(R3, R)
+
+
+def test_bf16_store_rounding_is_round_to_nearest_even():
+    """With s = 1, wherever the sum is exact in fp32 the stored state is exactly
+    torch's round-to-nearest-even bf16 of the sum (ties included)."""
+    X = inputs.make_gr_inputs(64, 4, 1024, 0, "bf16", seed=44, n_param_sets=0)
+    Rf, yf = X.X.float(), X.y.float()
+    f32_sum = Rf + yf[:, None, :]
+    exact = f32_sum.double() == X.X.double() + X.y.double()[:, None, :]
+    assert exact.float().mean().item() > 0.99
+    R = X.X.to(DEV)
+    gr.write(R, X.y.to(DEV), torch.ones(64, 4, device=DEV))
+    got = R.cpu()
+    want = f32_sum.to(torch.bfloat16)
+    assert bool((got.view(torch.int16) == want.view(torch.int16))[exact].all())
+
+
+def test_n1_gr_equals_add_rmsnorm():
+    """n = 1, unit gate, no write projection, s = 1: the fused GR call is the
+    fused residual add + RMSNorm."""
+    X = inputs.make_gr_inputs(300, 1, 4096, 0, "bf16", seed=45, with_write=False)
+    p = X.params[0]
+    R = X.X.to(DEV)
+    u, s = gr.fused_write_read(R, X.y.to(DEV), torch.ones(300, 1, device=DEV), dev_params(p))
+    x = X.X[:, 0].contiguous().to(DEV)
+    out = gr.residual_add_rmsnorm(x, X.y.to(DEV), p.gamma[0].contiguous().to(DEV))
+    assert torch.equal(R[:, 0], x)
+    check("n1 u vs addnorm", u, out, "bf16")
+    assert torch.all(s == 1.0)
+
+
+def test_deterministic():
+    X = inputs.make_gr_inputs(200, 4, 2048, 32, "bf16", seed=46)
+    outs = []
+    for _ in range(2):
+        R = X.X.to(DEV)
+        _, s0 = gr.read(R, dev_params(X.params[0]))
+        u, s = gr.fused_write_read(R, X.y.to(DEV), s0, dev_params(X.params[1]))
+        outs.append((R.cpu(), u.cpu(), s.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_outputs_stay_in_bounds():
+    """Outputs carved out of larger canary-filled buffers: nothing outside the
+    result regions changes."""
+    N, n, d, r = 45, 4, 512, 16
+    X = inputs.make_gr_inputs(N, n, d, r, "bf16", seed=47)
+    pad = 4096
+    canary = -1234.5
+    Rbuf = torch.full((pad + N * n * d + pad,), canary, dtype=torch.bfloat16, device=DEV)
+    ubuf = torch.full((pad + N * d + pad,), canary, dtype=torch.bfloat16, device=DEV)
+    sbuf = torch.full((pad + N * n + pad,), canary, dtype=torch.float32, device=DEV)
+    R = Rbuf[pad:pad + N * n * d].view(N, n, d)
+    R.copy_(X.X.to(DEV))
+    u = ubuf[pad:pad + N * d].view(N, d)
+    s = sbuf[pad:pad + N * n].view(N, n)
+    s_in = torch.ones(N, n, device=DEV)
+    gr.fused_write_read(R, X.y.to(DEV), s_in, dev_params(X.params[1]), u=u, s=s)
+    for buf, lo, hi in ((Rbuf, pad, pad + N * n * d), (ubuf, pad, pad + N * d),
+                        (sbuf, pad, pad + N * n)):
+        assert torch.all(buf[:lo] == canary) and torch.all(buf[hi:] == canary)
+
+
+# ---------------------------------------------------------------- the workloads
+
+def sampled_read_parity(Xin, idx, label, fused=True):
+    """Run the whole workload on the GPU; compare sampled tokens with the
+    oracle evaluated on just those tokens (GR is per token)."""
+    dt = Xin.dtype
+    p0, p1 = Xin.params[0], Xin.params[1]
+    X = Xin.X.to(DEV)
+    _, s0 = gr.read(X, dev_params(p0))
+    _, os0, _ = orc_read(Xin.X[idx], p0, dt)
+    check(f"{label} read s (sampled)", s0.cpu()[idx], os0, dt)
+    s_in = s0  # GPU strengths feed the GPU fused call; the oracle uses its own
+    u1, s1 = gr.fused_write_read(X, Xin.y.to(DEV), s_in, dev_params(p1))
+    oR, ou1, os1, A1 = orc_fused(Xin.X[idx], Xin.y[idx], os0, p1, dt)
+    Xc = X.cpu()
+    u1c = u1.cpu()
+    check(f"{label} fused state (sampled)", Xc[idx], oR, dt)
+    check(f"{label} fused u (sampled)", u1c[idx], ou1, dt, scale=A1)
+    check(f"{label} fused s (sampled)", s1.cpu()[idx], os1, dt)
+    assert torch.isfinite(u1c.float()).all() and torch.isfinite(Xc.float()).all()
+
+
+def test_prefill_workload_subset():
+    """Workload 3 (d=4096, n=4, r=64, per-branch scales 1, 0.5, 2, 1), first
+    1024 tokens, every token compared."""
+    run_read_write_fused(inputs.workload(3, N=1024), "prefill-1024")
+
+
+def test_prefill_workload_full_sampled():
+    """Workload 3 at its full size (N=16384), 96 sampled tokens."""
+    Xin = inputs.workload(3)
+    sampled_read_parity(Xin, sample_tokens(Xin.N, 96, seed=3), "prefill-16384")
+
+
+def test_decode_workload():
+    """Workload 4 (N=256), every token."""
+    run_read_write_fused(inputs.workload(4), "decode-256")
+
+
+def test_add_rmsnorm_workload():
+    """Workload 2 (n=1, N=8192, d=4096): full size, 128 sampled tokens, plus
+    a ragged small case compared whole."""
+    A = inputs.workload(2)
+    x = A.x.to(DEV)
+    out = gr.residual_add_rmsnorm(x, A.y.to(DEV), A.w.to(DEV))
+    idx = sample_tokens(A.N, 128, seed=2)
+    h, o = oracle.add_rmsnorm(A.x[idx], A.y[idx], A.w, A.eps, "bf16")
+    check("addnorm h", x.cpu()[idx], h, "bf16")
+    check("addnorm out", out.cpu()[idx], o, "bf16")
+    for N, d, dt in ((7, 24, "bf16"), (13, 4100, "f32"), (3, 40000, "bf16"), (5, 8, "bf16")):
+        B = inputs.make_addnorm_inputs(N, d, dt, seed=N + d)
+        x = B.x.to(DEV)
+        out = gr.residual_add_rmsnorm(x, B.y.to(DEV), B.w.to(DEV))
+        h, o = oracle.add_rmsnorm(B.x, B.y, B.w, B.eps, dt)
+        check(f"addnorm h {N}x{d}", x, h, dt)
+        check(f"addnorm out {N}x{d}", out, o, dt)
+
+
+def gpu_chain(Xin):
+    X = Xin.X.to(DEV)
+    ps = [dev_params(p) for p in Xin.params]
+    u, s = gr.read(X, ps[0])
+    y = gr.tanh_standin(u)
+    for p in ps[1:]:
+        u, s = gr.fused_write_read(X, y, s, p)
+        y = gr.tanh_standin(u)
+    gr.write(X, y, s)
+    return X
+
+
+def test_tanh_standin():
+    u = torch.randn(5000, dtype=torch.float32) * 3
+    for dt in (torch.float32, torch.bfloat16):
+        uu = u.to(dt)
+        y = gr.tanh_standin(uu.to(DEV))
+        check(f"tanh {dt}", y, oracle.tanh_standin(uu, "f32" if dt == torch.float32 else "bf16"),
+              "bf16")
+
+
+def chain_scale(X0, ss, ys):
+    """A for a chained state: |R^(0)| + sum_u |s^(u) y^(u)| (oracle values)."""
+    A = np.abs(to64(X0))
+    for s, y in zip(ss, ys):
+        A = A + np.abs(s[:, :, None] * y[:, None, :])
+    return A
+
+
+def test_chain_workload_subset():
+    """Workload 5's 32-sublayer chain (d=2048, n=4, r=32) on its first 256
+    tokens: final state vs the oracle's own chain (its own s, y and F)."""
+    Xin = inputs.workload(5, N=256)
+    R = gpu_chain(Xin)
+    oR, ss, ys = oracle.chain(Xin.X, Xin.params, Xin.eps, "bf16", record=True)
+    check_chain("chain final state", R, oR, chain_scale(Xin.X, ss, ys))
+    # The GPU trajectory is as close to the exact chain (fp64 storage, no
+    # rounding) as the oracle's own bf16 trajectory is.
+    exact = oracle.chain(Xin.X, Xin.params, Xin.eps, "f64")
+    dev_gpu = np.sqrt(np.mean((to64(R) - exact) ** 2))
+    dev_orc = np.sqrt(np.mean((oR - exact) ** 2))
+    assert dev_gpu <= 1.1 * dev_orc, (dev_gpu, dev_orc)
+
+
+def test_chain_workload_full_sampled():
+    """Workload 5 at full size (N=32768): the oracle runs the chain on 32
+    sampled tokens."""
+    Xin = inputs.workload(5)
+    R = gpu_chain(Xin).cpu()
+    idx = sample_tokens(Xin.N, 32, seed=5)
+    oR, ss, ys = oracle.chain(Xin.X[idx], Xin.params, Xin.eps, "bf16", record=True)
+    check_chain("chain-full final state (sampled)", R[idx], oR, chain_scale(Xin.X[idx], ss, ys))

@@ -1,1 +1,247 @@
-"""MI355X-native Gated Residual read/write path (binding filled in below)."""
+"""MI355X-native Gated Residual (GR) read/write path.
+
+Thin Python binding of ``libgr.so`` (the C ABI in ``include/gr.h``).  It only
+marshals arguments: checks that tensors live on the GPU with the shapes, dtype
+and contiguity the kernels assume, allocates outputs and the workspace with
+torch, and passes raw device pointers plus the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is missing the first call raises.
+
+GR ("Paper reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4):
+  read   u = (1/n) sum_i G_i (.) RMSNorm(R_i; gamma_i), s = 2 sigmoid(...)
+  write  R_i += s_i y
+  fused  write of sublayer l, then read of sublayer l+1, one pass over R.
+n = 1 fused residual add + RMSNorm: "Residual" (LLM inference), sec. 3.3.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["read", "write", "fused_write_read", "residual_add_rmsnorm", "tanh_standin",
+           "copy", "workspace_size", "library_path", "GRError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgr.so")
+
+GR_F32, GR_BF16 = 0, 1
+GR_OP_READ, GR_OP_FUSED_WRITE_READ = 0, 1
+
+
+class GRError(RuntimeError):
+    """A GR library call returned a non-success status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: status {status}: {message}")
+        self.status = status
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("d", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("gamma", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_write", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"GR HIP library not built ({_LIB_PATH}); run "
+                               "`python -m write_gr_read_amd.build` first")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        LP = ctypes.POINTER(_Layer)
+        L.gr_read.argtypes = [P, ctypes.c_int, I64, LP, P, P, P, ctypes.c_size_t, P]
+        L.gr_write.argtypes = [P, P, P, ctypes.c_int, I64, I32, I32, P]
+        L.gr_fused_write_read.argtypes = [P, P, P, ctypes.c_int, I64, LP, P, P, P,
+                                          ctypes.c_size_t, P]
+        L.residual_add_rmsnorm.argtypes = [P, P, P, F, P, ctypes.c_int, I64, I32, P]
+        L.gr_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, I64, LP,
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        L.gr_bench_tanh_standin.argtypes = [P, P, ctypes.c_int, I64, P]
+        L.gr_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
+        L.gr_status_string.argtypes = [ctypes.c_int]
+        L.gr_status_string.restype = ctypes.c_char_p
+        L.gr_last_error.argtypes = []
+        L.gr_last_error.restype = ctypes.c_char_p
+        for f in ("gr_read", "gr_write", "gr_fused_write_read", "residual_add_rmsnorm",
+                  "gr_workspace_size", "gr_bench_tanh_standin", "gr_bench_copy"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _call(fn: str, *args):
+    st = getattr(lib(), fn)(*args)
+    if st != 0:
+        raise GRError(fn, st, lib().gr_last_error().decode())
+
+
+# ------------------------------------------------------------------ argument checks
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GR_F32
+    if t.dtype == torch.bfloat16:
+        return GR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, shape, dtype, device) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _layer(layer, n: int, d: int, dtype, device, eps: float) -> _Layer:
+    g = _dev(layer.gamma, "gamma", (n, d), dtype, device)
+    r = 0 if layer.w_down is None else int(layer.w_down.shape[0])
+    wd = wu = None
+    if r:
+        wd = _dev(layer.w_down, "w_down", (r, n * d), dtype, device)
+        if layer.w_up is None:
+            raise ValueError("w_up is required when w_down is given")
+        wu = _dev(layer.w_up, "w_up", (n * d, r), dtype, device)
+    elif layer.w_up is not None:
+        raise ValueError("w_up given without w_down")
+    ww = None
+    if layer.w_write is not None:
+        ww = _dev(layer.w_write, "w_write", (n, n * d), dtype, device)
+    return _Layer(n, d, r, float(eps), g, wd, wu, ww)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_workspaces = {}
+
+
+def _workspace(device, nbytes: int) -> Tuple[int, int]:
+    """Per-device scratch buffer, grown on demand (used on the current stream)."""
+    if nbytes == 0:
+        return 0, 0
+    buf = _workspaces.get(device)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[device] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
+                   has_write: bool = True) -> int:
+    L = _Layer(n, d, r, 1e-6, None, None, None, 16 if has_write else None)
+    out = ctypes.c_size_t(0)
+    _call("gr_workspace_size", op, GR_BF16 if dtype == torch.bfloat16 else GR_F32, N,
+          ctypes.byref(L), ctypes.byref(out))
+    return out.value
+
+
+# ------------------------------------------------------------------ public API
+
+def read(state: torch.Tensor, layer, eps: float = 1e-6, u: Optional[torch.Tensor] = None,
+         s: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """GR read of ``state`` [N, n, d]: returns (u [N, d], s [N, n] fp32)."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    L = _layer(layer, n, d, dt, dev, eps)
+    u = torch.empty((N, d), dtype=dt, device=dev) if u is None else u
+    s = torch.empty((N, n), dtype=torch.float32, device=dev) if s is None else s
+    up = _dev(u, "u", (N, d), dt, dev)
+    spo = _dev(s, "s", (N, n), torch.float32, dev)
+    need = workspace_size(GR_OP_READ, dt, N, n, d, L.r, layer.w_write is not None)
+    wp, wn = _workspace(dev, need)
+    _call("gr_read", sp, _dt(state), N, ctypes.byref(L), up, spo, wp, wn, _stream(dev))
+    return u, s
+
+
+def write(state: torch.Tensor, y: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """GR write, in place: state[t, i, :] += s[t, i] * y[t, :].  Returns state."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    yp = _dev(y, "y", (N, d), dt, dev)
+    s_p = _dev(s, "s", (N, n), torch.float32, dev)
+    _call("gr_write", sp, yp, s_p, _dt(state), N, n, d, _stream(dev))
+    return state
+
+
+def fused_write_read(state: torch.Tensor, y: torch.Tensor, s_in: torch.Tensor, layer,
+                     eps: float = 1e-6, u: Optional[torch.Tensor] = None,
+                     s: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Write (y, s_in) into ``state`` in place, then read it with ``layer``:
+    returns (u_next [N, d], s_next [N, n])."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    yp = _dev(y, "y", (N, d), dt, dev)
+    sip = _dev(s_in, "s_in", (N, n), torch.float32, dev)
+    L = _layer(layer, n, d, dt, dev, eps)
+    u = torch.empty((N, d), dtype=dt, device=dev) if u is None else u
+    s = torch.empty((N, n), dtype=torch.float32, device=dev) if s is None else s
+    up = _dev(u, "u_next", (N, d), dt, dev)
+    spo = _dev(s, "s_next", (N, n), torch.float32, dev)
+    need = workspace_size(GR_OP_FUSED_WRITE_READ, dt, N, n, d, L.r, layer.w_write is not None)
+    wp, wn = _workspace(dev, need)
+    _call("gr_fused_write_read", sp, yp, sip, _dt(state), N, ctypes.byref(L), up, spo, wp, wn,
+          _stream(dev))
+    return u, s
+
+
+def residual_add_rmsnorm(x: torch.Tensor, y: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """n = 1: x += y in place (stored), returns out = RMSNorm(x; w)."""
+    N, d = x.shape
+    dev, dt = x.device, x.dtype
+    _dt(x)
+    xp = _dev(x, "x", (N, d), dt, None)
+    yp = _dev(y, "y", (N, d), dt, dev)
+    wp = _dev(w, "w", (d,), dt, dev)
+    out = torch.empty_like(x) if out is None else out
+    op = _dev(out, "out", (N, d), dt, dev)
+    _call("residual_add_rmsnorm", xp, yp, wp, float(eps), op, _dt(x), N, d, _stream(dev))
+    return out
+
+
+def tanh_standin(u: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The chained workload's sublayer stand-in, y = 0.1 tanh(u) (HIP kernel)."""
+    y = torch.empty_like(u) if y is None else y
+    up = _dev(u, "u", tuple(u.shape), u.dtype, None)
+    yp = _dev(y, "y", tuple(u.shape), u.dtype, u.device)
+    _call("gr_bench_tanh_standin", up, yp, _dt(u), u.numel(), _stream(u.device))
+    return y
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Streaming 16-byte copy probe (HBM bandwidth reference)."""
+    nbytes = src.numel() * src.element_size()
+    sp = _dev(src, "src", tuple(src.shape), src.dtype, None)
+    dp = _dev(dst, "dst", tuple(src.shape), src.dtype, src.device)
+    _call("gr_bench_copy", sp, dp, nbytes, _stream(src.device))
+    return dst

@@ -1,0 +1,244 @@
+// gr_api.hip -- host side of the C ABI declared in include/gr.h.
+//
+// Validates every argument on the host (before any HIP call, so argument
+// errors are testable without a GPU), picks a kernel variant and launches it
+// on the caller's stream.  No allocation, no synchronisation, no global state
+// except the per-thread error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gr.h"
+#include "gr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gr_status fail(gr_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gr_status ok() {
+    g_err[0] = '\0';
+    return GR_SUCCESS;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+gr_status check_dtype(gr_dtype dt, const char *fn) {
+    if (dt != GR_F32 && dt != GR_BF16) return fail(GR_ERROR_INVALID_VALUE, "%s: unknown dtype %d", fn, (int)dt);
+    return GR_SUCCESS;
+}
+
+gr_status check_ptr(const void *p, const char *what, const char *fn) {
+    if (!p) return fail(GR_ERROR_INVALID_VALUE, "%s: %s is NULL", fn, what);
+    if (!aligned16(p)) return fail(GR_ERROR_INVALID_VALUE, "%s: %s is not 16-byte aligned", fn, what);
+    return GR_SUCCESS;
+}
+
+gr_status check_width(gr_dtype dt, int64_t d, const char *fn) {
+    if (d < 1) return fail(GR_ERROR_INVALID_VALUE, "%s: d = %lld must be >= 1", fn, (long long)d);
+    const int vec = dt == GR_BF16 ? 8 : 4;
+    if (d % vec)
+        return fail(GR_ERROR_NOT_SUPPORTED, "%s: d = %lld must be a multiple of %d for this dtype", fn,
+                    (long long)d, vec);
+    if (d > (1 << 24)) return fail(GR_ERROR_NOT_SUPPORTED, "%s: d = %lld too large", fn, (long long)d);
+    return GR_SUCCESS;
+}
+
+gr_status check_tokens(int64_t N, const char *fn) {
+    if (N < 0) return fail(GR_ERROR_INVALID_VALUE, "%s: N = %lld is negative", fn, (long long)N);
+    if (N > 0x7fffffffLL) return fail(GR_ERROR_NOT_SUPPORTED, "%s: N = %lld exceeds 2^31-1", fn, (long long)N);
+    return GR_SUCCESS;
+}
+
+gr_status check_layer(const gr_layer *L, gr_dtype dt, const char *fn) {
+    if (!L) return fail(GR_ERROR_INVALID_VALUE, "%s: layer is NULL", fn);
+    if (L->n < 1 || L->n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, L->n);
+    gr_status st = check_width(dt, L->d, fn);
+    if (st) return st;
+    if (L->r < 0 || L->r > 512) return fail(GR_ERROR_INVALID_VALUE, "%s: r = %d outside 0..512", fn, L->r);
+    if (!(L->eps >= 0.f) || !isfinite(L->eps))
+        return fail(GR_ERROR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+    if ((int64_t)L->n * L->d > (1 << 24))
+        return fail(GR_ERROR_NOT_SUPPORTED, "%s: n*d too large", fn);
+    if ((st = check_ptr(L->gamma, "gamma", fn))) return st;
+    if (L->r > 0) {
+        if ((st = check_ptr(L->w_down, "w_down", fn))) return st;
+        if ((st = check_ptr(L->w_up, "w_up", fn))) return st;
+    } else if (L->w_down || L->w_up) {
+        return fail(GR_ERROR_INVALID_VALUE, "%s: r == 0 requires w_down == w_up == NULL", fn);
+    }
+    if (L->w_write && !aligned16(L->w_write))
+        return fail(GR_ERROR_INVALID_VALUE, "%s: w_write is not 16-byte aligned", fn);
+    return GR_SUCCESS;
+}
+
+size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
+    grk::ReadArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.N = N; a.n = L->n; a.d = L->d; a.r = L->r;
+    a.ww = L->w_write;
+    return grk::fast_path_ok(a) ? grk::fast_workspace_bytes(N, L->n, L->d, L->r) : 0;
+}
+
+gr_status launched(hipError_t e, const char *fn) {
+    if (e != hipSuccess) return fail(GR_ERROR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+gr_status run_read(grk::ReadArgs &a, const gr_layer *L, size_t ws_bytes, hipStream_t st,
+                   const char *fn) {
+    const gr_dtype dt = a.bf16 ? GR_BF16 : GR_F32;
+    const size_t need = read_workspace(dt, a.N, L);
+    if (need > 0) {
+        if (ws_bytes < need)
+            return fail(GR_ERROR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, need);
+        gr_status s = check_ptr(a.ws, "workspace", fn);
+        if (s) return s;
+    }
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    if (grk::fast_path_ok(a)) return launched(grk::launch_read_fast(a, st), fn);
+    return launched(grk::launch_read_generic(a, st), fn);
+}
+
+void fill_layer(grk::ReadArgs &a, const gr_layer *L) {
+    a.n = L->n; a.d = L->d; a.r = L->r; a.eps = L->eps;
+    a.gamma = L->gamma; a.wd = L->w_down; a.wu = L->w_up; a.ww = L->w_write;
+}
+
+}  // namespace
+
+extern "C" {
+
+gr_status gr_read(const void *state, gr_dtype dt, int64_t N, const gr_layer *L, void *u, float *s,
+                  void *workspace, size_t ws_bytes, void *stream) {
+    const char *fn = "gr_read";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_layer(L, dt, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(u, "u", fn)) ||
+        (st = check_ptr(s, "s", fn)))
+        return st;
+    grk::ReadArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.fused = false;
+    a.state = const_cast<void *>(state);
+    a.N = N;
+    fill_layer(a, L);
+    a.u = u; a.s_out = s; a.ws = workspace; a.ws_bytes = ws_bytes;
+    return run_read(a, L, ws_bytes, (hipStream_t)stream, fn);
+}
+
+gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_dtype dt, int64_t N,
+                              const gr_layer *next, void *u_next, float *s_next, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    const char *fn = "gr_fused_write_read";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_layer(next, dt, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) ||
+        (st = check_ptr(s_in, "s_in", fn)) || (st = check_ptr(u_next, "u_next", fn)) ||
+        (st = check_ptr(s_next, "s_next", fn)))
+        return st;
+    grk::ReadArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.fused = true;
+    a.state = state; a.y = y; a.s_in = s_in;
+    a.N = N;
+    fill_layer(a, next);
+    a.u = u_next; a.s_out = s_next; a.ws = workspace; a.ws_bytes = ws_bytes;
+    return run_read(a, next, ws_bytes, (hipStream_t)stream, fn);
+}
+
+gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int64_t N, int32_t n,
+                   int32_t d, void *stream) {
+    const char *fn = "gr_write";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if (n < 1 || n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, n);
+    if ((st = check_width(dt, d, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) ||
+        (st = check_ptr(s, "s", fn)))
+        return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_write(state, y, s, dt == GR_BF16, N, n, d, (hipStream_t)stream), fn);
+}
+
+gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
+                               gr_dtype dt, int64_t N, int32_t d, void *stream) {
+    const char *fn = "residual_add_rmsnorm";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_width(dt, d, fn))) return st;
+    if (!(eps >= 0.f) || !isfinite(eps))
+        return fail(GR_ERROR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+    if ((st = check_ptr(x, "x", fn)) || (st = check_ptr(y, "y", fn)) || (st = check_ptr(w, "w", fn)) ||
+        (st = check_ptr(out, "out", fn)))
+        return st;
+    if (out == x) return fail(GR_ERROR_INVALID_VALUE, "%s: out must not alias x", fn);
+    (void)hipGetLastError();
+    return launched(grk::launch_add_rmsnorm(x, y, w, eps, out, dt == GR_BF16, N, d, (hipStream_t)stream), fn);
+}
+
+gr_status gr_workspace_size(int op, gr_dtype dt, int64_t N, const gr_layer *L, size_t *bytes) {
+    const char *fn = "gr_workspace_size";
+    gr_status st;
+    if (!bytes) return fail(GR_ERROR_INVALID_VALUE, "%s: bytes is NULL", fn);
+    *bytes = 0;
+    if (op != GR_OP_READ && op != GR_OP_FUSED_WRITE_READ)
+        return fail(GR_ERROR_INVALID_VALUE, "%s: unknown op %d", fn, op);
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if (!L) return fail(GR_ERROR_INVALID_VALUE, "%s: layer is NULL", fn);
+    if (L->n < 1 || L->n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, L->n);
+    if ((st = check_width(dt, L->d, fn))) return st;
+    if (L->r < 0 || L->r > 512) return fail(GR_ERROR_INVALID_VALUE, "%s: r = %d outside 0..512", fn, L->r);
+    *bytes = read_workspace(dt, N, L);
+    return ok();
+}
+
+const char *gr_status_string(gr_status status) {
+    switch (status) {
+    case GR_SUCCESS: return "success";
+    case GR_ERROR_INVALID_VALUE: return "invalid value";
+    case GR_ERROR_NOT_SUPPORTED: return "not supported";
+    case GR_ERROR_LAUNCH: return "launch failed";
+    case GR_ERROR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+const char *gr_last_error(void) { return g_err; }
+
+gr_status gr_bench_tanh_standin(const void *u, void *y, gr_dtype dt, int64_t count, void *stream) {
+    const char *fn = "gr_bench_tanh_standin";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(count, fn))) return st;
+    if (count == 0) return ok();
+    if ((st = check_ptr(u, "u", fn)) || (st = check_ptr(y, "y", fn))) return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_tanh_standin(u, y, dt == GR_BF16, count, (hipStream_t)stream), fn);
+}
+
+gr_status gr_bench_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    const char *fn = "gr_bench_copy";
+    gr_status st;
+    if (bytes == 0) return ok();
+    if (bytes % 16) return fail(GR_ERROR_INVALID_VALUE, "%s: bytes must be a multiple of 16", fn);
+    if ((st = check_ptr(src, "src", fn)) || (st = check_ptr(dst, "dst", fn))) return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_copy(src, dst, bytes, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

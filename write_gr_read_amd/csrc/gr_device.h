@@ -1,0 +1,88 @@
+// gr_device.h -- device helpers shared by the HIP kernels of the GR library.
+//
+// gfx950 (CDNA4) only: wave64, bf16 stored as raw 16-bit words and widened to
+// fp32 by shifts, rounded back with the hardware round-to-nearest-even
+// conversion, sigmoid built from the hardware exp2 and reciprocal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace grk {
+
+typedef uint16_t bf16_t;  // bf16 storage word
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two fp32 -> packed bf16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 v = {a, b};
+    bf16x2 h = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float a) {
+    return __builtin_bit_cast(bf16_t, (__bf16)a);
+}
+
+// Storage-type adapters for the generic kernels.
+template <typename T> struct Store;
+template <> struct Store<float> {
+    __device__ static __forceinline__ float load(const float *p) { return *p; }
+    __device__ static __forceinline__ float round(float v) { return v; }
+    __device__ static __forceinline__ void store(float *p, float v) { *p = v; }
+};
+template <> struct Store<bf16_t> {
+    __device__ static __forceinline__ float load(const bf16_t *p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+    __device__ static __forceinline__ void store(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---- activations ----------------------------------------------------------
+// sigmoid(x) = 1 / (1 + e^-x) with e^-x = 2^(-x log2 e): hardware v_exp_f32 and
+// v_rcp_f32.  Saturates cleanly: e^-x -> inf gives 0, e^-x -> 0 gives 1.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// tanh(x) = sign(x) (1 - e^{-2|x|}) / (1 + e^{-2|x|}), from the hardware exp2.
+__device__ __forceinline__ float tanh_f(float x) {
+    float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * fabsf(x));
+    float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
+    return copysignf(t, x);
+}
+
+// ---- wave64 / workgroup reductions ----------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Sum over the whole workgroup (blockDim.x a multiple of 64, at most 1024).
+// `scratch` holds at least blockDim.x / 64 floats.  Every thread gets the sum.
+__device__ __forceinline__ float block_sum(float v, float *scratch) {
+    v = wave_sum(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
+    __syncthreads();
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int w = 0; w < nw; ++w) t += scratch[w];
+    return t;
+}
+
+}  // namespace grk

@@ -1,0 +1,322 @@
+// gr_generic.hip -- shape-generic kernels of the GR library.
+//
+// These cover every shape the C ABI accepts (1 <= n <= 8, any d with the
+// vector alignment, 0 <= r <= 512, fp32 or bf16) with plain VALU code: one
+// workgroup per token, fp32 arithmetic.  The MFMA fast path of the widened
+// bf16 state lives in gr_fast.hip; these are the fallback and the fp32 path.
+//
+// Method: "Paper reading: Qwen3.8 Flash Next", part 2 (Residual), sec. 4
+// (Gated Residual), eq:rms, eq:gate, eq:use_gate, eq:s, eq:write; the n = 1
+// fused add + RMSNorm of "Residual" (LLM inference), sec. 3.3.
+#include "gr_device.h"
+#include "gr_internal.h"
+
+namespace grk {
+
+constexpr int kGenThreads = 256;
+constexpr int kRowsPerPass = 8;  // projection rows accumulated per sweep
+
+// ---------------------------------------------------------------------------
+// GR read (optionally preceded by the write of the previous sublayer), one
+// workgroup per token.  Every pass walks the row in the same (branch, channel)
+// order with the same thread mapping, so each thread only re-reads elements it
+// wrote itself.
+//   FUSED: R' = R + s_in y is computed, rounded, stored, and the read then uses
+//   the stored R'.
+template <typename T, bool FUSED>
+__global__ void __launch_bounds__(kGenThreads)
+k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__restrict__ s_in,
+               int n, int d, int r, float eps, const T *__restrict__ gamma,
+               const T *__restrict__ wd, const T *__restrict__ wu, const T *__restrict__ ww,
+               T *__restrict__ u, float *__restrict__ s_out) {
+    __shared__ float red[kGenThreads / 64];
+    __shared__ float rho[8];
+    __shared__ float proj[512 + 8];  // z (then SiLU) for k < r, write logits after
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t nd = (int64_t)n * d;
+    T *Rt = state + t * nd;
+
+    // eq:write (FUSED) and the per-branch sum of squares of eq:rms.
+    for (int i = 0; i < n; ++i) {
+        float ss = 0.f;
+        const float si = FUSED ? s_in[t * n + i] : 0.f;
+        for (int c = tid; c < d; c += kGenThreads) {
+            float v = Store<T>::load(Rt + (int64_t)i * d + c);
+            if (FUSED) {
+                v = Store<T>::round(fmaf(si, Store<T>::load(y + t * d + c), v));
+                Store<T>::store(Rt + (int64_t)i * d + c, v);
+            }
+            ss = fmaf(v, v, ss);
+        }
+        ss = block_sum(ss, red);
+        if (tid == 0) rho[i] = 1.0f / sqrtf(ss / (float)d + eps);
+    }
+    __syncthreads();
+
+    // eq:gate down projection and eq:s logits: rows k < r of W_down, then the
+    // n rows of W_write, against v = vec(R-hat).
+    const int rows = r + (ww ? n : 0);
+    for (int k0 = 0; k0 < rows; k0 += kRowsPerPass) {
+        float acc[kRowsPerPass];
+#pragma unroll
+        for (int q = 0; q < kRowsPerPass; ++q) acc[q] = 0.f;
+        for (int i = 0; i < n; ++i) {
+            const float ri = rho[i];
+            for (int c = tid; c < d; c += kGenThreads) {
+                const int64_t j = (int64_t)i * d + c;
+                const float v = Store<T>::load(gamma + j) * Store<T>::load(Rt + j) * ri;
+#pragma unroll
+                for (int q = 0; q < kRowsPerPass; ++q) {
+                    const int k = k0 + q;
+                    if (k < rows) {
+                        const T *wrow = k < r ? wd + (int64_t)k * nd : ww + (int64_t)(k - r) * nd;
+                        acc[q] = fmaf(Store<T>::load(wrow + j), v, acc[q]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kRowsPerPass; ++q) {
+            const float tot = block_sum(acc[q], red);
+            if (tid == 0 && k0 + q < rows) proj[k0 + q] = tot / (float)n;
+        }
+    }
+    __syncthreads();
+    for (int k = tid; k < r; k += kGenThreads) proj[k] = silu_f(proj[k]);
+    __syncthreads();
+
+    // eq:gate up projection + sigmoid, eq:use_gate combine.
+    for (int c = tid; c < d; c += kGenThreads) {
+        float acc_u = 0.f;
+        for (int i = 0; i < n; ++i) {
+            const int64_t j = (int64_t)i * d + c;
+            float g = 1.0f;
+            if (r > 0) {
+                float l = 0.f;
+                const T *wrow = wu + j * r;
+                for (int k = 0; k < r; ++k) l = fmaf(Store<T>::load(wrow + k), proj[k], l);
+                g = sigmoid_f(l);
+            }
+            const float v = Store<T>::load(gamma + j) * Store<T>::load(Rt + j) * rho[i];
+            acc_u = fmaf(g, v, acc_u);
+        }
+        Store<T>::store(u + t * d + c, acc_u / (float)n);
+    }
+    if (s_out && tid < n) s_out[t * n + tid] = ww ? 2.0f * sigmoid_f(proj[r + tid]) : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// GR write, eq:write: streaming, 16-byte vectors (8 bf16 or 4 fp32 channels).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_write(T *__restrict__ state, const T *__restrict__ y, const float *__restrict__ s,
+        int64_t chunks, int n, int dv /* d / VEC */) {
+    constexpr int VEC = 16 / sizeof(T);
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < chunks;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t cv = q % dv;
+        const int64_t ti = q / dv;  // t * n + i
+        const int64_t t = ti / n;
+        const float si = s[ti];
+        u32x4 rv = *reinterpret_cast<const u32x4 *>(state + q * VEC);
+        const u32x4 yv = *reinterpret_cast<const u32x4 *>(y + (t * dv + cv) * VEC);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = fmaf(si, bf16_lo(yv[e]), bf16_lo(rv[e]));
+                const float hi = fmaf(si, bf16_hi(yv[e]), bf16_hi(rv[e]));
+                rv[e] = pack_bf16x2(lo, hi);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                rv[e] = __float_as_uint(fmaf(si, __uint_as_float(yv[e]), __uint_as_float(rv[e])));
+        }
+        *reinterpret_cast<u32x4 *>(state + q * VEC) = rv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// n = 1 fused residual add + RMSNorm ("Residual", sec. 3.3), one workgroup
+// per token.  KPT > 0: each thread keeps KPT 16-byte chunks of h in registers;
+// KPT == 0: any width, h is re-read (each thread only its own chunks).
+template <typename T, int KPT>
+__global__ void __launch_bounds__(256)
+k_add_rmsnorm(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ w, float eps,
+              T *out, int d) {
+    constexpr int VEC = 16 / sizeof(T);
+    __shared__ float red[4];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int dv = d / VEC;
+    T *xt = x + t * d;
+    const T *yt = y + t * d;
+    T *ot = out + t * d;
+    auto add_chunk = [&](int cv, u32x4 &hv, float &ss) {
+        u32x4 xv = *reinterpret_cast<const u32x4 *>(xt + cv * VEC);
+        const u32x4 yv = *reinterpret_cast<const u32x4 *>(yt + cv * VEC);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xv[e] = pack_bf16x2(bf16_lo(xv[e]) + bf16_lo(yv[e]), bf16_hi(xv[e]) + bf16_hi(yv[e]));
+                const float a = bf16_lo(xv[e]), b = bf16_hi(xv[e]);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float h = __uint_as_float(xv[e]) + __uint_as_float(yv[e]);
+                xv[e] = __float_as_uint(h);
+                ss = fmaf(h, h, ss);
+            }
+        }
+        *reinterpret_cast<u32x4 *>(xt + cv * VEC) = xv;
+        hv = xv;
+    };
+    auto norm_chunk = [&](int cv, const u32x4 &hv, float inv) {
+        const u32x4 wv = *reinterpret_cast<const u32x4 *>(w + cv * VEC);
+        u32x4 ov;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ov[e] = pack_bf16x2(bf16_lo(wv[e]) * bf16_lo(hv[e]) * inv,
+                                    bf16_hi(wv[e]) * bf16_hi(hv[e]) * inv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ov[e] = __float_as_uint(__uint_as_float(wv[e]) * __uint_as_float(hv[e]) * inv);
+        }
+        *reinterpret_cast<u32x4 *>(ot + cv * VEC) = ov;
+    };
+
+    float ss = 0.f;
+    if constexpr (KPT > 0) {
+        u32x4 h[KPT];
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int cv = tid + k * 256;
+            if (cv < dv) add_chunk(cv, h[k], ss);
+        }
+        const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int cv = tid + k * 256;
+            if (cv < dv) norm_chunk(cv, h[k], inv);
+        }
+    } else {
+        u32x4 h;
+        for (int cv = tid; cv < dv; cv += 256) add_chunk(cv, h, ss);
+        const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+        for (int cv = tid; cv < dv; cv += 256) {
+            h = *reinterpret_cast<const u32x4 *>(xt + cv * VEC);
+            norm_chunk(cv, h, inv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Measurement support: y = 0.1 tanh(u) elementwise; plain 16-byte copy.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tanh_standin(const T *__restrict__ u, T *__restrict__ y, int64_t count) {
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < count;
+         q += (int64_t)gridDim.x * blockDim.x)
+        Store<T>::store(y + q, 0.1f * tanh_f(Store<T>::load(u + q)));
+}
+
+__global__ void __launch_bounds__(256)
+k_copy(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int64_t vecs) {
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < vecs;
+         q += (int64_t)gridDim.x * blockDim.x)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + q), dst + q);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+static unsigned grid_for(int64_t items, int64_t per_block, int64_t cap = 1 << 16) {
+    int64_t g = (items + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (unsigned)g;
+}
+
+template <typename T>
+static hipError_t read_generic_t(const ReadArgs &a, hipStream_t st) {
+    T *state = (T *)a.state;
+    if (a.fused)
+        hipLaunchKernelGGL((k_read_generic<T, true>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
+                           st, state, (const T *)a.y, a.s_in, a.n, a.d, a.r, a.eps,
+                           (const T *)a.gamma, (const T *)a.wd, (const T *)a.wu,
+                           (const T *)a.ww, (T *)a.u, a.s_out);
+    else
+        hipLaunchKernelGGL((k_read_generic<T, false>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
+                           st, state, (const T *)nullptr, (const float *)nullptr, a.n, a.d, a.r,
+                           a.eps, (const T *)a.gamma, (const T *)a.wd, (const T *)a.wu,
+                           (const T *)a.ww, (T *)a.u, a.s_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_generic(const ReadArgs &a, hipStream_t st) {
+    return a.bf16 ? read_generic_t<bf16_t>(a, st) : read_generic_t<float>(a, st);
+}
+
+hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, int64_t N, int n,
+                        int d, hipStream_t st) {
+    const int vec = bf16 ? 8 : 4;
+    const int64_t chunks = N * n * (int64_t)(d / vec);
+    const unsigned g = grid_for(chunks, 256, 256 * 64);
+    if (bf16)
+        hipLaunchKernelGGL(k_write<bf16_t>, dim3(g), dim3(256), 0, st, (bf16_t *)state,
+                           (const bf16_t *)y, s, chunks, n, d / vec);
+    else
+        hipLaunchKernelGGL(k_write<float>, dim3(g), dim3(256), 0, st, (float *)state,
+                           (const float *)y, s, chunks, n, d / vec);
+    return hipGetLastError();
+}
+
+template <typename T, int KPT>
+static void add_rmsnorm_k(void *x, const void *y, const void *w, float eps, void *out,
+                          int64_t N, int d, hipStream_t st) {
+    hipLaunchKernelGGL((k_add_rmsnorm<T, KPT>), dim3((unsigned)N), dim3(256), 0, st, (T *)x,
+                       (const T *)y, (const T *)w, eps, (T *)out, d);
+}
+
+template <typename T>
+static void add_rmsnorm_t(void *x, const void *y, const void *w, float eps, void *out, int64_t N,
+                          int d, hipStream_t st) {
+    const int dv = d / (16 / (int)sizeof(T));
+    if (dv <= 256) add_rmsnorm_k<T, 1>(x, y, w, eps, out, N, d, st);
+    else if (dv <= 512) add_rmsnorm_k<T, 2>(x, y, w, eps, out, N, d, st);
+    else if (dv <= 1024) add_rmsnorm_k<T, 4>(x, y, w, eps, out, N, d, st);
+    else if (dv <= 2048) add_rmsnorm_k<T, 8>(x, y, w, eps, out, N, d, st);
+    else add_rmsnorm_k<T, 0>(x, y, w, eps, out, N, d, st);
+}
+
+hipError_t launch_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
+                              bool bf16, int64_t N, int d, hipStream_t st) {
+    if (bf16) add_rmsnorm_t<bf16_t>(x, y, w, eps, out, N, d, st);
+    else add_rmsnorm_t<float>(x, y, w, eps, out, N, d, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count, hipStream_t st) {
+    const unsigned g = grid_for(count, 256, 256 * 64);
+    if (bf16)
+        hipLaunchKernelGGL(k_tanh_standin<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t *)u,
+                           (bf16_t *)y, count);
+    else
+        hipLaunchKernelGGL(k_tanh_standin<float>, dim3(g), dim3(256), 0, st, (const float *)u,
+                           (float *)y, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t st) {
+    const int64_t vecs = (int64_t)(bytes / 16);
+    const unsigned g = grid_for(vecs, 256 * 4, 256 * 64);
+    hipLaunchKernelGGL(k_copy, dim3(g), dim3(256), 0, st, (const u32x4 *)src, (u32x4 *)dst, vecs);
+    return hipGetLastError();
+}
+
+}  // namespace grk

@@ -1,0 +1,40 @@
+// gr_internal.h -- declarations shared by the host API and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace grk {
+
+// Arguments of a read or fused write+read, already validated by the API.
+struct ReadArgs {
+    bool bf16;
+    bool fused;          // run eq:write with (y, s_in) first, in place
+    void *state;         // [N][n][d]
+    const void *y;       // [N][d]   (fused only)
+    const float *s_in;   // [N][n]   (fused only)
+    int64_t N;
+    int n, d, r;
+    float eps;
+    const void *gamma, *wd, *wu, *ww;
+    void *u;             // [N][d]
+    float *s_out;        // [N][n]
+    void *ws;            // workspace (device)
+    size_t ws_bytes;
+};
+
+hipError_t launch_read_generic(const ReadArgs &a, hipStream_t st);
+hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, int64_t N, int n,
+                        int d, hipStream_t st);
+hipError_t launch_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
+                              bool bf16, int64_t N, int d, hipStream_t st);
+hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count, hipStream_t st);
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
+
+// MFMA fast path for the bf16 widened state (gr_fast.hip).
+bool fast_path_ok(const ReadArgs &a);
+size_t fast_workspace_bytes(int64_t N, int n, int d, int r);
+hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st);
+
+}  // namespace grk
