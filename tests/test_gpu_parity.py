@@ -89,6 +89,19 @@ def test_shapes(N, n, d, r, dtype):
     run_read_write_fused(X, f"N{N}-n{n}-d{d}-r{r}-{dtype}")
 
 
+@pytest.mark.parametrize("N,d,r,w_std", [(64, 512, 32, 0.5), (130, 1024, 48, 0.3),
+                                         (48, 4096, 64, 0.2)])
+def test_saturating_gate(N, d, r, w_std):
+    """Large gate weights drive G over the whole (0, 1) range and s far from 1,
+    so a gate value landing on the wrong channel or branch cannot hide inside
+    the tolerance (with N(0, 0.02) weights G stays near 1/2)."""
+    X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=N + d + r, w_std=w_std)
+    _, _, _, G = oracle.read(X.X, X.params[0].gamma, X.params[0].w_down, X.params[0].w_up,
+                             X.params[0].w_write, detail=True)
+    assert G.min() < 0.05 and G.max() > 0.95
+    run_read_write_fused(X, f"saturating-N{N}-d{d}-r{r}")
+
+
 def test_no_write_projection_gives_unit_strength():
     X = inputs.make_gr_inputs(40, 4, 256, 16, "bf16", seed=41, with_write=False)
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))

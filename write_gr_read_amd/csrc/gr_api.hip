@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/gr.h"
@@ -80,12 +81,18 @@ gr_status check_layer(const gr_layer *L, gr_dtype dt, const char *fn) {
     return GR_SUCCESS;
 }
 
+// GR_KERNEL_VARIANT=generic forces the shape-generic kernels (A/B checks).
+bool force_generic() {
+    const char *v = getenv("GR_KERNEL_VARIANT");
+    return v && strcmp(v, "generic") == 0;
+}
+
 size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
     grk::ReadArgs a{};
     a.bf16 = dt == GR_BF16;
     a.N = N; a.n = L->n; a.d = L->d; a.r = L->r;
     a.ww = L->w_write;
-    return grk::fast_path_ok(a) ? grk::fast_workspace_bytes(N, L->n, L->d, L->r) : 0;
+    return grk::fast_path_ok(a) && !force_generic() ? grk::fast_workspace_bytes(N, L->n, L->d, L->r) : 0;
 }
 
 gr_status launched(hipError_t e, const char *fn) {
@@ -104,7 +111,7 @@ gr_status run_read(grk::ReadArgs &a, const gr_layer *L, size_t ws_bytes, hipStre
         if (s) return s;
     }
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    if (grk::fast_path_ok(a)) return launched(grk::launch_read_fast(a, st), fn);
+    if (grk::fast_path_ok(a) && !force_generic()) return launched(grk::launch_read_fast(a, st), fn);
     return launched(grk::launch_read_generic(a, st), fn);
 }
 

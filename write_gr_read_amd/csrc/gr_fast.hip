@@ -1,9 +1,464 @@
-// gr_fast.hip -- MFMA fast path (placeholder until implemented).
+// gr_fast.hip -- MFMA fast path of the GR read / fused write+read for a bf16
+// widened state ("Paper reading: Qwen3.8 Flash Next", part 2 Residual,
+// sec. 4 Gated Residual: eq:rms, eq:gate, eq:use_gate, eq:s; eq:write first
+// when fused; sec. 7: read fused into one traversal with Group RMSNorm).
+//
+// Two kernels, no inter-workgroup waiting (so no co-residency assumption):
+//
+// k_stream_proj   one workgroup per (token tile of 16*WAVES tokens, branch i).
+//                 Streams branch i of the tile once: (fused) R' = R + s_i y in
+//                 fp32, rounded to bf16 and stored; sum of squares of the stored
+//                 values (v_dot2_f32_bf16); and the down projection
+//                 P_i = W'^{(i)} R'_i on MFMA (v_mfma_f32_16x16x32_bf16), where
+//                 W' stacks W_down's and W_write's columns of branch i with the
+//                 gain gamma_i folded in.  Because
+//                     W_down vec(R-hat) = sum_i rho_i W_down^{(i)} (gamma_i . R_i)
+//                 the projections need no second sweep: rho_i is applied after.
+//                 Each workgroup writes (ss_i, P_i) for its tokens; the last of
+//                 the n workgroups of a tile to finish (atomic ticket) combines
+//                 them: rho_i = (ss_i/d + eps)^-1/2, z = (1/n) sum_i rho_i P_i,
+//                 a = SiLU(z), s = 2 sigmoid((1/n) sum_i rho_i P_i[r + .]).
+// k_gate_combine  one workgroup per (token tile, channel range).  Up projection
+//                 t = W_up (-log2(e) a) on MFMA, then per element
+//                 G_i rho_i = 1 / ((1 + 2^t) rms_i) and
+//                 u_c = sum_i (gamma_ic / n) R'_ic / ((1 + 2^t_ic) rms_i).
+//
+// Precision: an fp32 operand x of a contraction is carried as two bf16 words,
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (16 significant bits), and
+// multiplied in two MFMAs with fp32 accumulation.  This is done for W'
+// (W_down / W_write with gamma folded in) and for -log2(e) a; the state and
+// W_up enter as stored (exact bf16).
+//
+// MFMA operand convention (16x16x32 bf16): lane l holds A[l%16][8(l/16)+e] and
+// B[8(l/16)+e][l%16], e = 0..7; the result D[4(l/16)+m][l%16], m = 0..3.
+// A and B use the same k assignment, so the contraction is independent of how
+// the hardware orders k inside a lane group.
 #include "gr_device.h"
 #include "gr_internal.h"
 
 namespace grk {
-bool fast_path_ok(const ReadArgs &) { return false; }
-size_t fast_workspace_bytes(int64_t, int, int, int) { return 0; }
-hipError_t launch_read_fast(const ReadArgs &, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16 * kWaves;        // tokens per workgroup
+constexpr int kChunk = 32;                // channels per MFMA k-step
+constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
+constexpr int kLdsPitch = kChunk + 8;     // bf16 per staged row (padding vs. bank conflicts)
+constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
+
+struct FastShape {
+    int n, d, r, nw;     // nw = n if W_write given, else 0
+    int rows;            // r + nw
+    int row_blocks;      // ceil(rows / 16)
+    int pstride;         // floats per (token, branch) partial record
+    int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
+    int64_t N, tiles;
+};
+
+FastShape shape_of(const ReadArgs &a) {
+    FastShape s;
+    s.n = a.n; s.d = a.d; s.r = a.r;
+    s.nw = a.ww ? a.n : 0;
+    s.rows = s.r + s.nw;
+    s.row_blocks = (s.rows + 15) / 16;
+    s.pstride = 4 + 16 * s.row_blocks;
+    s.rk = (s.r + 31) / 32 * 32;
+    s.N = a.N;
+    s.tiles = (a.N + kTile - 1) / kTile;
+    return s;
+}
+
+// Workspace layout (all offsets 256-byte aligned):
+//   counters  [tiles] uint64      arrivals per tile (zero between calls)
+//   partial   [N][n][pstride] f32 ss at [0], projection rows at [4 ..]
+//   act       [N][2][rk] bf16     -log2(e) SiLU(z) as hi, lo words, zero-padded
+//   rms       [N][n] f32          1/rho
+struct Workspace {
+    unsigned long long *counters;
+    float *partial;
+    bf16_t *act;
+    float *rms;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_layout(const FastShape &s, char *base, Workspace *w) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    size_t o_cnt = take(sizeof(unsigned long long) * s.tiles);
+    size_t o_par = take(sizeof(float) * s.N * s.n * s.pstride);
+    size_t o_act = take(sizeof(bf16_t) * s.N * 2 * s.rk);
+    size_t o_rms = take(sizeof(float) * s.N * s.n);
+    if (w) {
+        w->counters = (unsigned long long *)(base + o_cnt);
+        w->partial = (float *)(base + o_par);
+        w->act = (bf16_t *)(base + o_act);
+        w->rms = (float *)(base + o_rms);
+    }
+    return off;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                          __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
+// the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
+// that XCD's L2) and consecutive dispatch slots.
+template <bool FUSED, int NRB>
+__global__ void __launch_bounds__(kThreads)
+k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
+              const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
+              const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, float *__restrict__ s_out,
+              Workspace ws, FastShape sh, float eps) {
+    // [buffer][hi/lo][row][k]
+    __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kLdsPitch];
+    __shared__ int s_last;
+
+    const int n = sh.n, d = sh.d;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = (b / 8 / n) * 8 + (b % 8);
+    const int br = (int)((b / 8) % n);
+    if (tile >= sh.tiles) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4;                 // lane group: channels 8g..8g+7 of a chunk
+    const int64_t t = tile * kTile + wave * 16 + (lane & 15);
+    const bool valid = t < sh.N;
+    const int64_t nd = (int64_t)n * d;
+
+    // Staging of W' for one chunk into LDS: row j < r from W_down, rows
+    // r..r+nw-1 from W_write, the rest zero; each times gamma of branch br.
+    auto stage = [&](int buf, int c0) {
+        const int vecs = NRB * 16 * (kChunk / 8);
+        for (int v = tid; v < vecs; v += kThreads) {
+            const int row = v / (kChunk / 8), cv = v % (kChunk / 8);
+            u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+            const bf16_t *src = nullptr;
+            if (row < sh.r) src = wd + (int64_t)row * nd;
+            else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
+            if (src) {
+                const int64_t col = (int64_t)br * d + c0 + cv * 8;
+                const u32x4 wv = *reinterpret_cast<const u32x4 *>(src + col);
+                const u32x4 gv = *reinterpret_cast<const u32x4 *>(gamma + col);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = bf16_lo(wv[e]) * bf16_lo(gv[e]);
+                    const float x1 = bf16_hi(wv[e]) * bf16_hi(gv[e]);
+                    hi[e] = pack_bf16x2(x0, x1);
+                    lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+                }
+            }
+            *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kLdsPitch + cv * 8]) = hi;
+            *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kLdsPitch + cv * 8]) = lo;
+        }
+    };
+
+    f32x4 acc[NRB];
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    const float si = (FUSED && valid) ? s_in[t * n + br] : 0.f;
+    bf16_t *rowp = state + (t * n + br) * (int64_t)d + 8 * g;
+    const bf16_t *yrow = FUSED ? y + t * (int64_t)d + 8 * g : nullptr;
+
+    const int nchunks = d / kChunk;
+    u32x4 rv = {0u, 0u, 0u, 0u}, yv = {0u, 0u, 0u, 0u};
+    if (valid) {
+        rv = *reinterpret_cast<const u32x4 *>(rowp);
+        if (FUSED) yv = *reinterpret_cast<const u32x4 *>(yrow);
+    }
+    stage(0, 0);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int cur = ch & 1;
+        // prefetch the next chunk of this lane's row (and y)
+        u32x4 rn = {0u, 0u, 0u, 0u}, yn = {0u, 0u, 0u, 0u};
+        if (valid && ch + 1 < nchunks) {
+            rn = *reinterpret_cast<const u32x4 *>(rowp + (ch + 1) * kChunk);
+            if (FUSED) yn = *reinterpret_cast<const u32x4 *>(yrow + (ch + 1) * kChunk);
+        }
+        if (ch + 1 < nchunks) stage(cur ^ 1, (ch + 1) * kChunk);
+        // eq:write, stored; the read below uses the stored (rounded) values
+        u32x4 w = rv;
+        if (FUSED) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = pack_bf16x2(fmaf(si, bf16_lo(yv[e]), bf16_lo(rv[e])),
+                                   fmaf(si, bf16_hi(yv[e]), bf16_hi(rv[e])));
+            if (valid) *reinterpret_cast<u32x4 *>(rowp + ch * kChunk) = w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
+        const bf16x8 bop = as_bf16x8(w);
+        const bf16_t *wh = &lds_w[cur][0][(lane & 15) * kLdsPitch + 8 * g];
+        const bf16_t *wlo = &lds_w[cur][1][(lane & 15) * kLdsPitch + 8 * g];
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) {
+            const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kLdsPitch);
+            const u32x4 al = *reinterpret_cast<const u32x4 *>(wlo + k * 16 * kLdsPitch);
+            acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop, acc[k], 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop, acc[k], 0, 0, 0);
+        }
+        rv = rn;
+        yv = yn;
+        __syncthreads();
+    }
+    // the four lane groups of a token hold disjoint channels: sum them
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+
+    if (valid) {
+        float *rec = ws.partial + (t * n + br) * (int64_t)sh.pstride;
+        if (g == 0) rec[0] = ss;
+#pragma unroll
+        for (int k = 0; k < NRB; ++k)
+            *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
+    }
+
+    // Last of the n workgroups of this tile combines the partial records.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned long long old = atomicAdd(ws.counters + tile, 1ull);
+        __threadfence();
+        s_last = (old == (unsigned long long)(n - 1));
+        if (s_last) ws.counters[tile] = 0ull;  // every arrival of this call is in
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    const int64_t t0 = tile * kTile;
+    const int cnt = (int)((sh.N - t0) < kTile ? (sh.N - t0) : kTile);
+    const float inv_n = 1.0f / (float)n;
+    // rho and rms per (token, branch)
+    __shared__ float s_rho[kTile * 8];
+    for (int q = tid; q < cnt * n; q += kThreads) {
+        const int tt = q / n, i = q % n;
+        const float ssum = __builtin_nontemporal_load(ws.partial + ((t0 + tt) * n + i) * (int64_t)sh.pstride);
+        const float ms = ssum / (float)d + eps;
+        const float rms = sqrtf(ms);
+        s_rho[tt * 8 + i] = 1.0f / rms;
+        ws.rms[(t0 + tt) * n + i] = rms;
+    }
+    __syncthreads();
+    // z -> -log2(e) SiLU(z) as (hi, lo) bf16 words, zero padded to rk;
+    // write logits -> s
+    const int outs = sh.rk + n;
+    for (int q = tid; q < cnt * outs; q += kThreads) {
+        const int tt = q / outs, j = q % outs;
+        const int64_t tok = t0 + tt;
+        if (j < sh.rk) {
+            float v = 0.f;
+            if (j < sh.r) {
+                float z = 0.f;
+                for (int i = 0; i < n; ++i)
+                    z = fmaf(s_rho[tt * 8 + i],
+                             __builtin_nontemporal_load(ws.partial + (tok * n + i) * (int64_t)sh.pstride + 4 + j), z);
+                v = -kLog2e * silu_f(z * inv_n);
+            }
+            const bf16_t h = f32_to_bf16(v);
+            ws.act[(tok * 2) * sh.rk + j] = h;
+            ws.act[(tok * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
+        } else {
+            const int i = j - sh.rk;
+            float sv = 1.0f;
+            if (sh.nw) {
+                float w = 0.f;
+                for (int i2 = 0; i2 < n; ++i2)
+                    w = fmaf(s_rho[tt * 8 + i2],
+                             __builtin_nontemporal_load(ws.partial + (tok * n + i2) * (int64_t)sh.pstride + 4 + sh.r + i), w);
+                sv = 2.0f * sigmoid_f(w * inv_n);
+            }
+            s_out[tok * n + i] = sv;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2.  blockIdx -> (tile, channel range); NB = n (compile time).
+// Staged per 32-channel chunk: W_up rows of the NB branches (as stored), read
+// in the order that makes the MFMA result of block h land on channels
+// 8g + 4h + m of the lane group g (the layout the state is loaded in), plus
+// gamma/n of the chunk.
+template <int NB, int RKS>
+__global__ void __launch_bounds__(kThreads)
+k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+               const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
+               int ranges) {
+    constexpr int RK = RKS * 32;
+    constexpr int kPitch = RK + 8;   // bf16 per staged W_up row
+    __shared__ __attribute__((aligned(16))) bf16_t lds_u[2][NB * kChunk * kPitch];
+    __shared__ float lds_g[2][NB * kChunk];
+
+    const int d = sh.d, r = sh.r;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = b / ranges;
+    const int range = (int)(b % ranges);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4;
+    const int64_t t = tile * kTile + wave * 16 + (lane & 15);
+    const bool valid = t < sh.N;
+    const int c_begin = range * kChanPerWg;
+    const int c_end = (c_begin + kChanPerWg) < d ? (c_begin + kChanPerWg) : d;
+    const float inv_n = 1.0f / (float)NB;
+
+    auto stage = [&](int buf, int c0) {
+        // W_up rows (i, c0 + cc), k < r; zero for r <= k < RK
+        const int vecs = NB * kChunk * (RK / 8);
+        for (int v = tid; v < vecs; v += kThreads) {
+            const int row = v / (RK / 8), kv = v % (RK / 8);
+            const int i = row / kChunk, cc = row % kChunk;
+            u32x4 out = {0u, 0u, 0u, 0u};
+            if (kv * 8 < r)
+                out = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
+            *reinterpret_cast<u32x4 *>(&lds_u[buf][row * kPitch + kv * 8]) = out;
+        }
+        for (int v = tid; v < NB * kChunk; v += kThreads) {
+            const int i = v / kChunk, cc = v % kChunk;
+            lds_g[buf][v] = bf16_to_f32(gamma[(int64_t)i * d + c0 + cc]) * inv_n;
+        }
+    };
+
+    // B operand: -log2(e) SiLU(z) of this lane's token as (hi, lo), k-steps of 32
+    bf16x8 bop[RKS], bopl[RKS];
+    float rms[NB];
+#pragma unroll
+    for (int ks = 0; ks < RKS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+        if (valid) {
+            v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
+            vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
+        }
+        bop[ks] = as_bf16x8(v);
+        bopl[ks] = as_bf16x8(vl);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rms[i] = valid ? ws.rms[t * NB + i] : 1.0f;
+
+    const bf16_t *srow = state + t * (int64_t)NB * d + 8 * g;
+    bf16_t *urow = u + t * (int64_t)d + 8 * g;
+    // row of W_up (within the staged chunk) that this lane feeds to block h
+    const int m16 = lane & 15;
+    const int a_row_h0 = 8 * (m16 >> 2) + (m16 & 3);
+
+    stage(0, c_begin);
+    __syncthreads();
+    for (int c0 = c_begin, it = 0; c0 < c_end; c0 += kChunk, ++it) {
+        const int cur = it & 1;
+        u32x4 rv[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            rv[i] = u32x4{0u, 0u, 0u, 0u};
+            if (valid) rv[i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c0);
+        }
+        if (c0 + kChunk < c_end) stage(cur ^ 1, c0 + kChunk);
+        float uacc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 tl = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t *ap = &lds_u[cur][(i * kChunk + a_row_h0 + 4 * h) * kPitch + 8 * g];
+#pragma unroll
+                for (int ks = 0; ks < RKS; ++ks) {
+                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                }
+                // tl[m] = -log2(e) * l for channel 8g + 4h + m of branch i
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = 4 * h + m;
+                    const uint32_t word = rv[i][e >> 1];
+                    const float rval = (e & 1) ? bf16_hi(word) : bf16_lo(word);
+                    const float bterm = rval * lds_g[cur][i * kChunk + 8 * g + e];
+                    const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                    uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
+                }
+            }
+        }
+        if (valid) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[2 * e], uacc[2 * e + 1]);
+            *reinterpret_cast<u32x4 *>(urow + c0) = o;
+        }
+        __syncthreads();
+    }
+}
+
+template <bool FUSED>
+hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    const int64_t tiles8 = (sh.tiles + 7) / 8 * 8;
+    const unsigned grid = (unsigned)(tiles8 * sh.n);
+    const bf16_t *y = (const bf16_t *)a.y;
+#define GR_K1(NRB)                                                                          \
+    case NRB:                                                                               \
+        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB>), dim3(grid), dim3(kThreads), 0, st,  \
+                           (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,           \
+                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, a.s_out, w, sh, a.eps); \
+        break;
+    switch (sh.row_blocks) {
+        GR_K1(1) GR_K1(2) GR_K1(3) GR_K1(4) GR_K1(5) GR_K1(6) GR_K1(7) GR_K1(8)
+    default: return hipErrorInvalidValue;
+    }
+#undef GR_K1
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    const int ranges = (sh.d + kChanPerWg - 1) / kChanPerWg;
+    const unsigned grid = (unsigned)(sh.tiles * ranges);
+#define GR_K2(RKS)                                                                          \
+    case RKS:                                                                               \
+        hipLaunchKernelGGL((k_gate_combine<NB, RKS>), dim3(grid), dim3(kThreads), 0, st,    \
+                           (const bf16_t *)a.state, (const bf16_t *)a.gamma,                \
+                           (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);             \
+        break;
+    switch (sh.rk / 32) {
+        GR_K2(1) GR_K2(2) GR_K2(3) GR_K2(4)
+    default: return hipErrorInvalidValue;
+    }
+#undef GR_K2
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool fast_path_ok(const ReadArgs &a) {
+    if (!a.bf16 || a.n != 4) return false;
+    if (a.r < 16 || a.r % 16 || a.r > 128) return false;
+    if (a.d % kChunk) return false;
+    const int rows = a.r + (a.ww ? a.n : 0);
+    return (rows + 15) / 16 <= kMaxRowBlocks;
+}
+
+size_t fast_workspace_bytes(int64_t N, int n, int d, int r) {
+    ReadArgs a{};
+    a.N = N; a.n = n; a.d = d; a.r = r;
+    a.ww = (const void *)16;  // worst case: with write rows
+    return workspace_layout(shape_of(a), nullptr, nullptr);
+}
+
+hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
+    const FastShape sh = shape_of(a);
+    Workspace w;
+    workspace_layout(sh, (char *)a.ws, &w);
+    hipError_t e = a.fused ? launch_k1<true>(a, sh, w, st) : launch_k1<false>(a, sh, w, st);
+    if (e != hipSuccess) return e;
+    return launch_k2<4>(a, sh, w, st);
+}
+
 }  // namespace grk
