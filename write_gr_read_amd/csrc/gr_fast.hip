@@ -44,8 +44,8 @@ constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16 * kWaves;        // tokens per workgroup
 constexpr int kChunk = 32;                // channels per MFMA k-step
+constexpr int kIter = 64;                 // channels per pipelined iteration (kernel 1)
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
-constexpr int kLdsPitch = kChunk + 8;     // bf16 per staged row (padding vs. bank conflicts)
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 
 struct FastShape {
@@ -102,6 +102,15 @@ size_t workspace_layout(const FastShape &s, char *base, Workspace *w) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// s_waitcnt with vmcnt = 0 and the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Device-coherent load (agent-scope relaxed atomic: misses stale caches).
+__device__ __forceinline__ float ld_coherent(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -112,14 +121,23 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
 // the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
 // that XCD's L2) and consecutive dispatch slots.
+//
+// Pipeline per iteration of kIter channels: the state / y of the iteration
+// two ahead are loaded into registers, the W' chunk of the next iteration
+// (loaded into registers during the previous one) is split into hi/lo and
+// written to the other LDS buffer, and the W' chunk after that is loaded.
 template <bool FUSED, int NRB>
 __global__ void __launch_bounds__(kThreads)
 k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, float *__restrict__ s_out,
               Workspace ws, FastShape sh, float eps) {
+    constexpr int KS = kIter / kChunk;                 // MFMA k-steps per iteration
+    constexpr int kPitch = kIter + 8;                  // bf16 per staged row
+    constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per iteration
+    constexpr int WV = (NV + kThreads - 1) / kThreads; // ... per thread
     // [buffer][hi/lo][row][k]
-    __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kLdsPitch];
+    __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
     __shared__ int s_last;
 
     const int n = sh.n, d = sh.d;
@@ -129,35 +147,52 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     if (tile >= sh.tiles) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4;                 // lane group: channels 8g..8g+7 of a chunk
+    const int g = lane >> 4;                 // lane group: channels 8g..8g+7 of a k-step
     const int64_t t = tile * kTile + wave * 16 + (lane & 15);
     const bool valid = t < sh.N;
     const int64_t nd = (int64_t)n * d;
+    const int nit = d / kIter;
 
-    // Staging of W' for one chunk into LDS: row j < r from W_down, rows
-    // r..r+nw-1 from W_write, the rest zero; each times gamma of branch br.
-    auto stage = [&](int buf, int c0) {
-        const int vecs = NRB * 16 * (kChunk / 8);
-        for (int v = tid; v < vecs; v += kThreads) {
-            const int row = v / (kChunk / 8), cv = v % (kChunk / 8);
-            u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+    // W' staging: row j < r from W_down, rows r..r+nw-1 from W_write, the rest
+    // zero; times gamma of branch br; stored as bf16 hi and lo planes.
+    u32x4 wreg[WV], greg[WV];
+    auto load_w = [&](int it) {
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
+            const int row = v / (kIter / 8), cv = v % (kIter / 8);
             const bf16_t *src = nullptr;
-            if (row < sh.r) src = wd + (int64_t)row * nd;
-            else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
+            if (v < NV && it < nit) {
+                if (row < sh.r) src = wd + (int64_t)row * nd;
+                else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
+            }
             if (src) {
-                const int64_t col = (int64_t)br * d + c0 + cv * 8;
-                const u32x4 wv = *reinterpret_cast<const u32x4 *>(src + col);
-                const u32x4 gv = *reinterpret_cast<const u32x4 *>(gamma + col);
+                const int64_t col = (int64_t)br * d + it * kIter + cv * 8;
+                wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
+                greg[q] = *reinterpret_cast<const u32x4 *>(gamma + col);
+            } else {
+                wreg[q] = u32x4{0u, 0u, 0u, 0u};
+                greg[q] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_w = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
+            if (v < NV) {
+                const int row = v / (kIter / 8), cv = v % (kIter / 8);
+                u32x4 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float x0 = bf16_lo(wv[e]) * bf16_lo(gv[e]);
-                    const float x1 = bf16_hi(wv[e]) * bf16_hi(gv[e]);
+                    const float x0 = bf16_lo(wreg[q][e]) * bf16_lo(greg[q][e]);
+                    const float x1 = bf16_hi(wreg[q][e]) * bf16_hi(greg[q][e]);
                     hi[e] = pack_bf16x2(x0, x1);
                     lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
                 }
+                *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kPitch + cv * 8]) = hi;
+                *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kPitch + cv * 8]) = lo;
             }
-            *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kLdsPitch + cv * 8]) = hi;
-            *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kLdsPitch + cv * 8]) = lo;
         }
     };
 
@@ -169,72 +204,96 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     bf16_t *rowp = state + (t * n + br) * (int64_t)d + 8 * g;
     const bf16_t *yrow = FUSED ? y + t * (int64_t)d + 8 * g : nullptr;
 
-    const int nchunks = d / kChunk;
-    u32x4 rv = {0u, 0u, 0u, 0u}, yv = {0u, 0u, 0u, 0u};
-    if (valid) {
-        rv = *reinterpret_cast<const u32x4 *>(rowp);
-        if (FUSED) yv = *reinterpret_cast<const u32x4 *>(yrow);
-    }
-    stage(0, 0);
+    u32x4 r0[KS], y0[KS], r1[KS], y1[KS], r2[KS], y2[KS];
+    auto load_data = [&](int it, u32x4 (&rr)[KS], u32x4 (&yy)[KS]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            rr[ks] = u32x4{0u, 0u, 0u, 0u};
+            yy[ks] = u32x4{0u, 0u, 0u, 0u};
+            if (valid && it < nit) {
+                rr[ks] = *reinterpret_cast<const u32x4 *>(rowp + it * kIter + ks * kChunk);
+                if (FUSED) yy[ks] = *reinterpret_cast<const u32x4 *>(yrow + it * kIter + ks * kChunk);
+            }
+        }
+    };
+
+    load_w(0);
+    store_w(0);
+    load_w(1);
+    load_data(0, r0, y0);
+    load_data(1, r1, y1);
     __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int cur = ch & 1;
-        // prefetch the next chunk of this lane's row (and y)
-        u32x4 rn = {0u, 0u, 0u, 0u}, yn = {0u, 0u, 0u, 0u};
-        if (valid && ch + 1 < nchunks) {
-            rn = *reinterpret_cast<const u32x4 *>(rowp + (ch + 1) * kChunk);
-            if (FUSED) yn = *reinterpret_cast<const u32x4 *>(yrow + (ch + 1) * kChunk);
-        }
-        if (ch + 1 < nchunks) stage(cur ^ 1, (ch + 1) * kChunk);
-        // eq:write, stored; the read below uses the stored (rounded) values
-        u32x4 w = rv;
-        if (FUSED) {
+    for (int it = 0; it < nit; ++it) {
+        const int cur = it & 1;
+        load_data(it + 2, r2, y2);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[e] = pack_bf16x2(fmaf(si, bf16_lo(yv[e]), bf16_lo(rv[e])),
-                                   fmaf(si, bf16_hi(yv[e]), bf16_hi(rv[e])));
-            if (valid) *reinterpret_cast<u32x4 *>(rowp + ch * kChunk) = w;
-        }
+        for (int ks = 0; ks < KS; ++ks) {
+            // eq:write, stored; the read below uses the stored (rounded) values
+            u32x4 w = r0[ks];
+            if (FUSED) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
-        const bf16x8 bop = as_bf16x8(w);
-        const bf16_t *wh = &lds_w[cur][0][(lane & 15) * kLdsPitch + 8 * g];
-        const bf16_t *wlo = &lds_w[cur][1][(lane & 15) * kLdsPitch + 8 * g];
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2(fmaf(si, bf16_lo(y0[ks][e]), bf16_lo(r0[ks][e])),
+                                       fmaf(si, bf16_hi(y0[ks][e]), bf16_hi(r0[ks][e])));
+                if (valid) *reinterpret_cast<u32x4 *>(rowp + it * kIter + ks * kChunk) = w;
+            }
 #pragma unroll
-        for (int k = 0; k < NRB; ++k) {
-            const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kLdsPitch);
-            const u32x4 al = *reinterpret_cast<const u32x4 *>(wlo + k * 16 * kLdsPitch);
-            acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop, acc[k], 0, 0, 0);
-            acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop, acc[k], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
+            const bf16x8 bop = as_bf16x8(w);
+            const bf16_t *wh = &lds_w[cur][0][(lane & 15) * kPitch + ks * kChunk + 8 * g];
+            const bf16_t *wl = &lds_w[cur][1][(lane & 15) * kPitch + ks * kChunk + 8 * g];
+#pragma unroll
+            for (int k = 0; k < NRB; ++k) {
+                const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kPitch);
+                const u32x4 al = *reinterpret_cast<const u32x4 *>(wl + k * 16 * kPitch);
+                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop, acc[k], 0, 0, 0);
+                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop, acc[k], 0, 0, 0);
+            }
         }
-        rv = rn;
-        yv = yn;
+        if (it + 1 < nit) store_w(cur ^ 1);
+        load_w(it + 2);
         __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            r0[ks] = r1[ks]; y0[ks] = y1[ks];
+            r1[ks] = r2[ks]; y1[ks] = y2[ks];
+        }
     }
     // the four lane groups of a token hold disjoint channels: sum them
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
 
+    // Publish (ss, P) of this branch.  The records are written with
+    // device-coherent stores (write-through past this XCD's L2) and drained
+    // before the ticket is taken, so the last workgroup -- which may run on
+    // another XCD -- reads them with device-coherent loads.  No L2 writeback
+    // (agent-scope release fence) is needed, which would otherwise flush the
+    // whole L2 full of freshly streamed state.
     if (valid) {
         float *rec = ws.partial + (t * n + br) * (int64_t)sh.pstride;
-        if (g == 0) rec[0] = ss;
+        if (g == 0) __hip_atomic_store(rec, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int k = 0; k < NRB; ++k)
-            *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
+        for (int k = 0; k < NRB; ++k) {
+            unsigned long long *q = reinterpret_cast<unsigned long long *>(rec + 4 + 16 * k + 4 * g);
+            __hip_atomic_store(q, __builtin_bit_cast(unsigned long long, float2{acc[k][0], acc[k][1]}),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(q + 1, __builtin_bit_cast(unsigned long long, float2{acc[k][2], acc[k][3]}),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-
-    // Last of the n workgroups of this tile combines the partial records.
-    __threadfence();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's stores are performed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (tid == 0) {
-        const unsigned long long old = atomicAdd(ws.counters + tile, 1ull);
-        __threadfence();
+        const unsigned long long old =
+            __hip_atomic_fetch_add(ws.counters + tile, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned long long)(n - 1));
-        if (s_last) ws.counters[tile] = 0ull;  // every arrival of this call is in
+        // every arrival of this call is in: leave the counter at zero
+        if (s_last) __hip_atomic_store(ws.counters + tile, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
     const int64_t t0 = tile * kTile;
     const int cnt = (int)((sh.N - t0) < kTile ? (sh.N - t0) : kTile);
@@ -243,7 +302,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     __shared__ float s_rho[kTile * 8];
     for (int q = tid; q < cnt * n; q += kThreads) {
         const int tt = q / n, i = q % n;
-        const float ssum = __builtin_nontemporal_load(ws.partial + ((t0 + tt) * n + i) * (int64_t)sh.pstride);
+        const float ssum = ld_coherent(ws.partial + ((t0 + tt) * n + i) * (int64_t)sh.pstride);
         const float ms = ssum / (float)d + eps;
         const float rms = sqrtf(ms);
         s_rho[tt * 8 + i] = 1.0f / rms;
@@ -262,7 +321,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                 float z = 0.f;
                 for (int i = 0; i < n; ++i)
                     z = fmaf(s_rho[tt * 8 + i],
-                             __builtin_nontemporal_load(ws.partial + (tok * n + i) * (int64_t)sh.pstride + 4 + j), z);
+                             ld_coherent(ws.partial + (tok * n + i) * (int64_t)sh.pstride + 4 + j), z);
                 v = -kLog2e * silu_f(z * inv_n);
             }
             const bf16_t h = f32_to_bf16(v);
@@ -275,7 +334,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                 float w = 0.f;
                 for (int i2 = 0; i2 < n; ++i2)
                     w = fmaf(s_rho[tt * 8 + i2],
-                             __builtin_nontemporal_load(ws.partial + (tok * n + i2) * (int64_t)sh.pstride + 4 + sh.r + i), w);
+                             ld_coherent(ws.partial + (tok * n + i2) * (int64_t)sh.pstride + 4 + sh.r + i), w);
                 sv = 2.0f * sigmoid_f(w * inv_n);
             }
             s_out[tok * n + i] = sv;
@@ -288,14 +347,17 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 // Staged per 32-channel chunk: W_up rows of the NB branches (as stored), read
 // in the order that makes the MFMA result of block h land on channels
 // 8g + 4h + m of the lane group g (the layout the state is loaded in), plus
-// gamma/n of the chunk.
+// gamma/n of the chunk.  Pipeline: the state of the chunk two ahead and the
+// W_up rows of the chunk one ahead are in flight while a chunk is combined.
 template <int NB, int RKS>
 __global__ void __launch_bounds__(kThreads)
 k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
     constexpr int RK = RKS * 32;
-    constexpr int kPitch = RK + 8;   // bf16 per staged W_up row
+    constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
+    constexpr int NV = NB * kChunk * (RK / 8);         // 16-byte vectors of W_up per chunk
+    constexpr int WV = (NV + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) bf16_t lds_u[2][NB * kChunk * kPitch];
     __shared__ float lds_g[2][NB * kChunk];
 
@@ -309,23 +371,35 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const bool valid = t < sh.N;
     const int c_begin = range * kChanPerWg;
     const int c_end = (c_begin + kChanPerWg) < d ? (c_begin + kChanPerWg) : d;
+    const int nit = (c_end - c_begin) / kChunk;
     const float inv_n = 1.0f / (float)NB;
 
-    auto stage = [&](int buf, int c0) {
-        // W_up rows (i, c0 + cc), k < r; zero for r <= k < RK
-        const int vecs = NB * kChunk * (RK / 8);
-        for (int v = tid; v < vecs; v += kThreads) {
+    u32x4 wreg[WV];
+    float greg = 0.f;
+    auto load_w = [&](int it) {
+        const int c0 = c_begin + it * kChunk;
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
             const int row = v / (RK / 8), kv = v % (RK / 8);
             const int i = row / kChunk, cc = row % kChunk;
-            u32x4 out = {0u, 0u, 0u, 0u};
-            if (kv * 8 < r)
-                out = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
-            *reinterpret_cast<u32x4 *>(&lds_u[buf][row * kPitch + kv * 8]) = out;
+            wreg[q] = u32x4{0u, 0u, 0u, 0u};
+            if (v < NV && it < nit && kv * 8 < r)
+                wreg[q] = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
         }
-        for (int v = tid; v < NB * kChunk; v += kThreads) {
-            const int i = v / kChunk, cc = v % kChunk;
-            lds_g[buf][v] = bf16_to_f32(gamma[(int64_t)i * d + c0 + cc]) * inv_n;
+        if (tid < NB * kChunk && it < nit)
+            greg = bf16_to_f32(gamma[(int64_t)(tid / kChunk) * d + c0 + tid % kChunk]) * inv_n;
+    };
+    auto store_w = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
+            if (v < NV) {
+                const int row = v / (RK / 8), kv = v % (RK / 8);
+                *reinterpret_cast<u32x4 *>(&lds_u[buf][row * kPitch + kv * 8]) = wreg[q];
+            }
         }
+        if (tid < NB * kChunk) lds_g[buf][tid] = greg;
     };
 
     // B operand: -log2(e) SiLU(z) of this lane's token as (hi, lo), k-steps of 32
@@ -350,17 +424,26 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const int m16 = lane & 15;
     const int a_row_h0 = 8 * (m16 >> 2) + (m16 & 3);
 
-    stage(0, c_begin);
-    __syncthreads();
-    for (int c0 = c_begin, it = 0; c0 < c_end; c0 += kChunk, ++it) {
-        const int cur = it & 1;
-        u32x4 rv[NB];
+    u32x4 s0[NB], s1[NB], s2[NB];
+    auto load_state = [&](int it, u32x4 (&sv)[NB]) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            rv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (valid) rv[i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c0);
+            sv[i] = u32x4{0u, 0u, 0u, 0u};
+            if (valid && it < nit)
+                sv[i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c_begin + it * kChunk);
         }
-        if (c0 + kChunk < c_end) stage(cur ^ 1, c0 + kChunk);
+    };
+
+    load_w(0);
+    store_w(0);
+    load_w(1);
+    load_state(0, s0);
+    load_state(1, s1);
+    __syncthreads();
+    for (int it = 0; it < nit; ++it) {
+        const int cur = it & 1;
+        const int c0 = c_begin + it * kChunk;
+        load_state(it + 2, s2);
         float uacc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
@@ -380,7 +463,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int e = 4 * h + m;
-                    const uint32_t word = rv[i][e >> 1];
+                    const uint32_t word = s0[i][e >> 1];
                     const float rval = (e & 1) ? bf16_hi(word) : bf16_lo(word);
                     const float bterm = rval * lds_g[cur][i * kChunk + 8 * g + e];
                     const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
@@ -394,7 +477,14 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
             for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[2 * e], uacc[2 * e + 1]);
             *reinterpret_cast<u32x4 *>(urow + c0) = o;
         }
+        if (it + 1 < nit) store_w(cur ^ 1);
+        load_w(it + 2);
         __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            s0[i] = s1[i];
+            s1[i] = s2[i];
+        }
     }
 }
 
@@ -440,7 +530,7 @@ hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w,
 bool fast_path_ok(const ReadArgs &a) {
     if (!a.bf16 || a.n != 4) return false;
     if (a.r < 16 || a.r % 16 || a.r > 128) return false;
-    if (a.d % kChunk) return false;
+    if (a.d % kIter) return false;
     const int rows = a.r + (a.ww ? a.n : 0);
     return (rows + 15) / 16 <= kMaxRowBlocks;
 }
