@@ -44,7 +44,18 @@ constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16 * kWaves;        // tokens per workgroup
 constexpr int kChunk = 32;                // channels per MFMA k-step
-constexpr int kIter = 64;                 // channels per pipelined iteration (kernel 1)
+#ifndef GR_K1_ITER
+#define GR_K1_ITER 64
+#endif
+#ifndef GR_K1_DEPTH
+#define GR_K1_DEPTH 2
+#endif
+constexpr int kIter = GR_K1_ITER;         // channels per pipelined iteration (kernel 1)
+constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight
+#ifndef GR_K2_MINB
+#define GR_K2_MINB 1
+#endif
+constexpr int kK2MinBlocks = GR_K2_MINB;  // kernel 2 workgroups per CU the register budget targets
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 
@@ -126,15 +137,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // two ahead are loaded into registers, the W' chunk of the next iteration
 // (loaded into registers during the previous one) is split into hi/lo and
 // written to the other LDS buffer, and the W' chunk after that is loaded.
-template <bool FUSED, int NRB>
+template <bool FUSED, int NRB, int KITER, int DEPTH>
 __global__ void __launch_bounds__(kThreads)
 k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, float *__restrict__ s_out,
               Workspace ws, FastShape sh, float eps) {
-    constexpr int KS = kIter / kChunk;                 // MFMA k-steps per iteration
-    constexpr int kPitch = kIter + 8;                  // bf16 per staged row
-    constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per iteration
+    constexpr int KS = KITER / kChunk;                 // MFMA k-steps per iteration
+    constexpr int kPitch = KITER + 8;                  // bf16 per staged row
+    constexpr int NV = NRB * 16 * (KITER / 8);         // 16-byte vectors of W' per iteration
     constexpr int WV = (NV + kThreads - 1) / kThreads; // ... per thread
     // [buffer][hi/lo][row][k]
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
@@ -151,7 +162,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     const int64_t t = tile * kTile + wave * 16 + (lane & 15);
     const bool valid = t < sh.N;
     const int64_t nd = (int64_t)n * d;
-    const int nit = d / kIter;
+    const int nit = d / KITER;
 
     // W' staging: row j < r from W_down, rows r..r+nw-1 from W_write, the rest
     // zero; times gamma of branch br; stored as bf16 hi and lo planes.
@@ -160,14 +171,14 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kThreads;
-            const int row = v / (kIter / 8), cv = v % (kIter / 8);
+            const int row = v / (KITER / 8), cv = v % (KITER / 8);
             const bf16_t *src = nullptr;
             if (v < NV && it < nit) {
                 if (row < sh.r) src = wd + (int64_t)row * nd;
                 else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
             }
             if (src) {
-                const int64_t col = (int64_t)br * d + it * kIter + cv * 8;
+                const int64_t col = (int64_t)br * d + it * KITER + cv * 8;
                 wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
                 greg[q] = *reinterpret_cast<const u32x4 *>(gamma + col);
             } else {
@@ -181,7 +192,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kThreads;
             if (v < NV) {
-                const int row = v / (kIter / 8), cv = v % (kIter / 8);
+                const int row = v / (KITER / 8), cv = v % (KITER / 8);
                 u32x4 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -204,15 +215,16 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     bf16_t *rowp = state + (t * n + br) * (int64_t)d + 8 * g;
     const bf16_t *yrow = FUSED ? y + t * (int64_t)d + 8 * g : nullptr;
 
-    u32x4 r0[KS], y0[KS], r1[KS], y1[KS], r2[KS], y2[KS];
-    auto load_data = [&](int it, u32x4 (&rr)[KS], u32x4 (&yy)[KS]) {
+    // data ring: slot 0 is the iteration being computed, slots 1..DEPTH are in flight
+    u32x4 rr[DEPTH + 1][KS], yy[DEPTH + 1][KS];
+    auto load_data = [&](int it, int slot) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            rr[ks] = u32x4{0u, 0u, 0u, 0u};
-            yy[ks] = u32x4{0u, 0u, 0u, 0u};
+            rr[slot][ks] = u32x4{0u, 0u, 0u, 0u};
+            yy[slot][ks] = u32x4{0u, 0u, 0u, 0u};
             if (valid && it < nit) {
-                rr[ks] = *reinterpret_cast<const u32x4 *>(rowp + it * kIter + ks * kChunk);
-                if (FUSED) yy[ks] = *reinterpret_cast<const u32x4 *>(yrow + it * kIter + ks * kChunk);
+                rr[slot][ks] = *reinterpret_cast<const u32x4 *>(rowp + it * KITER + ks * kChunk);
+                if (FUSED) yy[slot][ks] = *reinterpret_cast<const u32x4 *>(yrow + it * KITER + ks * kChunk);
             }
         }
     };
@@ -220,22 +232,22 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     load_w(0);
     store_w(0);
     load_w(1);
-    load_data(0, r0, y0);
-    load_data(1, r1, y1);
+#pragma unroll
+    for (int q = 0; q < DEPTH; ++q) load_data(q, q);
     __syncthreads();
     for (int it = 0; it < nit; ++it) {
         const int cur = it & 1;
-        load_data(it + 2, r2, y2);
+        load_data(it + DEPTH, DEPTH);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             // eq:write, stored; the read below uses the stored (rounded) values
-            u32x4 w = r0[ks];
+            u32x4 w = rr[0][ks];
             if (FUSED) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(fmaf(si, bf16_lo(y0[ks][e]), bf16_lo(r0[ks][e])),
-                                       fmaf(si, bf16_hi(y0[ks][e]), bf16_hi(r0[ks][e])));
-                if (valid) *reinterpret_cast<u32x4 *>(rowp + it * kIter + ks * kChunk) = w;
+                    w[e] = pack_bf16x2(fmaf(si, bf16_lo(yy[0][ks][e]), bf16_lo(rr[0][ks][e])),
+                                       fmaf(si, bf16_hi(yy[0][ks][e]), bf16_hi(rr[0][ks][e])));
+                if (valid) *reinterpret_cast<u32x4 *>(rowp + it * KITER + ks * kChunk) = w;
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
@@ -254,10 +266,12 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         load_w(it + 2);
         __syncthreads();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            r0[ks] = r1[ks]; y0[ks] = y1[ks];
-            r1[ks] = r2[ks]; y1[ks] = y2[ks];
-        }
+        for (int q = 0; q < DEPTH; ++q)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                rr[q][ks] = rr[q + 1][ks];
+                yy[q][ks] = yy[q + 1][ks];
+            }
     }
     // the four lane groups of a token hold disjoint channels: sum them
     ss += __shfl_xor(ss, 16, 64);
@@ -350,7 +364,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 // gamma/n of the chunk.  Pipeline: the state of the chunk two ahead and the
 // W_up rows of the chunk one ahead are in flight while a chunk is combined.
 template <int NB, int RKS>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, kK2MinBlocks)
 k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
@@ -495,7 +509,7 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     const bf16_t *y = (const bf16_t *)a.y;
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
-        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB>), dim3(grid), dim3(kThreads), 0, st,  \
+        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepth>), dim3(grid), dim3(kThreads), 0, st, \
                            (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,           \
                            (const bf16_t *)a.wd, (const bf16_t *)a.ww, a.s_out, w, sh, a.eps); \
         break;
