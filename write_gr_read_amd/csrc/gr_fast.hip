@@ -52,10 +52,16 @@ constexpr int kChunk = 32;                // channels per MFMA k-step
 #endif
 constexpr int kIter = GR_K1_ITER;         // channels per pipelined iteration (kernel 1)
 constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight
-#ifndef GR_K2_MINB
-#define GR_K2_MINB 1
+#ifndef GR_K2_WAVES_PER_SIMD
+#define GR_K2_WAVES_PER_SIMD 3
 #endif
-constexpr int kK2MinBlocks = GR_K2_MINB;  // kernel 2 workgroups per CU the register budget targets
+#ifndef GR_K2_WAVES
+#define GR_K2_WAVES 4
+#endif
+constexpr int kK2WavesPerSimd = GR_K2_WAVES_PER_SIMD;  // occupancy target of kernel 2
+constexpr int kK2Waves = GR_K2_WAVES;                  // waves per kernel-2 workgroup
+constexpr int kK2Threads = 64 * kK2Waves;
+constexpr int kK2Tile = 16 * kK2Waves;                 // tokens per kernel-2 workgroup
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 
@@ -358,22 +364,27 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 
 // ---------------------------------------------------------------------------
 // Kernel 2.  blockIdx -> (tile, channel range); NB = n (compile time).
-// Staged per 32-channel chunk: W_up rows of the NB branches (as stored), read
-// in the order that makes the MFMA result of block h land on channels
-// 8g + 4h + m of the lane group g (the layout the state is loaded in), plus
-// gamma/n of the chunk.  Pipeline: the state of the chunk two ahead and the
-// W_up rows of the chunk one ahead are in flight while a chunk is combined.
+// Staged per 32-channel chunk: W_up rows of the NB branches (as stored), placed
+// in LDS in MFMA row order -- LDS row i*32 + 16h + m holds channel
+// 8(m/4) + 4h + m%4 -- so that the result of block h lands on channels
+// 8g + 4h + m' of lane group g (the layout the state is loaded in) and each
+// fragment read covers 16 consecutive LDS rows (no bank conflicts at a pitch of
+// an odd number of 16-byte units).  Also staged: gamma/n of the chunk as bf16
+// words (exact for n = 4) masked to one half, so v_dot2 forms (gamma/n) R'
+// straight from the packed state.  Pipeline: the state of the chunk two ahead
+// and the W_up rows of the chunk after it are in flight while a chunk is
+// combined.
 template <int NB, int RKS>
-__global__ void __launch_bounds__(kThreads, kK2MinBlocks)
+__global__ void __launch_bounds__(kK2Threads, kK2WavesPerSimd)
 k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
     constexpr int RK = RKS * 32;
     constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
     constexpr int NV = NB * kChunk * (RK / 8);         // 16-byte vectors of W_up per chunk
-    constexpr int WV = (NV + kThreads - 1) / kThreads;
+    constexpr int WV = (NV + kK2Threads - 1) / kK2Threads;
     __shared__ __attribute__((aligned(16))) bf16_t lds_u[2][NB * kChunk * kPitch];
-    __shared__ float lds_g[2][NB * kChunk];
+    __shared__ uint32_t lds_g[2][NB * kChunk];  // (gamma/n) of channel cc in the half cc%2 of a word
 
     const int d = sh.d, r = sh.r;
     const int64_t b = blockIdx.x;
@@ -381,7 +392,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const int range = (int)(b % ranges);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4;
-    const int64_t t = tile * kTile + wave * 16 + (lane & 15);
+    const int64_t t = tile * kK2Tile + wave * 16 + (lane & 15);
     const bool valid = t < sh.N;
     const int c_begin = range * kChanPerWg;
     const int c_end = (c_begin + kChanPerWg) < d ? (c_begin + kChanPerWg) : d;
@@ -389,28 +400,32 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const float inv_n = 1.0f / (float)NB;
 
     u32x4 wreg[WV];
-    float greg = 0.f;
+    uint32_t greg = 0u;
     auto load_w = [&](int it) {
         const int c0 = c_begin + it * kChunk;
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
-            const int v = tid + q * kThreads;
+            const int v = tid + q * kK2Threads;
             const int row = v / (RK / 8), kv = v % (RK / 8);
             const int i = row / kChunk, cc = row % kChunk;
             wreg[q] = u32x4{0u, 0u, 0u, 0u};
             if (v < NV && it < nit && kv * 8 < r)
                 wreg[q] = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
         }
-        if (tid < NB * kChunk && it < nit)
-            greg = bf16_to_f32(gamma[(int64_t)(tid / kChunk) * d + c0 + tid % kChunk]) * inv_n;
+        if (tid < NB * kChunk && it < nit) {
+            const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)(tid / kChunk) * d + c0 + tid % kChunk]) * inv_n);
+            greg = (tid & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+        }
     };
     auto store_w = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
-            const int v = tid + q * kThreads;
+            const int v = tid + q * kK2Threads;
             if (v < NV) {
                 const int row = v / (RK / 8), kv = v % (RK / 8);
-                *reinterpret_cast<u32x4 *>(&lds_u[buf][row * kPitch + kv * 8]) = wreg[q];
+                const int i = row / kChunk, cc = row % kChunk;
+                const int pos = i * kChunk + 16 * ((cc >> 2) & 1) + 4 * (cc >> 3) + (cc & 3);
+                *reinterpret_cast<u32x4 *>(&lds_u[buf][pos * kPitch + kv * 8]) = wreg[q];
             }
         }
         if (tid < NB * kChunk) lds_g[buf][tid] = greg;
@@ -434,11 +449,9 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 
     const bf16_t *srow = state + t * (int64_t)NB * d + 8 * g;
     bf16_t *urow = u + t * (int64_t)d + 8 * g;
-    // row of W_up (within the staged chunk) that this lane feeds to block h
-    const int m16 = lane & 15;
-    const int a_row_h0 = 8 * (m16 >> 2) + (m16 & 3);
+    const int m16 = lane & 15;  // A row this lane feeds
 
-    u32x4 s0[NB], s1[NB], s2[NB];
+    u32x4 s0[NB], s1[NB];
     auto load_state = [&](int it, u32x4 (&sv)[NB]) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -452,12 +465,11 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     store_w(0);
     load_w(1);
     load_state(0, s0);
-    load_state(1, s1);
     __syncthreads();
     for (int it = 0; it < nit; ++it) {
         const int cur = it & 1;
         const int c0 = c_begin + it * kChunk;
-        load_state(it + 2, s2);
+        load_state(it + 1, s1);
         float uacc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
@@ -466,7 +478,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 f32x4 tl = {0.f, 0.f, 0.f, 0.f};
-                const bf16_t *ap = &lds_u[cur][(i * kChunk + a_row_h0 + 4 * h) * kPitch + 8 * g];
+                const bf16_t *ap = &lds_u[cur][(i * kChunk + 16 * h + m16) * kPitch + 8 * g];
 #pragma unroll
                 for (int ks = 0; ks < RKS; ++ks) {
                     const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
@@ -477,9 +489,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int e = 4 * h + m;
-                    const uint32_t word = s0[i][e >> 1];
-                    const float rval = (e & 1) ? bf16_hi(word) : bf16_lo(word);
-                    const float bterm = rval * lds_g[cur][i * kChunk + 8 * g + e];
+                    const float bterm = dot2_bf16(s0[i][e >> 1], lds_g[cur][i * kChunk + 8 * g + e], 0.f);
                     const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
                     uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
                 }
@@ -495,10 +505,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
         load_w(it + 2);
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            s0[i] = s1[i];
-            s1[i] = s2[i];
-        }
+        for (int i = 0; i < NB; ++i) s0[i] = s1[i];
     }
 }
 
@@ -524,10 +531,10 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
 template <int NB>
 hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     const int ranges = (sh.d + kChanPerWg - 1) / kChanPerWg;
-    const unsigned grid = (unsigned)(sh.tiles * ranges);
+    const unsigned grid = (unsigned)(((sh.N + kK2Tile - 1) / kK2Tile) * ranges);
 #define GR_K2(RKS)                                                                          \
     case RKS:                                                                               \
-        hipLaunchKernelGGL((k_gate_combine<NB, RKS>), dim3(grid), dim3(kThreads), 0, st,    \
+        hipLaunchKernelGGL((k_gate_combine<NB, RKS>), dim3(grid), dim3(kK2Threads), 0, st,  \
                            (const bf16_t *)a.state, (const bf16_t *)a.gamma,                \
                            (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);             \
         break;
