@@ -9,6 +9,11 @@ step of the hot path.  Inputs are seeded synthetic tensors already resident in
 HBM.  Prints one JSON line on stdout; progress goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --workload {prefill,decode,addnorm,chain,tiny,all}
+The default (prefill) line is the headline; the other workloads print their own
+line (decode: us per call with the state warm in cache, back to back; addnorm:
+the n = 1 fused residual add + RMSNorm; chain: 32 sublayers of read -> F ->
+fused write+read -> ... -> write with the elementwise F stand-in).
 """
 import argparse
 import hashlib
@@ -80,6 +85,119 @@ def cpu_baseline(Xin, threads, n_tokens):
                       f"{dt:.2f} s wall)"}
 
 
+def timed(fn, steps, warmup, stream):
+    """Average ms per call of fn over `steps` calls after `warmup` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def line(metric, value, unit, steps, warmup, ms, config, dtype="bf16", higher=True, **extra):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": ms, "higher_is_better": higher, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config}
+    out.update(extra)
+    return out
+
+
+def roofline(alg_bytes, ms, kernel, traffic=None):
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kernel,
+            "algorithmic_bytes_per_launch": alg_bytes}
+
+
+def bench_other(which, args, dev):
+    """Lines for the non-headline workloads."""
+    import torch
+    import write_gr_read_amd as gr
+    from write_gr_read_amd import inputs
+    stream = torch.cuda.current_stream(dev)
+    if which in ("decode", "tiny"):
+        k = 4 if which == "decode" else 1
+        W = inputs.WORKLOADS[k]
+        Xin = inputs.workload(k)
+        N, n, d, r = Xin.N, Xin.n, Xin.d, Xin.r
+        p0, p1 = Xin.params[0].to(dev), Xin.params[1].to(dev)
+        X, y = Xin.X.to(dev), Xin.y.to(dev)
+        u = torch.empty((N, d), dtype=X.dtype, device=dev)
+        so = torch.empty((N, n), dtype=torch.float32, device=dev)
+        _, s_in = gr.read(X, p0)
+        steps = args.steps if args.steps_given else 2000
+        ms = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so), steps, args.warmup, stream)
+        elt = 2 if Xin.dtype == "bf16" else 4
+        alg = algorithmic_bytes(N, n, d, r, elt)
+        log(f"{which}: {ms * 1e3:.2f} us/call")
+        return line(f"GR fused write+read us/call ({which}, N={N}, d={d}, n={n}, r={r})",
+                    ms * 1e3, "us/call", steps, args.warmup, ms,
+                    {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "cache": "warm, back-to-back"},
+                    dtype=Xin.dtype, higher=False, tokens_per_s=N / (ms * 1e-3),
+                    roofline=roofline(alg, ms, "gr_fused_write_read"))
+    if which == "addnorm":
+        W = inputs.WORKLOADS[2]
+        A = inputs.workload(2)
+        # three buffer sets rotate so the 192 MiB footprint does not sit in the 256 MB cache
+        sets = [(A.x.to(dev), A.y.to(dev), torch.empty_like(A.x, device=dev)) for _ in range(3)]
+        w = A.w.to(dev)
+        state = {"i": 0}
+        def step():
+            x, yy, out = sets[state["i"] % 3]
+            state["i"] += 1
+            gr.residual_add_rmsnorm(x, yy, w, out=out)
+        steps = args.steps if args.steps_given else 60
+        ms = timed(step, steps, args.warmup, stream)
+        alg = 4 * A.N * A.d * 2 + A.d * 2
+        log(f"addnorm: {ms * 1e3:.1f} us/call, {alg / ms / 1e6:.0f} GB/s")
+        return line(f"fused residual add + RMSNorm tokens/s (n=1, N={A.N}, d={A.d}, bf16)",
+                    A.N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
+                    {"workload": W["name"], "N": A.N, "d": A.d, "buffer_sets": 3},
+                    roofline=roofline(alg, ms, "residual_add_rmsnorm"))
+    if which == "chain":
+        W = inputs.WORKLOADS[5]
+        Xin = inputs.workload(5)
+        N, n, d, r = Xin.N, Xin.n, Xin.d, Xin.r
+        ps = [p.to(dev) for p in Xin.params]
+        X0 = Xin.X.to(dev)
+        X = X0.clone()
+        u = torch.empty((N, d), dtype=X.dtype, device=dev)
+        yb = torch.empty_like(u)
+        s_bufs = [torch.empty((N, n), dtype=torch.float32, device=dev) for _ in range(2)]
+        def chain():
+            s_cur = s_bufs[0]
+            gr.read(X, ps[0], u=u, s=s_cur)
+            gr.tanh_standin(u, yb)
+            for k, p in enumerate(ps[1:]):
+                s_nxt = s_bufs[(k + 1) % 2]
+                gr.fused_write_read(X, yb, s_cur, p, u=u, s=s_nxt)
+                gr.tanh_standin(u, yb)
+                s_cur = s_nxt
+            gr.write(X, yb, s_cur)
+        steps = args.steps if args.steps_given else 5
+        ms = timed(chain, steps, max(1, min(args.warmup, 2)), stream)
+        ms_f = timed(lambda: gr.tanh_standin(u, yb), 20, 2, stream)
+        gr_ms = ms - len(ps) * ms_f
+        per_fused = algorithmic_bytes(N, n, d, r)
+        weights = n * d * 2 + 2 * r * n * d * 2 + n * n * d * 2
+        read_b = N * (n * d * 2 + d * 2 + n * 4) + weights
+        write_b = N * (2 * n * d * 2 + d * 2 + n * 4)
+        alg = (len(ps) - 1) * per_fused + read_b + write_b
+        log(f"chain: {ms:.2f} ms per 32-sublayer pass (F stand-in {len(ps) * ms_f:.2f} ms of it)")
+        return line(f"GR 32-sublayer chain tokens/s (N={N}, d={d}, n={n}, r={r}, bf16)",
+                    N / (ms * 1e-3), "tokens/s", steps, 1, ms,
+                    {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "sublayers": len(ps)},
+                    gr_ms_per_pass=gr_ms, f_standin_ms_per_pass=len(ps) * ms_f,
+                    roofline=roofline(alg, gr_ms, "GR calls of the chain (F excluded)"))
+    raise ValueError(which)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,7 +206,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "addnorm", "chain", "tiny", "all"])
     args = ap.parse_args()
+    args.steps_given = "--steps" in sys.argv
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the GR path is per-token and is sharded over "
@@ -101,6 +222,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "prefill":
+        names = ["decode", "addnorm", "chain", "tiny"] if args.workload == "all" else [args.workload]
+        for w in names:
+            print(json.dumps(bench_other(w, args, dev)), flush=True)
+        if args.workload != "all":
+            return
     W = inputs.WORKLOADS[3]
     log(f"generating workload {W['name']} ...")
     Xin = inputs.workload(3)

@@ -64,12 +64,19 @@ constexpr int kK2Threads = 64 * kK2Waves;
 constexpr int kK2Tile = 16 * kK2Waves;                 // tokens per kernel-2 workgroup
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
+#ifndef GR_SPLIT_TARGET
+#define GR_SPLIT_TARGET 64
+#endif
+constexpr int kSplitTarget = GR_SPLIT_TARGET;  // kernel-1 workgroups wanted before splitting channels
 
 struct FastShape {
     int n, d, r, nw;     // nw = n if W_write given, else 0
     int rows;            // r + nw
     int row_blocks;      // ceil(rows / 16)
-    int pstride;         // floats per (token, branch) partial record
+    int pstride;         // floats per (token, branch, split) partial record
+    int ksplit;          // channel splits of kernel 1 (workgroups per (tile, branch))
+    int ksplit_chan;     // channels per split (multiple of kIter)
+    int k2_chan;         // channels per kernel-2 workgroup (multiple of kChunk)
     int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
     int64_t N, tiles;
 };
@@ -84,12 +91,24 @@ FastShape shape_of(const ReadArgs &a) {
     s.rk = (s.r + 31) / 32 * 32;
     s.N = a.N;
     s.tiles = (a.N + kTile - 1) / kTile;
+    // Enough workgroups to fill the GPU when N is small (decode): split the
+    // channels of kernel 1 (partial records are summed in the tile reduction)
+    // and narrow the channel range of kernel 2.
+    int ks = 1;
+    while (s.tiles * s.n * ks < kSplitTarget && (s.d / (ks * 2)) % kIter == 0 && s.d / (ks * 2) >= 2 * kIter)
+        ks *= 2;
+    s.ksplit = ks;
+    s.ksplit_chan = s.d / ks;
+    int c2 = kChanPerWg;
+    const int64_t tiles2 = (a.N + kK2Tile - 1) / kK2Tile;
+    while (tiles2 * ((s.d + c2 - 1) / c2) < 1024 && c2 > kChunk && (c2 / 2) % kChunk == 0) c2 /= 2;
+    s.k2_chan = c2;
     return s;
 }
 
 // Workspace layout (all offsets 256-byte aligned):
 //   counters  [tiles] uint64      arrivals per tile (zero between calls)
-//   partial   [N][n][pstride] f32 ss at [0], projection rows at [4 ..]
+//   partial   [N][n][ksplit][pstride] f32: ss at [0], projection rows at [4 ..]
 //   act       [N][2][rk] bf16     -log2(e) SiLU(z) as hi, lo words, zero-padded
 //   rms       [N][n] f32          1/rho
 struct Workspace {
@@ -105,7 +124,7 @@ size_t workspace_layout(const FastShape &s, char *base, Workspace *w) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     size_t o_cnt = take(sizeof(unsigned long long) * s.tiles);
-    size_t o_par = take(sizeof(float) * s.N * s.n * s.pstride);
+    size_t o_par = take(sizeof(float) * s.N * s.n * s.ksplit * s.pstride);
     size_t o_act = take(sizeof(bf16_t) * s.N * 2 * s.rk);
     size_t o_rms = take(sizeof(float) * s.N * s.n);
     if (w) {
@@ -134,6 +153,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+template <bool COHERENT>
+__device__ void combine_records(const Workspace &ws, const FastShape &sh, float eps,
+                                float *__restrict__ s_out, int64_t t0, int cnt, int tid,
+                                int nthreads, float *s_rho);
+
 // ---------------------------------------------------------------------------
 // Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
 // the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
@@ -157,10 +181,11 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
     __shared__ int s_last;
 
-    const int n = sh.n, d = sh.d;
+    const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
-    const int64_t tile = (b / 8 / n) * 8 + (b % 8);
-    const int br = (int)((b / 8) % n);
+    const int64_t tile = (b / 8 / (n * S)) * 8 + (b % 8);
+    const int br = (int)((b / 8) % (n * S)) / S;
+    const int split = (int)((b / 8) % S);
     if (tile >= sh.tiles) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -168,7 +193,8 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     const int64_t t = tile * kTile + wave * 16 + (lane & 15);
     const bool valid = t < sh.N;
     const int64_t nd = (int64_t)n * d;
-    const int nit = d / KITER;
+    const int nit = sh.ksplit_chan / KITER;
+    const int c_base = split * sh.ksplit_chan;  // first channel of this split
 
     // W' staging: row j < r from W_down, rows r..r+nw-1 from W_write, the rest
     // zero; times gamma of branch br; stored as bf16 hi and lo planes.
@@ -184,7 +210,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                 else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
             }
             if (src) {
-                const int64_t col = (int64_t)br * d + it * KITER + cv * 8;
+                const int64_t col = (int64_t)br * d + c_base + it * KITER + cv * 8;
                 wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
                 greg[q] = *reinterpret_cast<const u32x4 *>(gamma + col);
             } else {
@@ -218,8 +244,8 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     const float si = (FUSED && valid) ? s_in[t * n + br] : 0.f;
-    bf16_t *rowp = state + (t * n + br) * (int64_t)d + 8 * g;
-    const bf16_t *yrow = FUSED ? y + t * (int64_t)d + 8 * g : nullptr;
+    bf16_t *rowp = state + (t * n + br) * (int64_t)d + c_base + 8 * g;
+    const bf16_t *yrow = FUSED ? y + t * (int64_t)d + c_base + 8 * g : nullptr;
 
     // data ring: slot 0 is the iteration being computed, slots 1..DEPTH are in flight
     u32x4 rr[DEPTH + 1][KS], yy[DEPTH + 1][KS];
@@ -289,8 +315,14 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     // another XCD -- reads them with device-coherent loads.  No L2 writeback
     // (agent-scope release fence) is needed, which would otherwise flush the
     // whole L2 full of freshly streamed state.
-    if (valid) {
-        float *rec = ws.partial + (t * n + br) * (int64_t)sh.pstride;
+    if (valid && S > 1) {
+        // read by k_reduce_splits after this kernel: plain stores
+        float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
+        if (g == 0) rec[0] = ss;
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
+    } else if (valid) {
+        float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
         if (g == 0) __hip_atomic_store(rec, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int k = 0; k < NRB; ++k) {
@@ -301,6 +333,10 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    // With channel splits the records are combined by k_reduce_splits after
+    // this kernel (many workgroups share that work); without, the last of the
+    // n workgroups of the tile combines them here.
+    if (S > 1) return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's stores are performed
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -308,7 +344,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     if (tid == 0) {
         const unsigned long long old =
             __hip_atomic_fetch_add(ws.counters + tile, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (unsigned long long)(n - 1));
+        s_last = (old == (unsigned long long)(n * S - 1));
         // every arrival of this call is in: leave the counter at zero
         if (s_last) __hip_atomic_store(ws.counters + tile, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -317,31 +353,52 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 
     const int64_t t0 = tile * kTile;
     const int cnt = (int)((sh.N - t0) < kTile ? (sh.N - t0) : kTile);
-    const float inv_n = 1.0f / (float)n;
-    // rho and rms per (token, branch)
     __shared__ float s_rho[kTile * 8];
-    for (int q = tid; q < cnt * n; q += kThreads) {
+    combine_records<true>(ws, sh, eps, s_out, t0, cnt, tid, kThreads, s_rho);
+}
+
+// Combine the partial records of tokens [t0, t0 + cnt): rho_i and rms_i from
+// the summed squares, z = (1/n) sum_i rho_i P_i (rows < r), stored as
+// -log2(e) SiLU(z) in (hi, lo) bf16 words, and s = 2 sigmoid(...) from the
+// write rows.  Records are summed over splits and branches in a fixed order.
+// COHERENT: records were published in this kernel (device-coherent loads).
+template <bool COHERENT>
+__device__ void combine_records(const Workspace &ws, const FastShape &sh, float eps,
+                                float *__restrict__ s_out, int64_t t0, int cnt, int tid,
+                                int nthreads, float *s_rho /* [cnt][8] */) {
+    const int n = sh.n, S = sh.ksplit;
+    const float inv_n = 1.0f / (float)n;
+    auto rec = [&](int64_t tok, int i, int k) {
+        return ws.partial + ((tok * n + i) * S + k) * (int64_t)sh.pstride;
+    };
+    auto ld = [&](const float *p) { return COHERENT ? ld_coherent(p) : *p; };
+    auto sum_splits = [&](int64_t tok, int i, int off) {
+        float a0 = 0.f, a1 = 0.f;
+        int k = 0;
+        for (; k + 1 < S; k += 2) {
+            a0 += ld(rec(tok, i, k) + off);
+            a1 += ld(rec(tok, i, k + 1) + off);
+        }
+        if (k < S) a0 += ld(rec(tok, i, k) + off);
+        return a0 + a1;
+    };
+    for (int q = tid; q < cnt * n; q += nthreads) {
         const int tt = q / n, i = q % n;
-        const float ssum = ld_coherent(ws.partial + ((t0 + tt) * n + i) * (int64_t)sh.pstride);
-        const float ms = ssum / (float)d + eps;
+        const float ms = sum_splits(t0 + tt, i, 0) / (float)sh.d + eps;
         const float rms = sqrtf(ms);
         s_rho[tt * 8 + i] = 1.0f / rms;
         ws.rms[(t0 + tt) * n + i] = rms;
     }
     __syncthreads();
-    // z -> -log2(e) SiLU(z) as (hi, lo) bf16 words, zero padded to rk;
-    // write logits -> s
     const int outs = sh.rk + n;
-    for (int q = tid; q < cnt * outs; q += kThreads) {
+    for (int q = tid; q < cnt * outs; q += nthreads) {
         const int tt = q / outs, j = q % outs;
         const int64_t tok = t0 + tt;
         if (j < sh.rk) {
             float v = 0.f;
             if (j < sh.r) {
                 float z = 0.f;
-                for (int i = 0; i < n; ++i)
-                    z = fmaf(s_rho[tt * 8 + i],
-                             ld_coherent(ws.partial + (tok * n + i) * (int64_t)sh.pstride + 4 + j), z);
+                for (int i = 0; i < n; ++i) z = fmaf(s_rho[tt * 8 + i], sum_splits(tok, i, 4 + j), z);
                 v = -kLog2e * silu_f(z * inv_n);
             }
             const bf16_t h = f32_to_bf16(v);
@@ -353,8 +410,76 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
             if (sh.nw) {
                 float w = 0.f;
                 for (int i2 = 0; i2 < n; ++i2)
-                    w = fmaf(s_rho[tt * 8 + i2],
-                             ld_coherent(ws.partial + (tok * n + i2) * (int64_t)sh.pstride + 4 + sh.r + i), w);
+                    w = fmaf(s_rho[tt * 8 + i2], sum_splits(tok, i2, 4 + sh.r + i), w);
+                sv = 2.0f * sigmoid_f(w * inv_n);
+            }
+            s_out[tok * n + i] = sv;
+        }
+    }
+}
+
+// Kernel 1b (only with channel splits): combine the partial records written
+// by k_stream_proj for kRedTokens tokens per workgroup.  Records are summed
+// over splits as 16-byte vectors (one task per token, branch and group of four
+// rows), then over branches with rho applied, in a fixed order.
+constexpr int kRedTokens = 1;
+__global__ void __launch_bounds__(256)
+k_reduce_splits(float *__restrict__ s_out, Workspace ws, FastShape sh, float eps) {
+    __shared__ float s_rho[kRedTokens * 8];
+    __shared__ __attribute__((aligned(16))) float s_p[kRedTokens * 8 * 16 * kMaxRowBlocks];
+    const int n = sh.n, S = sh.ksplit, rows_p = 16 * sh.row_blocks;
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kRedTokens;
+    const int cnt = (int)((sh.N - t0) < kRedTokens ? (sh.N - t0) : kRedTokens);
+    const float inv_n = 1.0f / (float)n;
+    auto rec = [&](int tt, int i, int k) {
+        return ws.partial + (((t0 + tt) * n + i) * S + k) * (int64_t)sh.pstride;
+    };
+    // sums of squares -> rho, rms
+    for (int q = tid; q < cnt * n; q += 256) {
+        const int tt = q / n, i = q % n;
+        float a = 0.f;
+        for (int k = 0; k < S; ++k) a += rec(tt, i, k)[0];
+        const float rms = sqrtf(a / (float)sh.d + eps);
+        s_rho[tt * 8 + i] = 1.0f / rms;
+        ws.rms[(t0 + tt) * n + i] = rms;
+    }
+    __syncthreads();
+    // rho_i * (sum over splits of P_i), four rows per task
+    const int quads = rows_p / 4;
+    for (int q = tid; q < cnt * n * quads; q += 256) {
+        const int tt = q / (n * quads), rem = q % (n * quads), i = rem / quads, qd = rem % quads;
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        int k = 0;
+#pragma unroll 4
+        for (; k + 1 < S; k += 2) {
+            a0 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k) + 4 + 4 * qd);
+            a1 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k + 1) + 4 + 4 * qd);
+        }
+        if (k < S) a0 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k) + 4 + 4 * qd);
+        *reinterpret_cast<f32x4 *>(&s_p[((tt * 8 + i) * rows_p) + 4 * qd]) = (a0 + a1) * s_rho[tt * 8 + i];
+    }
+    __syncthreads();
+    const int outs = sh.rk + n;
+    for (int q = tid; q < cnt * outs; q += 256) {
+        const int tt = q / outs, j = q % outs;
+        const int64_t tok = t0 + tt;
+        if (j < sh.rk) {
+            float v = 0.f;
+            if (j < sh.r) {
+                float z = 0.f;
+                for (int i = 0; i < n; ++i) z += s_p[(tt * 8 + i) * rows_p + j];
+                v = -kLog2e * silu_f(z * inv_n);
+            }
+            const bf16_t h = f32_to_bf16(v);
+            ws.act[(tok * 2) * sh.rk + j] = h;
+            ws.act[(tok * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
+        } else {
+            const int i = j - sh.rk;
+            float sv = 1.0f;
+            if (sh.nw) {
+                float w = 0.f;
+                for (int i2 = 0; i2 < n; ++i2) w += s_p[(tt * 8 + i2) * rows_p + sh.r + i];
                 sv = 2.0f * sigmoid_f(w * inv_n);
             }
             s_out[tok * n + i] = sv;
@@ -394,8 +519,8 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const int g = lane >> 4;
     const int64_t t = tile * kK2Tile + wave * 16 + (lane & 15);
     const bool valid = t < sh.N;
-    const int c_begin = range * kChanPerWg;
-    const int c_end = (c_begin + kChanPerWg) < d ? (c_begin + kChanPerWg) : d;
+    const int c_begin = range * sh.k2_chan;
+    const int c_end = (c_begin + sh.k2_chan) < d ? (c_begin + sh.k2_chan) : d;
     const int nit = (c_end - c_begin) / kChunk;
     const float inv_n = 1.0f / (float)NB;
 
@@ -512,7 +637,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 template <bool FUSED>
 hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     const int64_t tiles8 = (sh.tiles + 7) / 8 * 8;
-    const unsigned grid = (unsigned)(tiles8 * sh.n);
+    const unsigned grid = (unsigned)(tiles8 * sh.n * sh.ksplit);
     const bf16_t *y = (const bf16_t *)a.y;
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
@@ -530,7 +655,7 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
 
 template <int NB>
 hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
-    const int ranges = (sh.d + kChanPerWg - 1) / kChanPerWg;
+    const int ranges = (sh.d + sh.k2_chan - 1) / sh.k2_chan;
     const unsigned grid = (unsigned)(((sh.N + kK2Tile - 1) / kK2Tile) * ranges);
 #define GR_K2(RKS)                                                                          \
     case RKS:                                                                               \
@@ -569,6 +694,11 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     workspace_layout(sh, (char *)a.ws, &w);
     hipError_t e = a.fused ? launch_k1<true>(a, sh, w, st) : launch_k1<false>(a, sh, w, st);
     if (e != hipSuccess) return e;
+    if (sh.ksplit > 1) {
+        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((sh.N + kRedTokens - 1) / kRedTokens)),
+                           dim3(256), 0, st, a.s_out, w, sh, a.eps);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     return launch_k2<4>(a, sh, w, st);
 }
 
