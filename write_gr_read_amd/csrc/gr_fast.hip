@@ -62,6 +62,10 @@ constexpr int kK2WavesPerSimd = GR_K2_WAVES_PER_SIMD;  // occupancy target of ke
 constexpr int kK2Waves = GR_K2_WAVES;                  // waves per kernel-2 workgroup
 constexpr int kK2Threads = 64 * kK2Waves;
 constexpr int kK2Tile = 16 * kK2Waves;                 // tokens per kernel-2 workgroup
+#ifndef GR_K2_SUB
+#define GR_K2_SUB 1
+#endif
+constexpr int kK2Sub = GR_K2_SUB;  // 32-channel chunks per kernel-2 iteration (whole 128-byte lines)
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 #ifndef GR_SPLIT_TARGET
@@ -504,12 +508,15 @@ __global__ void __launch_bounds__(kK2Threads, kK2WavesPerSimd)
 k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
+    constexpr int SUB = kK2Sub;                        // 32-channel chunks per iteration
+    constexpr int KC = SUB * kChunk;                   // channels per iteration
     constexpr int RK = RKS * 32;
     constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
-    constexpr int NV = NB * kChunk * (RK / 8);         // 16-byte vectors of W_up per chunk
+    constexpr int NV = NB * KC * (RK / 8);             // 16-byte vectors of W_up per iteration
     constexpr int WV = (NV + kK2Threads - 1) / kK2Threads;
-    __shared__ __attribute__((aligned(16))) bf16_t lds_u[2][NB * kChunk * kPitch];
-    __shared__ uint32_t lds_g[2][NB * kChunk];  // (gamma/n) of channel cc in the half cc%2 of a word
+    constexpr int NG = (NB * KC + kK2Threads - 1) / kK2Threads;
+    __shared__ __attribute__((aligned(16))) bf16_t lds_u[2][NB * KC * kPitch];
+    __shared__ uint32_t lds_g[2][NB * KC];  // (gamma/n) of channel cc in the half cc%2 of a word
 
     const int d = sh.d, r = sh.r;
     const int64_t b = blockIdx.x;
@@ -521,39 +528,51 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     const bool valid = t < sh.N;
     const int c_begin = range * sh.k2_chan;
     const int c_end = (c_begin + sh.k2_chan) < d ? (c_begin + sh.k2_chan) : d;
-    const int nit = (c_end - c_begin) / kChunk;
+    const int nch = (c_end - c_begin) / kChunk;        // 32-channel chunks of this range
+    const int nit = (nch + SUB - 1) / SUB;
     const float inv_n = 1.0f / (float)NB;
 
+    // W_up rows (branch i, channel c) of one iteration; row index i * KC + cc
     u32x4 wreg[WV];
-    uint32_t greg = 0u;
+    uint32_t greg[NG];
     auto load_w = [&](int it) {
-        const int c0 = c_begin + it * kChunk;
+        const int c0 = c_begin + it * KC;
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kK2Threads;
             const int row = v / (RK / 8), kv = v % (RK / 8);
-            const int i = row / kChunk, cc = row % kChunk;
+            const int i = row / KC, cc = row % KC;
             wreg[q] = u32x4{0u, 0u, 0u, 0u};
-            if (v < NV && it < nit && kv * 8 < r)
+            if (v < NV && it < nit && c0 + cc < c_end && kv * 8 < r)
                 wreg[q] = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
         }
-        if (tid < NB * kChunk && it < nit) {
-            const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)(tid / kChunk) * d + c0 + tid % kChunk]) * inv_n);
-            greg = (tid & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const int v = tid + q * kK2Threads;
+            greg[q] = 0u;
+            if (v < NB * KC && it < nit && c0 + v % KC < c_end) {
+                const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)(v / KC) * d + c0 + v % KC]) * inv_n);
+                greg[q] = (v & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+            }
         }
     };
+    // LDS row of (branch i, channel cc): chunk cc/32, then MFMA row order within it
     auto store_w = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kK2Threads;
             if (v < NV) {
                 const int row = v / (RK / 8), kv = v % (RK / 8);
-                const int i = row / kChunk, cc = row % kChunk;
-                const int pos = i * kChunk + 16 * ((cc >> 2) & 1) + 4 * (cc >> 3) + (cc & 3);
+                const int i = row / KC, cc = row % KC, c32 = cc % kChunk;
+                const int pos = (i * SUB + cc / kChunk) * kChunk + 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
                 *reinterpret_cast<u32x4 *>(&lds_u[buf][pos * kPitch + kv * 8]) = wreg[q];
             }
         }
-        if (tid < NB * kChunk) lds_g[buf][tid] = greg;
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            const int v = tid + q * kK2Threads;
+            if (v < NB * KC) lds_g[buf][v] = greg[q];
+        }
     };
 
     // B operand: -log2(e) SiLU(z) of this lane's token as (hi, lo), k-steps of 32
@@ -576,14 +595,17 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     bf16_t *urow = u + t * (int64_t)d + 8 * g;
     const int m16 = lane & 15;  // A row this lane feeds
 
-    u32x4 s0[NB], s1[NB];
-    auto load_state = [&](int it, u32x4 (&sv)[NB]) {
+    u32x4 s0[SUB][NB], s1[SUB][NB];
+    auto load_state = [&](int it, u32x4 (&sv)[SUB][NB]) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            sv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (valid && it < nit)
-                sv[i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c_begin + it * kChunk);
-        }
+        for (int sc = 0; sc < SUB; ++sc)
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int c0 = c_begin + it * KC + sc * kChunk;
+                sv[sc][i] = u32x4{0u, 0u, 0u, 0u};
+                if (valid && it < nit && c0 < c_end)
+                    sv[sc][i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c0);
+            }
     };
 
     load_w(0);
@@ -593,44 +615,50 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
     __syncthreads();
     for (int it = 0; it < nit; ++it) {
         const int cur = it & 1;
-        const int c0 = c_begin + it * kChunk;
         load_state(it + 1, s1);
-        float uacc[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+        for (int sc = 0; sc < SUB; ++sc) {
+            const int c0 = c_begin + it * KC + sc * kChunk;
+            float uacc[8];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
+            for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                f32x4 tl = {0.f, 0.f, 0.f, 0.f};
-                const bf16_t *ap = &lds_u[cur][(i * kChunk + 16 * h + m16) * kPitch + 8 * g];
+            for (int i = 0; i < NB; ++i) {
 #pragma unroll
-                for (int ks = 0; ks < RKS; ++ks) {
-                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
-                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
-                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
-                }
-                // tl[m] = -log2(e) * l for channel 8g + 4h + m of branch i
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 tl = {0.f, 0.f, 0.f, 0.f};
+                    const bf16_t *ap = &lds_u[cur][((i * SUB + sc) * kChunk + 16 * h + m16) * kPitch + 8 * g];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int e = 4 * h + m;
-                    const float bterm = dot2_bf16(s0[i][e >> 1], lds_g[cur][i * kChunk + 8 * g + e], 0.f);
-                    const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
-                    uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
+                    for (int ks = 0; ks < RKS; ++ks) {
+                        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
+                        tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
+                        tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                    }
+                    // tl[m] = -log2(e) * l for channel 8g + 4h + m of branch i
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int e = 4 * h + m;
+                        const float bterm = dot2_bf16(s0[sc][i][e >> 1],
+                                                      lds_g[cur][i * KC + sc * kChunk + 8 * g + e], 0.f);
+                        const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                        uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
+                    }
                 }
             }
-        }
-        if (valid) {
-            u32x4 o;
+            if (valid && c0 < c_end) {
+                u32x4 o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[2 * e], uacc[2 * e + 1]);
-            *reinterpret_cast<u32x4 *>(urow + c0) = o;
+                for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[2 * e], uacc[2 * e + 1]);
+                *reinterpret_cast<u32x4 *>(urow + c0) = o;
+            }
         }
         if (it + 1 < nit) store_w(cur ^ 1);
         load_w(it + 2);
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < NB; ++i) s0[i] = s1[i];
+        for (int sc = 0; sc < SUB; ++sc)
+#pragma unroll
+            for (int i = 0; i < NB; ++i) s0[sc][i] = s1[sc][i];
     }
 }
 
