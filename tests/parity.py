@@ -7,11 +7,13 @@ Tolerances (written here, used by every GPU parity test):
     for u, the sum of the absolute values of the terms of the n-branch
     combine, (1/n) sum_i |G_i R-hat_i| (eq:use_gate); for a chained state,
     |R^(0)| + sum_u |s^(u) y^(u)| (eq:rcv).  A comes from the oracle's own
-    intermediates.  Reason: a stored bf16 branch value may differ by one ulp
-    between the GPU (fp32 FMA, then round to bf16) and the oracle (exact
-    value rounded once), and a one-ulp change of a term moves a cancelling
-    sum by up to 2^-7 of that term.  Where no A is given the RMS(o)/16 floor
-    applies.  Also reported: max|g-o|/RMS(o) and the relative L2 error.
+    intermediates.  Reason: u is an n-term sum that may cancel; the GPU forms
+    it in fp32 from fp32 gate values (hi/lo bf16 operands on MFMA) and rounds
+    once, so its error is a small multiple of fp32 rounding of the TERMS, not
+    of the result, plus one bf16 ulp of the result.  Where no A is given the
+    RMS(o)/16 floor applies.  Also reported: max|g-o|/RMS(o) and the relative L2 error.
+  * written state (eq:write): bit for bit (check_exact).  Both sides store
+    the exact R + s y rounded once to the state dtype.
   * chained bf16 state after L sublayers (check_chain): each stored value is
     rounded L times, and a rounding decision that differs between the two
     sides (a pre-rounding difference of 1e-7 lands on a bf16 rounding
@@ -58,6 +60,18 @@ def check(name: str, got, ref, dtype: str, rms=None, scale=None):
             raise AssertionError(f"{name}: {int(bad.sum())} elements outside 2e-2 rel (worst at "
                                  f"{idx}: gpu {g[idx]!r} oracle {o[idx]!r}); stats {stats}")
     return stats
+
+
+def check_exact(name: str, got, ref):
+    """Assert bit-for-bit equality of a stored tensor with the oracle's value
+    (the oracle returns the stored values widened to fp64)."""
+    g, o = to64(got), to64(ref)
+    assert g.shape == o.shape, f"{name}: shape {g.shape} vs {o.shape}"
+    diff = g != o
+    if diff.any():
+        idx = tuple(int(v) for v in np.argwhere(diff)[0])
+        raise AssertionError(f"{name}: {int(diff.sum())} of {diff.size} elements differ "
+                             f"(first at {idx}: gpu {g[idx]!r} oracle {o[idx]!r})")
 
 
 def sample_tokens(N: int, k: int, seed: int = 0) -> np.ndarray:

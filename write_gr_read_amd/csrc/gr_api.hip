@@ -81,10 +81,19 @@ gr_status check_layer(const gr_layer *L, gr_dtype dt, const char *fn) {
     return GR_SUCCESS;
 }
 
-// GR_KERNEL_VARIANT=generic forces the shape-generic kernels (A/B checks).
+// GR_KERNEL_VARIANT selects kernels for A/B checks: "generic" forces the
+// shape-generic kernels; "staged" / "resident" force that form of the fast
+// path's second kernel whatever the token count.
 bool force_generic() {
     const char *v = getenv("GR_KERNEL_VARIANT");
     return v && strcmp(v, "generic") == 0;
+}
+
+int k2_variant() {
+    const char *v = getenv("GR_KERNEL_VARIANT");
+    if (v && strcmp(v, "staged") == 0) return 1;
+    if (v && strcmp(v, "resident") == 0) return 2;
+    return 0;
 }
 
 size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
@@ -111,6 +120,7 @@ gr_status run_read(grk::ReadArgs &a, const gr_layer *L, size_t ws_bytes, hipStre
         if (s) return s;
     }
     (void)hipGetLastError();  // clear a stale error so the check below is ours
+    a.k2_variant = k2_variant();
     if (grk::fast_path_ok(a) && !force_generic()) return launched(grk::launch_read_fast(a, st), fn);
     return launched(grk::launch_read_generic(a, st), fn);
 }

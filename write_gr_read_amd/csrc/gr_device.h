@@ -36,16 +36,49 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float a) {
     return __builtin_bit_cast(bf16_t, (__bf16)a);
 }
 
+// eq:write for a bf16 state element: r + s y rounded ONCE to bf16 (nearest
+// even).  fmaf gives r + s y correctly rounded to fp32; rounding that again to
+// bf16 can only go wrong where the fp32 value lies exactly on a bf16 rounding
+// midpoint (low 16 bits 0x8000) while the exact sum does not -- common when s
+// saturates near 0 or 2.  There the sign of the fp32 rounding error decides:
+// s y - v is exact in fp64 (when v is such a midpoint both terms lie within
+// 2^42 of each other), one more fp64 add of r rounds once and keeps the sign.
+// The fp32 value is moved one unit off the midpoint towards the exact sum, and
+// the final bf16 conversion then rounds the right way.  Returns that fp32 value.
+// s_pow2: s is 0 or +-2^k (no mantissa bits).  Then s y is exact with at most
+// 8 significant bits, and r + s y is either exact in fp32 or within 2^-16 of
+// its larger term -- never on a midpoint -- so the check is skipped (s == 1
+// without a write projection; there midpoints are frequent and all exact).
+__device__ __forceinline__ bool write_scale_pow2(float s) {
+    return (__float_as_uint(s) & 0x7fffffu) == 0u;
+}
+__device__ __forceinline__ float write_sum_bf16(float s, float y, float r, bool s_pow2) {
+    float v = fmaf(s, y, r);
+    uint32_t b = __float_as_uint(v);
+    if (__builtin_expect((b & 0xffffu) == 0x8000u && !s_pow2, 0)) {
+        const double e = fma((double)s, (double)y, -(double)v) + (double)r;
+        if (e != 0.0) b += ((e > 0.0) == (v > 0.0)) ? 1u : 0xffffffffu;
+        v = __uint_as_float(b);
+    }
+    return v;
+}
+
 // Storage-type adapters for the generic kernels.
 template <typename T> struct Store;
 template <> struct Store<float> {
     __device__ static __forceinline__ float load(const float *p) { return *p; }
     __device__ static __forceinline__ float round(float v) { return v; }
+    // eq:write, one rounding (fmaf)
+    __device__ static __forceinline__ float write(float s, float y, float r) { return fmaf(s, y, r); }
     __device__ static __forceinline__ void store(float *p, float v) { *p = v; }
 };
 template <> struct Store<bf16_t> {
     __device__ static __forceinline__ float load(const bf16_t *p) { return bf16_to_f32(*p); }
     __device__ static __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+    // eq:write, one rounding to bf16 (stored value, widened)
+    __device__ static __forceinline__ float write(float s, float y, float r) {
+        return round(write_sum_bf16(s, y, r, write_scale_pow2(s)));
+    }
     __device__ static __forceinline__ void store(bf16_t *p, float v) { *p = f32_to_bf16(v); }
 };
 

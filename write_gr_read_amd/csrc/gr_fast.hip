@@ -248,6 +248,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     const float si = (FUSED && valid) ? s_in[t * n + br] : 0.f;
+    const bool sp2 = write_scale_pow2(si);
     bf16_t *rowp = state + (t * n + br) * (int64_t)d + c_base + 8 * g;
     const bf16_t *yrow = FUSED ? y + t * (int64_t)d + c_base + 8 * g : nullptr;
 
@@ -281,8 +282,8 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
             if (FUSED) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(fmaf(si, bf16_lo(yy[0][ks][e]), bf16_lo(rr[0][ks][e])),
-                                       fmaf(si, bf16_hi(yy[0][ks][e]), bf16_hi(rr[0][ks][e])));
+                    w[e] = pack_bf16x2(write_sum_bf16(si, bf16_lo(yy[0][ks][e]), bf16_lo(rr[0][ks][e]), sp2),
+                                       write_sum_bf16(si, bf16_hi(yy[0][ks][e]), bf16_hi(rr[0][ks][e]), sp2));
                 if (valid) *reinterpret_cast<u32x4 *>(rowp + it * KITER + ks * kChunk) = w;
             }
 #pragma unroll
@@ -644,6 +645,9 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
                         uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
                     }
                 }
+                // materialise per branch (else the element work sinks into the store's branch)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(uacc[e]));
             }
             if (valid && c0 < c_end) {
                 u32x4 o;
@@ -659,6 +663,187 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
         for (int sc = 0; sc < SUB; ++sc)
 #pragma unroll
             for (int i = 0; i < NB; ++i) s0[sc][i] = s1[sc][i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2, resident form (many tokens).  One workgroup per (channel range of
+// CH channels, residue class p of the token tiles modulo P).  The W_up rows of
+// the range (every branch, MFMA row order as above) and gamma/n are staged in
+// LDS once; the workgroup then walks the tiles p, p + P, ... in steps of 64
+// channels.  A step reads, per token and branch, one whole 128-byte line of
+// the state (its two 64-byte halves back to back) and writes one whole line of
+// u, so no line is fetched or written in halves.  The next step's state is
+// loaded branch by branch, each as soon as the current step has finished with
+// that branch: the prefetch costs no registers beyond one step's state.  The
+// activations and rms of the next tile are loaded before the state of its
+// first step, so waiting for them never waits for that state.
+constexpr int kResStep = 64;   // channels per step (a 128-byte line of bf16)
+
+template <int RKS> struct ResidentCfg {
+    // channels per workgroup: keeps the staged W_up near 72 KiB (two per CU)
+    static constexpr int CH = RKS <= 2 ? 128 : 64;
+};
+
+#ifndef GR_K2R_WAVES
+#define GR_K2R_WAVES 8
+#endif
+#ifndef GR_K2R_WAVES_PER_SIMD
+#define GR_K2R_WAVES_PER_SIMD 4
+#endif
+constexpr int kResWaves = GR_K2R_WAVES;
+constexpr int kResThreads = 64 * kResWaves;
+constexpr int kResTile = 16 * kResWaves;         // tokens per tile
+constexpr int kResWgsTarget = 512;               // workgroups wanted (two per CU)
+
+template <int NB, int RKS, int CH>
+__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? GR_K2R_WAVES_PER_SIMD : 2)
+k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+                        const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
+                        FastShape sh, int ranges, int P) {
+    constexpr int NC = CH / kChunk;                    // 32-channel chunks per range
+    constexpr int RK = RKS * 32;
+    constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
+    __shared__ __attribute__((aligned(16))) bf16_t lds_u[NB * CH * kPitch];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_g[NB * CH];
+
+    const int d = sh.d, r = sh.r;
+    const int range = (int)(blockIdx.x % ranges);
+    const int64_t p = blockIdx.x / ranges;
+    const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
+    if (p >= tiles) return;                            // whole workgroup
+    const int c_begin = range * CH;
+    const int nchan = (d - c_begin) < CH ? (d - c_begin) : CH;
+    const int nsteps = nchan / kResStep;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m16 = lane & 15;
+    const float inv_n = 1.0f / (float)NB;
+
+    auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
+    auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
+        const int64_t t = token(T);
+        const bool ok = t < sh.N;
+#pragma unroll
+        for (int ks = 0; ks < RKS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+            if (ok) {
+                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
+                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
+            }
+            hi[ks] = as_bf16x8(v);
+            lo[ks] = as_bf16x8(vl);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+    };
+    // state of branch i, step st of tile T: two 16-byte words per lane
+    auto load_state = [&](int64_t T, int st, int i, u32x4 (&sv)[2]) {
+        const int64_t t = token(T);
+        const bf16_t *q = state + t * (int64_t)NB * d + (int64_t)i * d + c_begin + st * kResStep + 8 * g;
+        const bool ok = t < sh.N;
+#pragma unroll
+        for (int sc = 0; sc < 2; ++sc)
+            sv[sc] = ok ? *reinterpret_cast<const u32x4 *>(q + sc * kChunk) : u32x4{0u, 0u, 0u, 0u};
+    };
+
+    bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
+    float rms[NB], nrms[NB];
+    u32x4 sv[NB][2];
+    int64_t T = p;
+    int st = 0;
+    load_act(T, bop, bopl, rms);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load_state(T, 0, i, sv[i]);
+
+    // stage W_up rows (branch i, channel cc of the range) and gamma/n
+    for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
+        const int row = v / (RK / 8), kv = v % (RK / 8);
+        const int i = row / CH, cc = row % CH, c32 = cc % kChunk;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (cc < nchan && kv * 8 < r)
+            w = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8);
+        const int pos = (i * NC + cc / kChunk) * kChunk + 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+        *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w;
+    }
+    for (int v = tid; v < NB * CH; v += kResThreads) {
+        const int i = v / CH, cc = v % CH;
+        uint32_t gw = 0u;
+        if (cc < nchan) {
+            const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)i * d + c_begin + cc]) * inv_n);
+            gw = (cc & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+        }
+        lds_g[v] = gw;
+    }
+    __syncthreads();
+
+    for (;;) {
+        int64_t Tn = T;
+        int sn = st + 1;
+        if (sn == nsteps) { sn = 0; Tn = T + P; }
+        const bool more = Tn < tiles;
+        if (sn == 0 && more) load_act(Tn, nbop, nbopl, nrms);
+
+        float uacc[2][8];
+#pragma unroll
+        for (int sc = 0; sc < 2; ++sc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) uacc[sc][e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int sc = 0; sc < 2; ++sc) {
+                const int chunk = i * NC + st * 2 + sc;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 tl = {0.f, 0.f, 0.f, 0.f};
+                    const bf16_t *ap = &lds_u[(chunk * kChunk + 16 * h + m16) * kPitch + 8 * g];
+#pragma unroll
+                    for (int ks = 0; ks < RKS; ++ks) {
+                        const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
+                        tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
+                        tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                    }
+                    // tl[m] = -log2(e) * l for channel 8g + 4h + m of the chunk, branch i
+                    const uint32_t *gp = &lds_g[i * CH + (st * 2 + sc) * kChunk + 8 * g + 4 * h];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int e = 4 * h + m;
+                        const float bterm = dot2_bf16(sv[i][sc][e >> 1], gp[m], 0.f);
+                        const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                        uacc[sc][e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[sc][e]);
+                    }
+                }
+            }
+            // Materialise the sums here: otherwise the compiler sinks all of the
+            // step's element work into the (token < N) store below and keeps
+            // every MFMA result live at once.
+#pragma unroll
+            for (int sc = 0; sc < 2; ++sc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(uacc[sc][e]));
+            // branch i of this step is consumed: fetch it for the next step
+            if (more) load_state(Tn, sn, i, sv[i]);
+        }
+        const int64_t t = token(T);
+        if (t < sh.N) {
+            bf16_t *q = u + t * (int64_t)d + c_begin + st * kResStep + 8 * g;
+#pragma unroll
+            for (int sc = 0; sc < 2; ++sc) {
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[sc][2 * e], uacc[sc][2 * e + 1]);
+                *reinterpret_cast<u32x4 *>(q + sc * kChunk) = o;
+            }
+        }
+        if (!more) break;
+        if (sn == 0) {
+#pragma unroll
+            for (int ks = 0; ks < RKS; ++ks) { bop[ks] = nbop[ks]; bopl[ks] = nbopl[ks]; }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) rms[i] = nrms[i];
+        }
+        T = Tn;
+        st = sn;
     }
 }
 
@@ -699,6 +884,37 @@ hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     return hipGetLastError();
 }
 
+template <int NB, int RKS>
+hipError_t launch_k2_resident_rks(const ReadArgs &a, const FastShape &sh, const Workspace &w,
+                                  hipStream_t st) {
+    constexpr int CH = ResidentCfg<RKS>::CH;
+    const int ranges = (sh.d + CH - 1) / CH;
+    const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
+    int64_t P = (kResWgsTarget + ranges / 2) / ranges;
+    if (P > tiles) P = tiles;
+    if (P < 1) P = 1;
+    hipLaunchKernelGGL((k_gate_combine_resident<NB, RKS, CH>), dim3((unsigned)(ranges * P)),
+                       dim3(kResThreads), 0, st, (const bf16_t *)a.state, (const bf16_t *)a.gamma,
+                       (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges, (int)P);
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Workspace &w,
+                              hipStream_t st) {
+    switch (sh.rk / 32) {
+    case 1: return launch_k2_resident_rks<NB, 1>(a, sh, w, st);
+    case 2: return launch_k2_resident_rks<NB, 2>(a, sh, w, st);
+    case 3: return launch_k2_resident_rks<NB, 3>(a, sh, w, st);
+    case 4: return launch_k2_resident_rks<NB, 4>(a, sh, w, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// The resident kernel 2 pays a one-off W_up staging per workgroup; it wins
+// once every workgroup walks a few token tiles.
+constexpr int64_t kResidentMinTokens = 4096;
+
 }  // namespace
 
 bool fast_path_ok(const ReadArgs &a) {
@@ -727,7 +943,8 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
                            dim3(256), 0, st, a.s_out, w, sh, a.eps);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return launch_k2<4>(a, sh, w, st);
+    const bool resident = a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
+    return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }
 
 }  // namespace grk

@@ -21,8 +21,8 @@ constexpr int kRowsPerPass = 8;  // projection rows accumulated per sweep
 // workgroup per token.  Every pass walks the row in the same (branch, channel)
 // order with the same thread mapping, so each thread only re-reads elements it
 // wrote itself.
-//   FUSED: R' = R + s_in y is computed, rounded, stored, and the read then uses
-//   the stored R'.
+//   FUSED: R' = R + s_in y is computed, rounded once to the state dtype,
+//   stored, and the read then uses the stored R'.
 template <typename T, bool FUSED>
 __global__ void __launch_bounds__(kGenThreads)
 k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__restrict__ s_in,
@@ -44,7 +44,7 @@ k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__re
         for (int c = tid; c < d; c += kGenThreads) {
             float v = Store<T>::load(Rt + (int64_t)i * d + c);
             if (FUSED) {
-                v = Store<T>::round(fmaf(si, Store<T>::load(y + t * d + c), v));
+                v = Store<T>::write(si, Store<T>::load(y + t * d + c), v);
                 Store<T>::store(Rt + (int64_t)i * d + c, v);
             }
             ss = fmaf(v, v, ss);
@@ -119,13 +119,14 @@ k_write(T *__restrict__ state, const T *__restrict__ y, const float *__restrict_
         const int64_t ti = q / dv;  // t * n + i
         const int64_t t = ti / n;
         const float si = s[ti];
+        const bool sp2 = write_scale_pow2(si);
         u32x4 rv = *reinterpret_cast<const u32x4 *>(state + q * VEC);
         const u32x4 yv = *reinterpret_cast<const u32x4 *>(y + (t * dv + cv) * VEC);
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float lo = fmaf(si, bf16_lo(yv[e]), bf16_lo(rv[e]));
-                const float hi = fmaf(si, bf16_hi(yv[e]), bf16_hi(rv[e]));
+                const float lo = write_sum_bf16(si, bf16_lo(yv[e]), bf16_lo(rv[e]), sp2);
+                const float hi = write_sum_bf16(si, bf16_hi(yv[e]), bf16_hi(rv[e]), sp2);
                 rv[e] = pack_bf16x2(lo, hi);
             }
         } else {

@@ -22,6 +22,7 @@ struct ReadArgs {
     float *s_out;        // [N][n]
     void *ws;            // workspace (device)
     size_t ws_bytes;
+    int k2_variant;      // fast path's second kernel: 0 by size, 1 staged, 2 resident
 };
 
 hipError_t launch_read_generic(const ReadArgs &a, hipStream_t st);
