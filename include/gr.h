@@ -128,9 +128,9 @@ gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps,
                                gr_dtype dt, int64_t N, int32_t d, void *stream);
 
 /* Bytes of workspace `op` needs for N tokens of layer L (may be 0).
- * A workspace must be zero-filled (e.g. hipMemset) before the first call that
- * uses it; every call leaves it ready for the next one.  Calls that share a
- * workspace must not run concurrently (same stream, or synchronised). */
+ * The workspace needs no initialisation: a call writes every byte it reads.
+ * Calls that share a workspace must not run concurrently (same stream, or
+ * synchronised). */
 gr_status gr_workspace_size(int op, gr_dtype dt, int64_t N, const gr_layer *L, size_t *bytes);
 
 /* Static description of a status code. */

@@ -119,6 +119,27 @@ def test_saturating_gate(N, d, r, w_std):
     run_read_write_fused(X, f"saturating-N{N}-d{d}-r{r}")
 
 
+def test_workspace_needs_no_initialisation():
+    """Every workspace byte a call reads is written earlier in the same call:
+    a workspace full of 0xFF (NaN floats, huge counts) changes nothing."""
+    X = inputs.make_gr_inputs(300, 4, 1024, 32, "bf16", seed=45)
+    p0, p1 = dev_params(X.params[0]), dev_params(X.params[1])
+    R = X.X.to(DEV)
+    y = X.y.to(DEV)
+    s_in = torch.full((300, 4), 0.75, device=DEV)
+    runs = []
+    for fill in (0xFF, 0x00):
+        gr.read(R, p0)  # make sure the per-device workspace exists
+        gr._workspaces[torch.device(DEV)].fill_(fill)
+        Rc = R.clone()
+        u, s = gr.fused_write_read(Rc, y, s_in, p1)
+        torch.cuda.synchronize()
+        runs.append((Rc.cpu(), u.cpu(), s.cpu()))
+    for a, b in zip(runs[0], runs[1]):
+        assert torch.equal(a, b)
+    assert torch.isfinite(runs[0][1].float()).all()
+
+
 def test_no_write_projection_gives_unit_strength():
     X = inputs.make_gr_inputs(40, 4, 256, 16, "bf16", seed=41, with_write=False)
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))

@@ -140,13 +140,13 @@ _workspaces = {}
 
 
 def _workspace(device, nbytes: int) -> Tuple[int, int]:
-    """Per-device scratch buffer, grown on demand (used on the current stream).
-    Zero-filled when allocated, as the library requires before first use."""
+    """Per-device scratch buffer, grown on demand (used on the current stream;
+    the library needs no initialisation of it)."""
     if nbytes == 0:
         return 0, 0
     buf = _workspaces.get(device)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[device] = buf
     return buf.data_ptr(), buf.numel()
 

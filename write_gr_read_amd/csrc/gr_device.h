@@ -63,6 +63,34 @@ __device__ __forceinline__ float write_sum_bf16(float s, float y, float r, bool 
     return v;
 }
 
+// Eight eq:write elements of a bf16 state: packed y and r words (low half =
+// even channel) -> packed stored words, each the exact r + s y rounded once.
+// The midpoint test runs on all eight sums; the fp64 tie-break (rare) is one
+// branch for the group.
+__device__ __forceinline__ u32x4 write8_bf16(float s, bool s_pow2, u32x4 y, u32x4 r) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = fmaf(s, bf16_lo(y[e]), bf16_lo(r[e]));
+        v[2 * e + 1] = fmaf(s, bf16_hi(y[e]), bf16_hi(r[e]));
+    }
+    bool mid = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mid |= (__float_as_uint(v[k]) & 0xffffu) == 0x8000u;
+    if (__builtin_expect(mid && !s_pow2, 0)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float yk = (k & 1) ? bf16_hi(y[k >> 1]) : bf16_lo(y[k >> 1]);
+            const float rk = (k & 1) ? bf16_hi(r[k >> 1]) : bf16_lo(r[k >> 1]);
+            v[k] = write_sum_bf16(s, yk, rk, false);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    return o;
+}
+
 // Storage-type adapters for the generic kernels.
 template <typename T> struct Store;
 template <> struct Store<float> {

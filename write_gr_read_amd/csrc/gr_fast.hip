@@ -3,8 +3,11 @@
 // sec. 4 Gated Residual: eq:rms, eq:gate, eq:use_gate, eq:s; eq:write first
 // when fused; sec. 7: read fused into one traversal with Group RMSNorm).
 //
-// Two kernels, no inter-workgroup waiting (so no co-residency assumption):
+// Four kernels in stream order, no inter-workgroup waiting (so no
+// co-residency assumption):
 //
+// k_prep_wprime   (many tokens) W' = (W_down ; W_write) . gamma per branch,
+//                 split once into bf16 hi / lo planes for the whole call.
 // k_stream_proj   one workgroup per (token tile of 16*WAVES tokens, branch i).
 //                 Streams branch i of the tile once: (fused) R' = R + s_i y in
 //                 fp32, rounded to bf16 and stored; sum of squares of the stored
@@ -14,11 +17,13 @@
 //                 gain gamma_i folded in.  Because
 //                     W_down vec(R-hat) = sum_i rho_i W_down^{(i)} (gamma_i . R_i)
 //                 the projections need no second sweep: rho_i is applied after.
-//                 Each workgroup writes (ss_i, P_i) for its tokens; the last of
-//                 the n workgroups of a tile to finish (atomic ticket) combines
-//                 them: rho_i = (ss_i/d + eps)^-1/2, z = (1/n) sum_i rho_i P_i,
-//                 a = SiLU(z), s = 2 sigmoid((1/n) sum_i rho_i P_i[r + .]).
-// k_gate_combine  one workgroup per (token tile, channel range).  Up projection
+//                 Each workgroup writes a record (ss_i, P_i) per token.
+// k_reduce_records  one wave per token: rho_i = (ss_i/d + eps)^-1/2,
+//                 z = (1/n) sum_i rho_i P_i, a = SiLU(z),
+//                 s = 2 sigmoid((1/n) sum_i rho_i P_i[r + .]).
+// k_gate_combine  one workgroup per (token tile, channel range) -- or, for
+//                 many tokens, per (channel range, tile residue), walking
+//                 tiles with the range's W_up resident.  Up projection
 //                 t = W_up (-log2(e) a) on MFMA, then per element
 //                 G_i rho_i = 1 / ((1 + 2^t) rms_i) and
 //                 u_c = sum_i (gamma_ic / n) R'_ic / ((1 + 2^t_ic) rms_i).
@@ -48,10 +53,17 @@ constexpr int kChunk = 32;                // channels per MFMA k-step
 #define GR_K1_ITER 64
 #endif
 #ifndef GR_K1_DEPTH
-#define GR_K1_DEPTH 2
+#define GR_K1_DEPTH 1             // many tokens (with the W' prep)
+#endif
+#ifndef GR_K1_DEPTH_SPLIT
+#define GR_K1_DEPTH_SPLIT 2       // few tokens: short channel splits need a deeper pipeline
 #endif
 constexpr int kIter = GR_K1_ITER;         // channels per pipelined iteration (kernel 1)
-constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight
+constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight (with prep)
+constexpr int kDepthSplit = GR_K1_DEPTH_SPLIT;  // ... without (few tokens)
+#ifndef GR_K1_STATIC_RING
+#define GR_K1_STATIC_RING 0
+#endif
 #ifndef GR_K2_WAVES_PER_SIMD
 #define GR_K2_WAVES_PER_SIMD 3
 #endif
@@ -72,6 +84,12 @@ constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgro
 #define GR_SPLIT_TARGET 64
 #endif
 constexpr int kSplitTarget = GR_SPLIT_TARGET;  // kernel-1 workgroups wanted before splitting channels
+constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power of two)
+#ifndef GR_PREP_MIN_TILES
+#define GR_PREP_MIN_TILES 8
+#endif
+constexpr int kPrepMinTiles = GR_PREP_MIN_TILES;  // token tiles from which W' is split once per call
+
 
 struct FastShape {
     int n, d, r, nw;     // nw = n if W_write given, else 0
@@ -82,6 +100,7 @@ struct FastShape {
     int ksplit_chan;     // channels per split (multiple of kIter)
     int k2_chan;         // channels per kernel-2 workgroup (multiple of kChunk)
     int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
+    bool prep;           // W' split once per call by k_prep_wprime (enough token tiles)
     int64_t N, tiles;
 };
 
@@ -99,7 +118,8 @@ FastShape shape_of(const ReadArgs &a) {
     // channels of kernel 1 (partial records are summed in the tile reduction)
     // and narrow the channel range of kernel 2.
     int ks = 1;
-    while (s.tiles * s.n * ks < kSplitTarget && (s.d / (ks * 2)) % kIter == 0 && s.d / (ks * 2) >= 2 * kIter)
+    while (s.tiles * s.n * ks < kSplitTarget && ks < kMaxSplit && (s.d / (ks * 2)) % kIter == 0 &&
+           s.d / (ks * 2) >= 2 * kIter)
         ks *= 2;
     s.ksplit = ks;
     s.ksplit_chan = s.d / ks;
@@ -107,19 +127,21 @@ FastShape shape_of(const ReadArgs &a) {
     const int64_t tiles2 = (a.N + kK2Tile - 1) / kK2Tile;
     while (tiles2 * ((s.d + c2 - 1) / c2) < 1024 && c2 > kChunk && (c2 / 2) % kChunk == 0) c2 /= 2;
     s.k2_chan = c2;
+    s.prep = s.tiles >= kPrepMinTiles;
     return s;
 }
 
-// Workspace layout (all offsets 256-byte aligned):
-//   counters  [tiles] uint64      arrivals per tile (zero between calls)
+// Workspace layout (all offsets 256-byte aligned; every region is written
+// before it is read within a call, so no initialisation is needed):
 //   partial   [N][n][ksplit][pstride] f32: ss at [0], projection rows at [4 ..]
 //   act       [N][2][rk] bf16     -log2(e) SiLU(z) as hi, lo words, zero-padded
 //   rms       [N][n] f32          1/rho
+//   wprime    [n][2][16*row_blocks][d] bf16   W' hi and lo planes (when prep)
 struct Workspace {
-    unsigned long long *counters;
     float *partial;
     bf16_t *act;
     float *rms;
+    bf16_t *wprime;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -127,29 +149,20 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t workspace_layout(const FastShape &s, char *base, Workspace *w) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    size_t o_cnt = take(sizeof(unsigned long long) * s.tiles);
     size_t o_par = take(sizeof(float) * s.N * s.n * s.ksplit * s.pstride);
     size_t o_act = take(sizeof(bf16_t) * s.N * 2 * s.rk);
     size_t o_rms = take(sizeof(float) * s.N * s.n);
+    size_t o_wp = take(sizeof(bf16_t) * (size_t)s.n * 2 * 16 * s.row_blocks * s.d);
     if (w) {
-        w->counters = (unsigned long long *)(base + o_cnt);
         w->partial = (float *)(base + o_par);
         w->act = (bf16_t *)(base + o_act);
         w->rms = (float *)(base + o_rms);
+        w->wprime = (bf16_t *)(base + o_wp);
     }
     return off;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// s_waitcnt with vmcnt = 0 and the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-// Device-coherent load (agent-scope relaxed atomic: misses stale caches).
-__device__ __forceinline__ float ld_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -157,33 +170,79 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-template <bool COHERENT>
-__device__ void combine_records(const Workspace &ws, const FastShape &sh, float eps,
-                                float *__restrict__ s_out, int64_t t0, int cnt, int tid,
-                                int nthreads, float *s_rho);
+// W' = W (.) gamma for 8 channels (one 16-byte vector of each), as bf16 hi
+// and lo words: hi = bf16(x), lo = bf16(x - hi); x = w * gamma is exact in fp32.
+__device__ __forceinline__ void split_wprime(u32x4 w, u32x4 gm, u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo(w[e]) * bf16_lo(gm[e]);
+        const float x1 = bf16_hi(w[e]) * bf16_hi(gm[e]);
+        hi[e] = pack_bf16x2(x0, x1);
+        lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
+    }
+}
+
+// W' of every branch for the whole call: rows j < r of W_down, r..r+nw-1 of
+// W_write, zero up to 16*row_blocks; times gamma; bf16 hi and lo planes,
+// [n][2][rows][d].  The same arithmetic as kernel 1's own split.
+__global__ void __launch_bounds__(256)
+k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
+              const bf16_t *__restrict__ ww, Workspace ws, FastShape sh) {
+    const int d8 = sh.d / 8, rows_p = 16 * sh.row_blocks;
+    const int64_t total = (int64_t)sh.n * rows_p * d8;
+    const int64_t nd = (int64_t)sh.n * sh.d;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+        const int cv = (int)(q % d8);
+        const int64_t rest = q / d8;
+        const int j = (int)(rest % rows_p), i = (int)(rest / rows_p);
+        const int64_t col = (int64_t)i * sh.d + cv * 8;
+        const bf16_t *src = j < sh.r ? wd + (int64_t)j * nd
+                          : (j < sh.rows ? ww + (int64_t)(j - sh.r) * nd : nullptr);
+        u32x4 w = {0u, 0u, 0u, 0u}, gm = {0u, 0u, 0u, 0u};
+        if (src) {
+            w = *reinterpret_cast<const u32x4 *>(src + col);
+            gm = *reinterpret_cast<const u32x4 *>(gamma + col);
+        }
+        u32x4 hi, lo;
+        split_wprime(w, gm, hi, lo);
+        *reinterpret_cast<u32x4 *>(ws.wprime + ((int64_t)(i * 2) * rows_p + j) * sh.d + cv * 8) = hi;
+        *reinterpret_cast<u32x4 *>(ws.wprime + ((int64_t)(i * 2 + 1) * rows_p + j) * sh.d + cv * 8) = lo;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
 // the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
 // that XCD's L2) and consecutive dispatch slots.
 //
-// Pipeline per iteration of kIter channels: the state / y of the iteration
-// two ahead are loaded into registers, the W' chunk of the next iteration
-// (loaded into registers during the previous one) is split into hi/lo and
-// written to the other LDS buffer, and the W' chunk after that is loaded.
-template <bool FUSED, int NRB, int KITER, int DEPTH>
-__global__ void __launch_bounds__(kThreads)
+// W' (W_down / W_write rows of the branch times gamma, as bf16 hi and lo
+// planes) is either formed here per chunk (PREP = false) or read ready-made
+// from the workspace, where k_prep_wprime wrote it once for the call
+// (PREP = true: every token tile would otherwise redo the same split).
+//
+// Pipeline per iteration of KITER channels: the state / y of the iteration
+// DEPTH ahead are loaded into registers, the W' chunk of the next iteration
+// (loaded into registers during the previous one) is written to the other LDS
+// buffer, and the W' chunk after that is loaded.  The register ring of state /
+// y is shifted by copies after each iteration (GR_K1_STATIC_RING=1 unrolls
+// the loop by DEPTH + 1 instead; it needs more registers).
+#ifndef GR_K1_WAVES_PER_SIMD
+#define GR_K1_WAVES_PER_SIMD 4
+#endif
+template <bool FUSED, int NRB, int KITER, int DEPTH, bool PREP>
+__global__ void __launch_bounds__(kThreads, NRB <= 5 ? GR_K1_WAVES_PER_SIMD : 2)
 k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
-              const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, float *__restrict__ s_out,
-              Workspace ws, FastShape sh, float eps) {
+              const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
+              FastShape sh) {
     constexpr int KS = KITER / kChunk;                 // MFMA k-steps per iteration
     constexpr int kPitch = KITER + 8;                  // bf16 per staged row
-    constexpr int NV = NRB * 16 * (KITER / 8);         // 16-byte vectors of W' per iteration
-    constexpr int WV = (NV + kThreads - 1) / kThreads; // ... per thread
+    constexpr int NV = NRB * 16 * (KITER / 8);         // 16-byte vectors of W' per iteration (per plane)
+    constexpr int WV = PREP ? (2 * NV + kThreads - 1) / kThreads  // hi and lo planes, ready-made
+                            : (NV + kThreads - 1) / kThreads;     // W and gamma, split here
+    constexpr int NSLOT = DEPTH + 1;
     // [buffer][hi/lo][row][k]
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
-    __shared__ int s_last;
 
     const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
@@ -199,27 +258,38 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     const int64_t nd = (int64_t)n * d;
     const int nit = sh.ksplit_chan / KITER;
     const int c_base = split * sh.ksplit_chan;  // first channel of this split
+    const int rows_p = NRB * 16;
 
-    // W' staging: row j < r from W_down, rows r..r+nw-1 from W_write, the rest
-    // zero; times gamma of branch br; stored as bf16 hi and lo planes.
-    u32x4 wreg[WV], greg[WV];
+    // W' staging.  PREP: vector v < NV of the hi plane, NV + v of the lo plane.
+    // Else: row j < r from W_down, rows r..r+nw-1 from W_write, the rest zero;
+    // times gamma of branch br; split into bf16 hi and lo planes here.
+    u32x4 wreg[WV], greg[PREP ? 1 : WV];
     auto load_w = [&](int it) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kThreads;
-            const int row = v / (KITER / 8), cv = v % (KITER / 8);
-            const bf16_t *src = nullptr;
-            if (v < NV && it < nit) {
-                if (row < sh.r) src = wd + (int64_t)row * nd;
-                else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
-            }
-            if (src) {
-                const int64_t col = (int64_t)br * d + c_base + it * KITER + cv * 8;
-                wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
-                greg[q] = *reinterpret_cast<const u32x4 *>(gamma + col);
-            } else {
+            if (PREP) {
+                const int plane = v / NV, rem = v % NV;
+                const int row = rem / (KITER / 8), cv = rem % (KITER / 8);
                 wreg[q] = u32x4{0u, 0u, 0u, 0u};
-                greg[q] = u32x4{0u, 0u, 0u, 0u};
+                if (v < 2 * NV && it < nit)
+                    wreg[q] = *reinterpret_cast<const u32x4 *>(
+                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + it * KITER + cv * 8);
+            } else {
+                const int row = v / (KITER / 8), cv = v % (KITER / 8);
+                const bf16_t *src = nullptr;
+                if (v < NV && it < nit) {
+                    if (row < sh.r) src = wd + (int64_t)row * nd;
+                    else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
+                }
+                if (src) {
+                    const int64_t col = (int64_t)br * d + c_base + it * KITER + cv * 8;
+                    wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
+                    greg[PREP ? 0 : q] = *reinterpret_cast<const u32x4 *>(gamma + col);
+                } else {
+                    wreg[q] = u32x4{0u, 0u, 0u, 0u};
+                    greg[PREP ? 0 : q] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
         }
     };
@@ -227,16 +297,16 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kThreads;
-            if (v < NV) {
+            if (PREP) {
+                if (v < 2 * NV) {
+                    const int plane = v / NV, rem = v % NV;
+                    const int row = rem / (KITER / 8), cv = rem % (KITER / 8);
+                    *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + cv * 8]) = wreg[q];
+                }
+            } else if (v < NV) {
                 const int row = v / (KITER / 8), cv = v % (KITER / 8);
                 u32x4 hi, lo;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x0 = bf16_lo(wreg[q][e]) * bf16_lo(greg[q][e]);
-                    const float x1 = bf16_hi(wreg[q][e]) * bf16_hi(greg[q][e]);
-                    hi[e] = pack_bf16x2(x0, x1);
-                    lo[e] = pack_bf16x2(x0 - bf16_lo(hi[e]), x1 - bf16_hi(hi[e]));
-                }
+                split_wprime(wreg[q], greg[PREP ? 0 : q], hi, lo);
                 *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kPitch + cv * 8]) = hi;
                 *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kPitch + cv * 8]) = lo;
             }
@@ -252,8 +322,8 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     bf16_t *rowp = state + (t * n + br) * (int64_t)d + c_base + 8 * g;
     const bf16_t *yrow = FUSED ? y + t * (int64_t)d + c_base + 8 * g : nullptr;
 
-    // data ring: slot 0 is the iteration being computed, slots 1..DEPTH are in flight
-    u32x4 rr[DEPTH + 1][KS], yy[DEPTH + 1][KS];
+    // data ring: slot it % NSLOT holds iteration it
+    u32x4 rr[NSLOT][KS], yy[NSLOT][KS];
     auto load_data = [&](int it, int slot) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -272,18 +342,15 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 #pragma unroll
     for (int q = 0; q < DEPTH; ++q) load_data(q, q);
     __syncthreads();
-    for (int it = 0; it < nit; ++it) {
+    // one iteration of KITER channels on ring slot `slot`
+    auto iteration = [&](int it, int slot) {
         const int cur = it & 1;
-        load_data(it + DEPTH, DEPTH);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             // eq:write, stored; the read below uses the stored (rounded) values
-            u32x4 w = rr[0][ks];
+            u32x4 w = rr[slot][ks];
             if (FUSED) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(write_sum_bf16(si, bf16_lo(yy[0][ks][e]), bf16_lo(rr[0][ks][e]), sp2),
-                                       write_sum_bf16(si, bf16_hi(yy[0][ks][e]), bf16_hi(rr[0][ks][e]), sp2));
+                w = write8_bf16(si, sp2, yy[slot][ks], rr[slot][ks]);
                 if (valid) *reinterpret_cast<u32x4 *>(rowp + it * KITER + ks * kChunk) = w;
             }
 #pragma unroll
@@ -302,6 +369,24 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         if (it + 1 < nit) store_w(cur ^ 1);
         load_w(it + 2);
         __syncthreads();
+    };
+#if GR_K1_STATIC_RING
+    for (int it0 = 0; it0 < nit; it0 += NSLOT) {
+#pragma unroll
+        for (int ph = 0; ph < NSLOT; ++ph) {
+            const int it = it0 + ph;
+            if (it < nit) {
+                const int slot = ph;
+                load_data(it + DEPTH, (ph + DEPTH) % NSLOT);
+                iteration(it, slot);
+            }
+        }
+    }
+#else
+    for (int it = 0; it < nit; ++it) {
+        const int slot = 0;
+        load_data(it + DEPTH, DEPTH);
+        iteration(it, slot);
 #pragma unroll
         for (int q = 0; q < DEPTH; ++q)
 #pragma unroll
@@ -310,184 +395,80 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                 yy[q][ks] = yy[q + 1][ks];
             }
     }
+#endif
     // the four lane groups of a token hold disjoint channels: sum them
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
 
-    // Publish (ss, P) of this branch.  The records are written with
-    // device-coherent stores (write-through past this XCD's L2) and drained
-    // before the ticket is taken, so the last workgroup -- which may run on
-    // another XCD -- reads them with device-coherent loads.  No L2 writeback
-    // (agent-scope release fence) is needed, which would otherwise flush the
-    // whole L2 full of freshly streamed state.
-    if (valid && S > 1) {
-        // read by k_reduce_splits after this kernel: plain stores
+    // The record (ss, P) of this (token, branch, split); k_reduce_records,
+    // launched next on the same stream, combines them.
+    if (valid) {
         float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
         if (g == 0) rec[0] = ss;
 #pragma unroll
         for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
-    } else if (valid) {
-        float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
-        if (g == 0) __hip_atomic_store(rec, ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Kernel 1b: combine the partial records written by k_stream_proj.  One wave
+// per token, four tokens per workgroup: lanes 0..NB-1 sum the squares over
+// the splits (rho_i, rms_i; shared by shuffles), then each lane owns outputs
+// j = lane, lane + 64, ...: the split sums of P_i[j] for every branch (lanes
+// read consecutive j: coalesced; four splits in flight per chain), rho
+// applied, summed over branches in order.
+//   j < r        z = (1/n) sum_i rho_i P_i[j]  ->  -log2(e) SiLU(z) as (hi, lo)
+//   r <= j < rk  zero padding of the up projection's k-steps
+//   rk + i       s_i = 2 sigmoid((1/n) sum_i' rho_i' P_i'[r + i])  (1 without W_write)
+constexpr int kRedWaves = 4;
+template <int NB, int S>
+__global__ void __launch_bounds__(64 * kRedWaves)
+k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kRedWaves + (threadIdx.x >> 6);
+    if (t >= sh.N) return;  // whole wave
+    const int ps = sh.pstride;
+    const float inv_n = 1.0f / (float)NB;
+    const float *rec = ws.partial + t * NB * S * (int64_t)ps;  // (i, k) at (i*S + k)*pstride
+    // sum over the S splits of record word `off` of branch i (pairwise, fixed order)
+    auto split_sum = [&](int i, int off) {
+        const float *q = rec + (int64_t)i * S * ps + off;
+        float v[S];
 #pragma unroll
-        for (int k = 0; k < NRB; ++k) {
-            unsigned long long *q = reinterpret_cast<unsigned long long *>(rec + 4 + 16 * k + 4 * g);
-            __hip_atomic_store(q, __builtin_bit_cast(unsigned long long, float2{acc[k][0], acc[k][1]}),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(q + 1, __builtin_bit_cast(unsigned long long, float2{acc[k][2], acc[k][3]}),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    // With channel splits the records are combined by k_reduce_splits after
-    // this kernel (many workgroups share that work); without, the last of the
-    // n workgroups of the tile combines them here.
-    if (S > 1) return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's stores are performed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned long long old =
-            __hip_atomic_fetch_add(ws.counters + tile, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (unsigned long long)(n * S - 1));
-        // every arrival of this call is in: leave the counter at zero
-        if (s_last) __hip_atomic_store(ws.counters + tile, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-
-    const int64_t t0 = tile * kTile;
-    const int cnt = (int)((sh.N - t0) < kTile ? (sh.N - t0) : kTile);
-    __shared__ float s_rho[kTile * 8];
-    combine_records<true>(ws, sh, eps, s_out, t0, cnt, tid, kThreads, s_rho);
-}
-
-// Combine the partial records of tokens [t0, t0 + cnt): rho_i and rms_i from
-// the summed squares, z = (1/n) sum_i rho_i P_i (rows < r), stored as
-// -log2(e) SiLU(z) in (hi, lo) bf16 words, and s = 2 sigmoid(...) from the
-// write rows.  Records are summed over splits and branches in a fixed order.
-// COHERENT: records were published in this kernel (device-coherent loads).
-template <bool COHERENT>
-__device__ void combine_records(const Workspace &ws, const FastShape &sh, float eps,
-                                float *__restrict__ s_out, int64_t t0, int cnt, int tid,
-                                int nthreads, float *s_rho /* [cnt][8] */) {
-    const int n = sh.n, S = sh.ksplit;
-    const float inv_n = 1.0f / (float)n;
-    auto rec = [&](int64_t tok, int i, int k) {
-        return ws.partial + ((tok * n + i) * S + k) * (int64_t)sh.pstride;
+        for (int k = 0; k < S; ++k) v[k] = q[k * ps];
+#pragma unroll
+        for (int w = 1; w < S; w *= 2)
+#pragma unroll
+            for (int k = 0; k + w < S; k += 2 * w) v[k] += v[k + w];
+        return v[0];
     };
-    auto ld = [&](const float *p) { return COHERENT ? ld_coherent(p) : *p; };
-    auto sum_splits = [&](int64_t tok, int i, int off) {
-        float a0 = 0.f, a1 = 0.f;
-        int k = 0;
-        for (; k + 1 < S; k += 2) {
-            a0 += ld(rec(tok, i, k) + off);
-            a1 += ld(rec(tok, i, k + 1) + off);
-        }
-        if (k < S) a0 += ld(rec(tok, i, k) + off);
-        return a0 + a1;
-    };
-    for (int q = tid; q < cnt * n; q += nthreads) {
-        const int tt = q / n, i = q % n;
-        const float ms = sum_splits(t0 + tt, i, 0) / (float)sh.d + eps;
-        const float rms = sqrtf(ms);
-        s_rho[tt * 8 + i] = 1.0f / rms;
-        ws.rms[(t0 + tt) * n + i] = rms;
+    float rho_l = 0.f;
+    if (lane < NB) {
+        const float rms = sqrtf(split_sum(lane, 0) / (float)sh.d + eps);
+        rho_l = 1.0f / rms;
+        ws.rms[t * NB + lane] = rms;
     }
-    __syncthreads();
-    const int outs = sh.rk + n;
-    for (int q = tid; q < cnt * outs; q += nthreads) {
-        const int tt = q / outs, j = q % outs;
-        const int64_t tok = t0 + tt;
+    float rho[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rho[i] = __shfl(rho_l, i, 64);
+    auto proj = [&](int row) {  // sum_i rho_i (sum over splits of P_i[row]), i in order
+        float p[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) p[i] = split_sum(i, 4 + row);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) z = fmaf(rho[i], p[i], z);
+        return z;
+    };
+    const int outs = sh.rk + NB;
+    for (int j = lane; j < outs; j += 64) {
         if (j < sh.rk) {
-            float v = 0.f;
-            if (j < sh.r) {
-                float z = 0.f;
-                for (int i = 0; i < n; ++i) z = fmaf(s_rho[tt * 8 + i], sum_splits(tok, i, 4 + j), z);
-                v = -kLog2e * silu_f(z * inv_n);
-            }
+            const float v = j < sh.r ? -kLog2e * silu_f(proj(j) * inv_n) : 0.f;
             const bf16_t h = f32_to_bf16(v);
-            ws.act[(tok * 2) * sh.rk + j] = h;
-            ws.act[(tok * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
+            ws.act[(t * 2) * sh.rk + j] = h;
+            ws.act[(t * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
         } else {
             const int i = j - sh.rk;
-            float sv = 1.0f;
-            if (sh.nw) {
-                float w = 0.f;
-                for (int i2 = 0; i2 < n; ++i2)
-                    w = fmaf(s_rho[tt * 8 + i2], sum_splits(tok, i2, 4 + sh.r + i), w);
-                sv = 2.0f * sigmoid_f(w * inv_n);
-            }
-            s_out[tok * n + i] = sv;
-        }
-    }
-}
-
-// Kernel 1b (only with channel splits): combine the partial records written
-// by k_stream_proj for kRedTokens tokens per workgroup.  Records are summed
-// over splits as 16-byte vectors (one task per token, branch and group of four
-// rows), then over branches with rho applied, in a fixed order.
-constexpr int kRedTokens = 1;
-__global__ void __launch_bounds__(256)
-k_reduce_splits(float *__restrict__ s_out, Workspace ws, FastShape sh, float eps) {
-    __shared__ float s_rho[kRedTokens * 8];
-    __shared__ __attribute__((aligned(16))) float s_p[kRedTokens * 8 * 16 * kMaxRowBlocks];
-    const int n = sh.n, S = sh.ksplit, rows_p = 16 * sh.row_blocks;
-    const int tid = threadIdx.x;
-    const int64_t t0 = (int64_t)blockIdx.x * kRedTokens;
-    const int cnt = (int)((sh.N - t0) < kRedTokens ? (sh.N - t0) : kRedTokens);
-    const float inv_n = 1.0f / (float)n;
-    auto rec = [&](int tt, int i, int k) {
-        return ws.partial + (((t0 + tt) * n + i) * S + k) * (int64_t)sh.pstride;
-    };
-    // sums of squares -> rho, rms
-    for (int q = tid; q < cnt * n; q += 256) {
-        const int tt = q / n, i = q % n;
-        float a = 0.f;
-        for (int k = 0; k < S; ++k) a += rec(tt, i, k)[0];
-        const float rms = sqrtf(a / (float)sh.d + eps);
-        s_rho[tt * 8 + i] = 1.0f / rms;
-        ws.rms[(t0 + tt) * n + i] = rms;
-    }
-    __syncthreads();
-    // rho_i * (sum over splits of P_i), four rows per task
-    const int quads = rows_p / 4;
-    for (int q = tid; q < cnt * n * quads; q += 256) {
-        const int tt = q / (n * quads), rem = q % (n * quads), i = rem / quads, qd = rem % quads;
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        int k = 0;
-#pragma unroll 4
-        for (; k + 1 < S; k += 2) {
-            a0 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k) + 4 + 4 * qd);
-            a1 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k + 1) + 4 + 4 * qd);
-        }
-        if (k < S) a0 += *reinterpret_cast<const f32x4 *>(rec(tt, i, k) + 4 + 4 * qd);
-        *reinterpret_cast<f32x4 *>(&s_p[((tt * 8 + i) * rows_p) + 4 * qd]) = (a0 + a1) * s_rho[tt * 8 + i];
-    }
-    __syncthreads();
-    const int outs = sh.rk + n;
-    for (int q = tid; q < cnt * outs; q += 256) {
-        const int tt = q / outs, j = q % outs;
-        const int64_t tok = t0 + tt;
-        if (j < sh.rk) {
-            float v = 0.f;
-            if (j < sh.r) {
-                float z = 0.f;
-                for (int i = 0; i < n; ++i) z += s_p[(tt * 8 + i) * rows_p + j];
-                v = -kLog2e * silu_f(z * inv_n);
-            }
-            const bf16_t h = f32_to_bf16(v);
-            ws.act[(tok * 2) * sh.rk + j] = h;
-            ws.act[(tok * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
-        } else {
-            const int i = j - sh.rk;
-            float sv = 1.0f;
-            if (sh.nw) {
-                float w = 0.f;
-                for (int i2 = 0; i2 < n; ++i2) w += s_p[(tt * 8 + i2) * rows_p + sh.r + i];
-                sv = 2.0f * sigmoid_f(w * inv_n);
-            }
-            s_out[tok * n + i] = sv;
+            s_out[t * NB + i] = sh.nw ? 2.0f * sigmoid_f(proj(sh.r + i) * inv_n) : 1.0f;
         }
     }
 }
@@ -852,11 +833,24 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     const int64_t tiles8 = (sh.tiles + 7) / 8 * 8;
     const unsigned grid = (unsigned)(tiles8 * sh.n * sh.ksplit);
     const bf16_t *y = (const bf16_t *)a.y;
+    if (sh.prep) {
+        const int64_t total = (int64_t)sh.n * 16 * sh.row_blocks * (sh.d / 8);
+        const int64_t blocks = (total + 255) / 256;
+        hipLaunchKernelGGL(k_prep_wprime, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
+                           (const bf16_t *)a.gamma, (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
-        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepth>), dim3(grid), dim3(kThreads), 0, st, \
-                           (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,           \
-                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, a.s_out, w, sh, a.eps); \
+        if (sh.prep)                                                                        \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepth, true>), dim3(grid), dim3(kThreads), 0, st, \
+                               (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
+                               (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
+        else                                                                                \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepthSplit, false>), dim3(grid), dim3(kThreads), 0, st, \
+                               (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
+                               (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;
     switch (sh.row_blocks) {
         GR_K1(1) GR_K1(2) GR_K1(3) GR_K1(4) GR_K1(5) GR_K1(6) GR_K1(7) GR_K1(8)
@@ -938,11 +932,16 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     workspace_layout(sh, (char *)a.ws, &w);
     hipError_t e = a.fused ? launch_k1<true>(a, sh, w, st) : launch_k1<false>(a, sh, w, st);
     if (e != hipSuccess) return e;
-    if (sh.ksplit > 1) {
-        hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((sh.N + kRedTokens - 1) / kRedTokens)),
-                           dim3(256), 0, st, a.s_out, w, sh, a.eps);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 rgrid((unsigned)((sh.N + kRedWaves - 1) / kRedWaves)), rblock(64 * kRedWaves);
+    switch (sh.ksplit) {
+    case 1: hipLaunchKernelGGL((k_reduce_records<4, 1>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 2: hipLaunchKernelGGL((k_reduce_records<4, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 4: hipLaunchKernelGGL((k_reduce_records<4, 4>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 8: hipLaunchKernelGGL((k_reduce_records<4, 8>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 16: hipLaunchKernelGGL((k_reduce_records<4, 16>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    default: return hipErrorInvalidValue;
     }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     const bool resident = a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
     return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }

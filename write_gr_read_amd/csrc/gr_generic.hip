@@ -123,12 +123,7 @@ k_write(T *__restrict__ state, const T *__restrict__ y, const float *__restrict_
         u32x4 rv = *reinterpret_cast<const u32x4 *>(state + q * VEC);
         const u32x4 yv = *reinterpret_cast<const u32x4 *>(y + (t * dv + cv) * VEC);
         if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = write_sum_bf16(si, bf16_lo(yv[e]), bf16_lo(rv[e]), sp2);
-                const float hi = write_sum_bf16(si, bf16_hi(yv[e]), bf16_hi(rv[e]), sp2);
-                rv[e] = pack_bf16x2(lo, hi);
-            }
+            rv = write8_bf16(si, sp2, yv, rv);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
