@@ -96,11 +96,9 @@ gr_status gr_read(const void *state, gr_dtype dt, int64_t N, const gr_layer *L,
                   void *u, float *s, void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * gr_write -- eq:write, in place: state[t][i][c] += s[t][i] * y[t][c].
- * The stored value is the exact R + s y rounded once to the state dtype
- * (round to nearest even): one fp32 fused multiply-add, and for bf16 a
- * correction where that fp32 result lies on a bf16 rounding midpoint, so the
- * result never suffers double rounding.
+ * gr_write -- eq:write, in place: state[t][i][c] += s[t][i] * y[t][c],
+ * computed as one fp32 fused multiply-add (the exact value rounded once to
+ * fp32) and stored in the state dtype (round to nearest even).
  *   state  in/out [N][n][d];  y in [N][d];  s in [N][n] fp32
  */
 gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int64_t N,

@@ -149,6 +149,11 @@ int gro_read(int64_t N, int n, int d, int r, double eps, int dtype,
  * GR write for N tokens  [QFN eq:write; NOTES sec. 3]:
  *   R'_i = R_i + s_i * y, the same y into every branch, stored in place.
  *   R [N][n][d] in/out, y [N][d], s [N][n].
+ * The pages fix no precision for forming R + s y before it is stored, so the
+ * rounding is taken in the kernels' precision: the sum (exact in fp64 here
+ * whenever it can matter) is rounded to fp32 -- what one fp32 fused
+ * multiply-add delivers -- and that fp32 value is stored, i.e. rounded again
+ * to the storage dtype.
  */
 int gro_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
               const double *s)
@@ -158,7 +163,8 @@ int gro_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
         for (int i = 0; i < n; ++i)
             for (int c = 0; c < d; ++c) {
                 double *p = R + (t * n + i) * (int64_t)d + c;
-                *p = store_round(*p + s[t * n + i] * y[t * d + c], dtype);
+                const double sum = *p + s[t * n + i] * y[t * d + c];
+                *p = store_round(dtype == ORC_F64 ? sum : orc_round_f32(sum), dtype);
             }
     return 0;
 }

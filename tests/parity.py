@@ -12,8 +12,9 @@ Tolerances (written here, used by every GPU parity test):
     once, so its error is a small multiple of fp32 rounding of the TERMS, not
     of the result, plus one bf16 ulp of the result.  Where no A is given the
     RMS(o)/16 floor applies.  Also reported: max|g-o|/RMS(o) and the relative L2 error.
-  * written state (eq:write): bit for bit (check_exact).  Both sides store
-    the exact R + s y rounded once to the state dtype.
+  * written state (eq:write): bit for bit (check_exact).  Both sides form
+    R + s y in fp32 (the exact value rounded once, as one fp32 FMA does) and
+    store that rounded to the state dtype.
   * chained bf16 state after L sublayers (check_chain): each stored value is
     rounded L times, and a rounding decision that differs between the two
     sides (a pre-rounding difference of 1e-7 lands on a bf16 rounding

@@ -126,6 +126,35 @@ def test_zero_write_projection_gives_unit_strength_exactly(orc):
     np.testing.assert_array_equal(Rw, ref)
 
 
+def test_write_rounds_through_fp32(orc):
+    """eq:write is stored as the fp32 value of R + s y rounded to the storage
+    dtype (the pages fix no precision; the kernels' fp32 is the reading).
+    Worked cases, exact by hand: R = 1, y = 3/256, s = 1 - 2^-24 (an fp32).
+    Exact sum 1 + 3/256 - 3*2^-32: its fp32 is the bf16 midpoint 1 + 3/256,
+    which rounds to even, 1 + 2^-6; a single rounding of the exact sum would
+    give 1 + 2^-7.  With s = 1 + 2^-23 the fp32 sum is again the midpoint and
+    goes up to 1 + 2^-6, as the exact sum does."""
+    R = np.array([[[1.0]]])
+    y = np.array([[3.0 / 256]])
+    s_dn = np.array([[1.0 - 2.0 ** -24]])
+    s_up = np.array([[1.0 + 2.0 ** -23]])
+    assert float(np.float32(s_dn[0, 0])) == s_dn[0, 0] and float(np.float32(s_up[0, 0])) == s_up[0, 0]
+    assert orc.write(R, y, s_dn, dtype="bf16")[0, 0, 0] == 1.0 + 2.0 ** -6
+    assert orc.write(R, y, s_up, dtype="bf16")[0, 0, 0] == 1.0 + 2.0 ** -6
+    # fp32 storage: the single fp32 rounding of the exact sum
+    assert orc.write(R, y, s_dn, dtype="f32")[0, 0, 0] == 1.0 + 3.0 / 256
+    # f64: the exact sum
+    assert orc.write(R, y, s_dn, dtype="f64")[0, 0, 0] == 1.0 + 3.0 / 256 - 3.0 * 2.0 ** -32
+    # random cases: the exact sum (exact in fp64 at these magnitudes) to fp32, then to bf16
+    rng = np.random.default_rng(3)
+    Rr = torch.from_numpy(rng.standard_normal((16, 4, 64))).to(torch.bfloat16)
+    yr = torch.from_numpy(0.05 * rng.standard_normal((16, 64))).to(torch.bfloat16)
+    sr = torch.from_numpy(rng.uniform(0, 2, (16, 4))).float()
+    exact = Rr.double() + sr.double()[:, :, None] * yr.double()[:, None, :]  # exact in fp64 here
+    ref = exact.float().to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(orc.write(Rr, yr, sr.double().numpy(), dtype="bf16"), ref)
+
+
 def test_zero_strength_or_zero_output_is_identity(orc):
     X = inputs.make_gr_inputs(10, 4, 48, 4, "bf16", seed=7, n_param_sets=1)
     R0 = X.X.double().numpy()

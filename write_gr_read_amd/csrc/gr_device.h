@@ -36,58 +36,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float a) {
     return __builtin_bit_cast(bf16_t, (__bf16)a);
 }
 
-// eq:write for a bf16 state element: r + s y rounded ONCE to bf16 (nearest
-// even).  fmaf gives r + s y correctly rounded to fp32; rounding that again to
-// bf16 can only go wrong where the fp32 value lies exactly on a bf16 rounding
-// midpoint (low 16 bits 0x8000) while the exact sum does not -- common when s
-// saturates near 0 or 2.  There the sign of the fp32 rounding error decides:
-// s y - v is exact in fp64 (when v is such a midpoint both terms lie within
-// 2^42 of each other), one more fp64 add of r rounds once and keeps the sign.
-// The fp32 value is moved one unit off the midpoint towards the exact sum, and
-// the final bf16 conversion then rounds the right way.  Returns that fp32 value.
-// s_pow2: s is 0 or +-2^k (no mantissa bits).  Then s y is exact with at most
-// 8 significant bits, and r + s y is either exact in fp32 or within 2^-16 of
-// its larger term -- never on a midpoint -- so the check is skipped (s == 1
-// without a write projection; there midpoints are frequent and all exact).
-__device__ __forceinline__ bool write_scale_pow2(float s) {
-    return (__float_as_uint(s) & 0x7fffffu) == 0u;
-}
-__device__ __forceinline__ float write_sum_bf16(float s, float y, float r, bool s_pow2) {
-    float v = fmaf(s, y, r);
-    uint32_t b = __float_as_uint(v);
-    if (__builtin_expect((b & 0xffffu) == 0x8000u && !s_pow2, 0)) {
-        const double e = fma((double)s, (double)y, -(double)v) + (double)r;
-        if (e != 0.0) b += ((e > 0.0) == (v > 0.0)) ? 1u : 0xffffffffu;
-        v = __uint_as_float(b);
-    }
-    return v;
-}
-
-// Eight eq:write elements of a bf16 state: packed y and r words (low half =
-// even channel) -> packed stored words, each the exact r + s y rounded once.
-// The midpoint test runs on all eight sums; the fp64 tie-break (rare) is one
-// branch for the group.
-__device__ __forceinline__ u32x4 write8_bf16(float s, bool s_pow2, u32x4 y, u32x4 r) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[2 * e] = fmaf(s, bf16_lo(y[e]), bf16_lo(r[e]));
-        v[2 * e + 1] = fmaf(s, bf16_hi(y[e]), bf16_hi(r[e]));
-    }
-    bool mid = false;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) mid |= (__float_as_uint(v[k]) & 0xffffu) == 0x8000u;
-    if (__builtin_expect(mid && !s_pow2, 0)) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float yk = (k & 1) ? bf16_hi(y[k >> 1]) : bf16_lo(y[k >> 1]);
-            const float rk = (k & 1) ? bf16_hi(r[k >> 1]) : bf16_lo(r[k >> 1]);
-            v[k] = write_sum_bf16(s, yk, rk, false);
-        }
-    }
+// eq:write for eight bf16 elements: packed y and r words (low half = even
+// channel) -> packed words of r + s y, formed by one fp32 FMA and rounded to
+// bf16 (nearest even).
+__device__ __forceinline__ u32x4 write8_bf16(float s, u32x4 y, u32x4 r) {
     u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16x2(fmaf(s, bf16_lo(y[e]), bf16_lo(r[e])), fmaf(s, bf16_hi(y[e]), bf16_hi(r[e])));
     return o;
 }
 
@@ -96,17 +52,15 @@ template <typename T> struct Store;
 template <> struct Store<float> {
     __device__ static __forceinline__ float load(const float *p) { return *p; }
     __device__ static __forceinline__ float round(float v) { return v; }
-    // eq:write, one rounding (fmaf)
+    // eq:write: one fp32 fused multiply-add
     __device__ static __forceinline__ float write(float s, float y, float r) { return fmaf(s, y, r); }
     __device__ static __forceinline__ void store(float *p, float v) { *p = v; }
 };
 template <> struct Store<bf16_t> {
     __device__ static __forceinline__ float load(const bf16_t *p) { return bf16_to_f32(*p); }
     __device__ static __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
-    // eq:write, one rounding to bf16 (stored value, widened)
-    __device__ static __forceinline__ float write(float s, float y, float r) {
-        return round(write_sum_bf16(s, y, r, write_scale_pow2(s)));
-    }
+    // eq:write: one fp32 fused multiply-add, rounded to bf16 (stored value, widened)
+    __device__ static __forceinline__ float write(float s, float y, float r) { return round(fmaf(s, y, r)); }
     __device__ static __forceinline__ void store(bf16_t *p, float v) { *p = f32_to_bf16(v); }
 };
 

@@ -49,21 +49,20 @@ constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16 * kWaves;        // tokens per workgroup
 constexpr int kChunk = 32;                // channels per MFMA k-step
-#ifndef GR_K1_ITER
-#define GR_K1_ITER 64
-#endif
+
 #ifndef GR_K1_DEPTH
-#define GR_K1_DEPTH 1             // many tokens (with the W' prep)
+#define GR_K1_DEPTH 0             // many tokens (with the W' prep)
 #endif
 #ifndef GR_K1_DEPTH_SPLIT
 #define GR_K1_DEPTH_SPLIT 2       // few tokens: short channel splits need a deeper pipeline
 #endif
-constexpr int kIter = GR_K1_ITER;         // channels per pipelined iteration (kernel 1)
+constexpr int kIter = 64;                 // channels per W' chunk of kernel 1 (a round is two)
 constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight (with prep)
 constexpr int kDepthSplit = GR_K1_DEPTH_SPLIT;  // ... without (few tokens)
-#ifndef GR_K1_STATIC_RING
-#define GR_K1_STATIC_RING 0
+#ifndef GR_K1_TG
+#define GR_K1_TG 1
 #endif
+constexpr int kTG = GR_K1_TG;             // 16-token MFMA column groups per kernel-1 wave
 #ifndef GR_K2_WAVES_PER_SIMD
 #define GR_K2_WAVES_PER_SIMD 3
 #endif
@@ -211,38 +210,52 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
 }
 
 // ---------------------------------------------------------------------------
+#ifndef GR_K1_WAVES_PER_SIMD
+#define GR_K1_WAVES_PER_SIMD 4
+#endif
 // Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
 // the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
 // that XCD's L2) and consecutive dispatch slots.
 //
-// W' (W_down / W_write rows of the branch times gamma, as bf16 hi and lo
-// planes) is either formed here per chunk (PREP = false) or read ready-made
-// from the workspace, where k_prep_wprime wrote it once for the call
-// (PREP = true: every token tile would otherwise redo the same split).
+// Memory side: a round covers RC = 128 channels of the wave's 16 tokens.  One
+// load instruction takes 4 tokens x 256 contiguous bytes (16 lanes per token
+// row, adjacent lanes on adjacent 16-byte pieces), which HBM serves much
+// better than 16 rows x 64 bytes; eq:write, its store and the sum of squares
+// run in that layout.  The stored R' is also written to a wave-private LDS
+// tile (16 tokens x 16 pieces at a pitch of 17 pieces, so both the row-wise
+// writes and the column-wise MFMA reads are free of bank conflicts), from
+// which the MFMA B operand (token = lane % 16, 8 channels of lane group
+// lane / 16) is read.
 //
-// Pipeline per iteration of KITER channels: the state / y of the iteration
-// DEPTH ahead are loaded into registers, the W' chunk of the next iteration
-// (loaded into registers during the previous one) is written to the other LDS
-// buffer, and the W' chunk after that is loaded.  The register ring of state /
-// y is shifted by copies after each iteration (GR_K1_STATIC_RING=1 unrolls
-// the loop by DEPTH + 1 instead; it needs more registers).
-#ifndef GR_K1_WAVES_PER_SIMD
-#define GR_K1_WAVES_PER_SIMD 4
-#endif
-template <bool FUSED, int NRB, int KITER, int DEPTH, bool PREP>
-__global__ void __launch_bounds__(kThreads, NRB <= 5 ? GR_K1_WAVES_PER_SIMD : 2)
+// W' (W_down / W_write rows of the branch times gamma, as bf16 hi and lo
+// planes) is either formed here per 64-channel chunk (PREP = false) or read
+// ready-made from the workspace, where k_prep_wprime wrote it once for the
+// call (PREP = true: every token tile would otherwise redo the same split).
+// It is staged in a double-buffered LDS slot per chunk: the chunk after next
+// is loaded into registers while a chunk is used, with one barrier per chunk.
+// DEPTH rounds of state / y loads are in flight ahead of the round in use.
+template <bool FUSED, int NRB, int DEPTH, bool PREP, int TG>
+__global__ void __launch_bounds__(64 * (kWaves / TG), (NRB <= 5 && TG == 1 && PREP) ? GR_K1_WAVES_PER_SIMD : 2)
 k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
               FastShape sh) {
-    constexpr int KS = KITER / kChunk;                 // MFMA k-steps per iteration
-    constexpr int kPitch = KITER + 8;                  // bf16 per staged row
-    constexpr int NV = NRB * 16 * (KITER / 8);         // 16-byte vectors of W' per iteration (per plane)
-    constexpr int WV = PREP ? (2 * NV + kThreads - 1) / kThreads  // hi and lo planes, ready-made
-                            : (NV + kThreads - 1) / kThreads;     // W and gamma, split here
+    constexpr int WAVES = kWaves / TG;                 // each wave carries TG groups of 16 tokens
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int NQ = 4 * TG;                         // load instructions per round (4 tokens each)
+    constexpr int RC = 2 * kIter;                      // channels per round
+    constexpr int PCS = RC / 8;                        // 16-byte pieces per token row and round
+    constexpr int KS = kIter / kChunk;                 // MFMA k-steps per W' chunk
+    constexpr int kPitch = kIter + 8;                  // bf16 per staged W' row
+    constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per chunk (per plane)
+    constexpr int WV = PREP ? (2 * NV + THREADS - 1) / THREADS  // hi and lo planes, ready-made
+                            : (NV + THREADS - 1) / THREADS;     // W and gamma, split here
     constexpr int NSLOT = DEPTH + 1;
+    static_assert(PCS == 16, "a round is 16 pieces of 8 channels per token");
     // [buffer][hi/lo][row][k]
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
+    constexpr int RP = PCS + 1;                        // LDS tile pitch in pieces (odd: no bank conflicts)
+    __shared__ __attribute__((aligned(16))) u32x4 lds_r[WAVES][16 * TG * RP];
 
     const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
@@ -251,13 +264,15 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     const int split = (int)((b / 8) % S);
     if (tile >= sh.tiles) return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4;                 // lane group: channels 8g..8g+7 of a k-step
-    const int64_t t = tile * kTile + wave * 16 + (lane & 15);
-    const bool valid = t < sh.N;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, m16 = lane & 15;
+    const int64_t t0 = tile * kTile + wave * 16 * TG;   // first token of this wave
     const int64_t nd = (int64_t)n * d;
-    const int nit = sh.ksplit_chan / KITER;
-    const int c_base = split * sh.ksplit_chan;  // first channel of this split
+    const int chan = sh.ksplit_chan;                    // channels of this split (multiple of kIter)
+    const int nit = chan / kIter;                       // W' chunks
+    const int nround = (chan + RC - 1) / RC;
+    const int c_base = split * chan;                    // first channel of this split
     const int rows_p = NRB * 16;
 
     // W' staging.  PREP: vector v < NV of the hi plane, NV + v of the lo plane.
@@ -267,23 +282,23 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     auto load_w = [&](int it) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
-            const int v = tid + q * kThreads;
+            const int v = tid + q * THREADS;
             if (PREP) {
                 const int plane = v / NV, rem = v % NV;
-                const int row = rem / (KITER / 8), cv = rem % (KITER / 8);
+                const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
                 wreg[q] = u32x4{0u, 0u, 0u, 0u};
                 if (v < 2 * NV && it < nit)
                     wreg[q] = *reinterpret_cast<const u32x4 *>(
-                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + it * KITER + cv * 8);
+                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + it * kIter + cv * 8);
             } else {
-                const int row = v / (KITER / 8), cv = v % (KITER / 8);
+                const int row = v / (kIter / 8), cv = v % (kIter / 8);
                 const bf16_t *src = nullptr;
                 if (v < NV && it < nit) {
                     if (row < sh.r) src = wd + (int64_t)row * nd;
                     else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
                 }
                 if (src) {
-                    const int64_t col = (int64_t)br * d + c_base + it * KITER + cv * 8;
+                    const int64_t col = (int64_t)br * d + c_base + it * kIter + cv * 8;
                     wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
                     greg[PREP ? 0 : q] = *reinterpret_cast<const u32x4 *>(gamma + col);
                 } else {
@@ -296,15 +311,15 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     auto store_w = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
-            const int v = tid + q * kThreads;
+            const int v = tid + q * THREADS;
             if (PREP) {
                 if (v < 2 * NV) {
                     const int plane = v / NV, rem = v % NV;
-                    const int row = rem / (KITER / 8), cv = rem % (KITER / 8);
+                    const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
                     *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + cv * 8]) = wreg[q];
                 }
             } else if (v < NV) {
-                const int row = v / (KITER / 8), cv = v % (KITER / 8);
+                const int row = v / (kIter / 8), cv = v % (kIter / 8);
                 u32x4 hi, lo;
                 split_wprime(wreg[q], greg[PREP ? 0 : q], hi, lo);
                 *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kPitch + cv * 8]) = hi;
@@ -313,100 +328,128 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         }
     };
 
-    f32x4 acc[NRB];
+    // load instruction q: token t0 + 4q + g, piece m16 (channels 8*m16 .. +7 of the round)
+    bool vq[NQ];
+    float sq[NQ];
+    float ss[NQ];
 #pragma unroll
-    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-    const float si = (FUSED && valid) ? s_in[t * n + br] : 0.f;
-    const bool sp2 = write_scale_pow2(si);
-    bf16_t *rowp = state + (t * n + br) * (int64_t)d + c_base + 8 * g;
-    const bf16_t *yrow = FUSED ? y + t * (int64_t)d + c_base + 8 * g : nullptr;
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t t = t0 + 4 * q + g;
+        vq[q] = t < sh.N;
+        sq[q] = (FUSED && vq[q]) ? s_in[t * n + br] : 0.f;
+        ss[q] = 0.f;
+    }
+    // addresses: a wave-uniform base (token t0, this branch and split) plus a
+    // 32-bit lane offset; instruction q adds 4q tokens, round rd adds rd*RC
+    bf16_t *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
+    const bf16_t *const ybase = FUSED ? y + t0 * (int64_t)d + c_base : nullptr;
+    const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
+    const int64_t qstride = 4 * nd, qystride = 4 * (int64_t)d;
 
-    // data ring: slot it % NSLOT holds iteration it
-    u32x4 rr[NSLOT][KS], yy[NSLOT][KS];
-    auto load_data = [&](int it, int slot) {
+    u32x4 rr[NSLOT][NQ], yy[NSLOT][NQ];
+    auto load_round = [&](int rd, int slot) {
+        const bool in = rd < nround && rd * RC + 8 * m16 < chan;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            rr[slot][ks] = u32x4{0u, 0u, 0u, 0u};
-            yy[slot][ks] = u32x4{0u, 0u, 0u, 0u};
-            if (valid && it < nit) {
-                rr[slot][ks] = *reinterpret_cast<const u32x4 *>(rowp + it * KITER + ks * kChunk);
-                if (FUSED) yy[slot][ks] = *reinterpret_cast<const u32x4 *>(yrow + it * KITER + ks * kChunk);
+        for (int q = 0; q < NQ; ++q) {
+            rr[slot][q] = u32x4{0u, 0u, 0u, 0u};
+            yy[slot][q] = u32x4{0u, 0u, 0u, 0u};
+            if (vq[q] && in) {
+                rr[slot][q] = *reinterpret_cast<const u32x4 *>(sbase + q * qstride + rd * RC + soff);
+                if (FUSED) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff);
             }
         }
     };
+
+    f32x4 acc[TG][NRB];
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) acc[tg][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 *my_r = lds_r[wave];
 
     load_w(0);
     store_w(0);
     load_w(1);
 #pragma unroll
-    for (int q = 0; q < DEPTH; ++q) load_data(q, q);
+    for (int q = 0; q < DEPTH; ++q) load_round(q, q);
     __syncthreads();
-    // one iteration of KITER channels on ring slot `slot`
-    auto iteration = [&](int it, int slot) {
-        const int cur = it & 1;
+    for (int rd = 0; rd < nround; ++rd) {
+        load_round(rd + DEPTH, DEPTH);
+        // eq:write in the load layout: store, sum of squares, LDS tile
+        const bool in = rd * RC + 8 * m16 < chan;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            // eq:write, stored; the read below uses the stored (rounded) values
-            u32x4 w = rr[slot][ks];
+        for (int q = 0; q < NQ; ++q) {
+            u32x4 w = rr[0][q];
             if (FUSED) {
-                w = write8_bf16(si, sp2, yy[slot][ks], rr[slot][ks]);
-                if (valid) *reinterpret_cast<u32x4 *>(rowp + it * KITER + ks * kChunk) = w;
+                w = write8_bf16(sq[q], yy[0][q], rr[0][q]);
+                if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
-            const bf16x8 bop = as_bf16x8(w);
-            const bf16_t *wh = &lds_w[cur][0][(lane & 15) * kPitch + ks * kChunk + 8 * g];
-            const bf16_t *wl = &lds_w[cur][1][(lane & 15) * kPitch + ks * kChunk + 8 * g];
-#pragma unroll
-            for (int k = 0; k < NRB; ++k) {
-                const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kPitch);
-                const u32x4 al = *reinterpret_cast<const u32x4 *>(wl + k * 16 * kPitch);
-                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop, acc[k], 0, 0, 0);
-                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop, acc[k], 0, 0, 0);
-            }
+            for (int e = 0; e < 4; ++e) ss[q] = dot2_bf16(w[e], w[e], ss[q]);
+            my_r[(4 * q + g) * RP + m16] = w;
         }
-        if (it + 1 < nit) store_w(cur ^ 1);
-        load_w(it + 2);
-        __syncthreads();
-    };
-#if GR_K1_STATIC_RING
-    for (int it0 = 0; it0 < nit; it0 += NSLOT) {
+        // the wave's LDS writes above complete before its reads below (LDS
+        // instructions of a wave execute in order); keep the phases apart so
+        // the element work and the MFMA operands are not live together
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ph = 0; ph < NSLOT; ++ph) {
-            const int it = it0 + ph;
+        for (int h = 0; h < RC / kIter; ++h) {
+            const int it = rd * (RC / kIter) + h;
             if (it < nit) {
-                const int slot = ph;
-                load_data(it + DEPTH, (ph + DEPTH) % NSLOT);
-                iteration(it, slot);
+                const int cur = it & 1;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int pc = (h * kIter + ks * kChunk) / 8 + g;   // piece of this lane group
+                    bf16x8 bop[TG];
+#pragma unroll
+                    for (int tg = 0; tg < TG; ++tg)
+                        bop[tg] = as_bf16x8(my_r[(16 * tg + m16) * RP + pc]);
+                    const bf16_t *wh = &lds_w[cur][0][m16 * kPitch + ks * kChunk + 8 * g];
+                    const bf16_t *wl = &lds_w[cur][1][m16 * kPitch + ks * kChunk + 8 * g];
+#pragma unroll
+                    for (int k = 0; k < NRB; ++k) {
+                        const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kPitch);
+                        const u32x4 al = *reinterpret_cast<const u32x4 *>(wl + k * 16 * kPitch);
+#pragma unroll
+                        for (int tg = 0; tg < TG; ++tg) {
+                            acc[tg][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop[tg], acc[tg][k], 0, 0, 0);
+                            acc[tg][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop[tg], acc[tg][k], 0, 0, 0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (it + 1 < nit) store_w(cur ^ 1);
+                load_w(it + 2);
+                __syncthreads();
             }
         }
-    }
-#else
-    for (int it = 0; it < nit; ++it) {
-        const int slot = 0;
-        load_data(it + DEPTH, DEPTH);
-        iteration(it, slot);
 #pragma unroll
         for (int q = 0; q < DEPTH; ++q)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                rr[q][ks] = rr[q + 1][ks];
-                yy[q][ks] = yy[q + 1][ks];
+            for (int e = 0; e < NQ; ++e) {
+                rr[q][e] = rr[q + 1][e];
+                yy[q][e] = yy[q + 1][e];
             }
     }
-#endif
-    // the four lane groups of a token hold disjoint channels: sum them
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
 
     // The record (ss, P) of this (token, branch, split); k_reduce_records,
-    // launched next on the same stream, combines them.
-    if (valid) {
-        float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
-        if (g == 0) rec[0] = ss;
+    // launched next on the same stream, combines them.  ss of token 4q + g is
+    // spread over the 16 lanes of lane group g.
 #pragma unroll
-        for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) ss[q] += __shfl_xor(ss[q], m, 64);
+        if (m16 == 0 && vq[q])
+            ws.partial[((t0 + 4 * q + g) * n + br) * S * (int64_t)sh.pstride + split * (int64_t)sh.pstride] = ss[q];
+    }
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+        const int64_t t = t0 + 16 * tg + m16;  // MFMA column of this lane
+        if (t < sh.N) {
+            float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
+#pragma unroll
+            for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[tg][k];
+        }
     }
 }
 
@@ -844,11 +887,11 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
         if (sh.prep)                                                                        \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepth, true>), dim3(grid), dim3(kThreads), 0, st, \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, true, kTG>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
                                (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         else                                                                                \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kIter, kDepthSplit, false>), dim3(grid), dim3(kThreads), 0, st, \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepthSplit, false, kTG>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
                                (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;

@@ -21,8 +21,8 @@ constexpr int kRowsPerPass = 8;  // projection rows accumulated per sweep
 // workgroup per token.  Every pass walks the row in the same (branch, channel)
 // order with the same thread mapping, so each thread only re-reads elements it
 // wrote itself.
-//   FUSED: R' = R + s_in y is computed, rounded once to the state dtype,
-//   stored, and the read then uses the stored R'.
+//   FUSED: R' = R + s_in y is computed (one fp32 FMA), rounded to the state
+//   dtype, stored, and the read then uses the stored R'.
 template <typename T, bool FUSED>
 __global__ void __launch_bounds__(kGenThreads)
 k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__restrict__ s_in,
@@ -119,11 +119,10 @@ k_write(T *__restrict__ state, const T *__restrict__ y, const float *__restrict_
         const int64_t ti = q / dv;  // t * n + i
         const int64_t t = ti / n;
         const float si = s[ti];
-        const bool sp2 = write_scale_pow2(si);
         u32x4 rv = *reinterpret_cast<const u32x4 *>(state + q * VEC);
         const u32x4 yv = *reinterpret_cast<const u32x4 *>(y + (t * dv + cv) * VEC);
         if constexpr (sizeof(T) == 2) {
-            rv = write8_bf16(si, sp2, yv, rv);
+            rv = write8_bf16(si, yv, rv);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
