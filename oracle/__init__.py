@@ -6,8 +6,10 @@ never does.  The arithmetic lives in ``gr_oracle.c`` (plain loops, fp64,
 built with ``-O2 -ffp-contract=off``); this file only marshals numpy arrays.
 
 Functions take and return float64 numpy arrays holding the exact stored values
-(a bfloat16 or float32 input widened to float64 is exact).  Storage dtypes:
-"f32", "bf16", or "f64" (no rounding at store points, for closed-form checks).
+(a bfloat16, float32 or e4m3 input widened to float64 is exact).  Storage
+dtypes: "f32", "bf16", "f64" (no rounding at store points, for closed-form
+checks), or "fp8" (the branch state in OCP e4m3, saturating at +-448; u, y,
+gains and weights in bf16).
 
 Every function follows a passage of the pages:
   read / write / fused  -- "Paper reading: Qwen3.8 Flash Next", part 2
@@ -31,7 +33,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gr_oracle.c")
 _LIB = os.path.join(_HERE, "libgr_oracle.so")
-_DT = {"f32": 0, "bf16": 1, "f64": 2}
+_DT = {"f32": 0, "bf16": 1, "f64": 2, "fp8": 3}
 
 _lib = None
 
@@ -61,6 +63,8 @@ def _load():
         lib.gro_tanh_standin.argtypes = [I64, I, P, P]
         lib.orc_round_bf16.argtypes = [D]
         lib.orc_round_bf16.restype = D
+        lib.orc_round_e4m3.argtypes = [D]
+        lib.orc_round_e4m3.restype = D
         for f in (lib.gro_read, lib.gro_write, lib.gro_fused, lib.gro_add_rmsnorm,
                   lib.gro_tanh_standin):
             f.restype = ctypes.c_int
@@ -91,6 +95,11 @@ def _check(rc: int, name: str):
 
 def round_bf16(x: float) -> float:
     return _load().orc_round_bf16(float(x))
+
+
+def round_e4m3(x: float) -> float:
+    """Nearest OCP e4m3 value, ties to even, saturating at +-448."""
+    return _load().orc_round_e4m3(float(x))
 
 
 def read(R, gamma, w_down, w_up, w_write, eps: float = 1e-6, dtype: str = "bf16",

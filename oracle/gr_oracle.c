@@ -27,6 +27,12 @@
  *     where the path stores them: the state, u, and (for the chain) F's y;
  *     s is rounded to fp32.  Storage dtype 2 ("f64") skips that rounding, for
  *     exact closed-form checks.
+ *   - Storage dtype 3 ("fp8"): the branch state is OCP e4m3 (e4m3fn: 3
+ *     mantissa bits, no infinities, largest finite 448), everything else --
+ *     u, y, gains, weights -- is bf16.  [QFN sec. 7] names an FP8 state
+ *     without a format or a scale: unscaled e4m3 is the reading, and a value
+ *     beyond +-448 saturates to +-448 (e4m3fn has no infinity; a NaN would
+ *     poison the residual stream).
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -35,7 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_FP8 = 3 };
 
 /* Largest finite bfloat16: (2 - 2^-7) * 2^127. */
 #define ORC_BF16_MAX 3.3895313892515355e38
@@ -57,9 +63,35 @@ double orc_round_bf16(double x)
 /* Round x to the nearest fp32 (C conversion under the default rounding mode). */
 double orc_round_f32(double x) { return (double)(float)x; }
 
-static double store_round(double x, int dtype)
+/* Round x to the nearest OCP e4m3 value (4 significant bits, exponent bias 7,
+ * subnormal step 2^-9 below 2^-6), ties to even; magnitudes beyond the largest
+ * finite value 448 saturate to +-448. */
+double orc_round_e4m3(double x)
+{
+    if (x == 0.0 || isnan(x)) return x;
+    if (fabs(x) >= 448.0) return copysign(448.0, x);
+    int e;
+    frexp(x, &e);                  /* |x| in [2^(e-1), 2^e) */
+    int q = e - 4;                 /* spacing of 4-bit significands there */
+    if (q < -9) q = -9;
+    double y = ldexp(nearbyint(ldexp(x, -q)), q);   /* nearbyint: ties-to-even */
+    if (fabs(y) > 448.0) return copysign(448.0, x);
+    return y;
+}
+
+/* Stores of the branch state. */
+static double store_state(double x, int dtype)
 {
     if (dtype == ORC_BF16) return orc_round_bf16(x);
+    if (dtype == ORC_F32) return orc_round_f32(x);
+    if (dtype == ORC_FP8) return orc_round_e4m3(x);
+    return x;
+}
+
+/* Stores of everything else (u, the chain's y, add+RMSNorm's outputs). */
+static double store_round(double x, int dtype)
+{
+    if (dtype == ORC_BF16 || dtype == ORC_FP8) return orc_round_bf16(x);
     if (dtype == ORC_F32) return orc_round_f32(x);
     return x;
 }
@@ -164,7 +196,7 @@ int gro_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
             for (int c = 0; c < d; ++c) {
                 double *p = R + (t * n + i) * (int64_t)d + c;
                 const double sum = *p + s[t * n + i] * y[t * d + c];
-                *p = store_round(dtype == ORC_F64 ? sum : orc_round_f32(sum), dtype);
+                *p = store_state(dtype == ORC_F64 ? sum : orc_round_f32(sum), dtype);
             }
     return 0;
 }
@@ -192,7 +224,7 @@ int gro_fused(int64_t N, int n, int d, int r, double eps, int dtype, double *R,
 int gro_add_rmsnorm(int64_t N, int d, double eps, int dtype, double *x,
                     const double *y, const double *w, double *out)
 {
-    if (N < 0 || d < 1) return -1;
+    if (N < 0 || d < 1 || dtype == ORC_FP8) return -1;
     for (int64_t t = 0; t < N; ++t) {
         double *h = x + t * d;
         double ss = 0.0;

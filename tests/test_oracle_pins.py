@@ -155,6 +155,56 @@ def test_write_rounds_through_fp32(orc):
     np.testing.assert_array_equal(orc.write(Rr, yr, sr.double().numpy(), dtype="bf16"), ref)
 
 
+def test_round_e4m3_matches_torch_and_saturates(orc):
+    """OCP e4m3 rounding (fp8 branch state) equals torch's float8_e4m3fn cast
+    -- round to nearest, ties to even, subnormal step 2^-9 -- wherever that
+    cast is finite; beyond the largest finite value 448 the state saturates
+    (reading: e4m3fn has no infinity)."""
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([rng.standard_normal(20000) * 4, rng.standard_normal(20000) * 0.01,
+                           rng.standard_normal(2000) * 200,
+                           # ties: midpoints between neighbours at several scales, subnormals
+                           [1.0625, 1.1875, 3 * 2.0 ** -10, 2.0 ** -10, 5 * 2.0 ** -10, 0.0, -1.0625,
+                            440.0, 447.0, 456.0, 463.0]])
+    vals = vals.astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(vals).float().to(torch.float8_e4m3fn).double().numpy()
+    got = np.array([orc.round_e4m3(v) for v in vals])
+    finite = np.isfinite(ref)
+    np.testing.assert_array_equal(got[finite], ref[finite])
+    big = ~finite
+    assert big.sum() > 0
+    np.testing.assert_array_equal(got[big], np.copysign(448.0, vals[big]))
+    for v, want in ((464.0, 448.0), (1e6, 448.0), (-1e6, -448.0), (448.0, 448.0)):
+        assert orc.round_e4m3(v) == want
+
+
+def test_fp8_state_write_and_read(orc):
+    """fp8 storage: the write stores e4m3(fp32(R + s y)); the read's u is bf16.
+    Worked write cases (R = 1, y = 1/16): s = 1 gives 1.0625, an e4m3
+    midpoint, stored as 1 (ties to even); s = 1 + 2^-23 gives an exact sum
+    just above the midpoint whose fp32 value IS the midpoint, so it is also
+    stored as 1 (one rounding of the exact sum would give 1.125)."""
+    R = np.array([[[1.0]]])
+    y = np.array([[1.0 / 16]])
+    assert orc.write(R, y, np.array([[1.0]]), dtype="fp8")[0, 0, 0] == 1.0
+    assert orc.write(R, y, np.array([[1.0 + 2.0 ** -23]]), dtype="fp8")[0, 0, 0] == 1.0
+    assert orc.write(R, y, np.array([[1.0 + 2.0 ** -19]]), dtype="fp8")[0, 0, 0] == 1.125  # fp32 sum one ulp above
+    # random state: every stored value is an e4m3 number (fixed point of the rounding)
+    X = inputs.make_gr_inputs(6, 4, 64, 8, "bf16", seed=31, n_param_sets=1)
+    R8 = X.X.float().to(torch.float8_e4m3fn).double().numpy()
+    s = np.random.default_rng(2).uniform(0, 2, (6, 4)).astype(np.float32).astype(np.float64)
+    Rw = orc.write(R8, X.y, s, dtype="fp8")
+    np.testing.assert_array_equal(Rw, torch.from_numpy(Rw).float().to(torch.float8_e4m3fn).double().numpy())
+    exact = (R8 + s[:, :, None] * X.y.double().numpy()[:, None, :]).astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(Rw, np.array([orc.round_e4m3(v) for v in exact.ravel()]).reshape(exact.shape))
+    # the read of an fp8 state stores u in bf16: the exact read rounded once
+    p = X.params[0]
+    u8, s8 = orc.read(R8, p.gamma, p.w_down, p.w_up, p.w_write, dtype="fp8")
+    u64, s64 = orc.read(R8, p.gamma, p.w_down, p.w_up, p.w_write, dtype="f64")
+    np.testing.assert_array_equal(u8, np.array([orc.round_bf16(v) for v in u64.ravel()]).reshape(u64.shape))
+    np.testing.assert_array_equal(s8, s64.astype(np.float32).astype(np.float64))
+
+
 def test_zero_strength_or_zero_output_is_identity(orc):
     X = inputs.make_gr_inputs(10, 4, 48, 4, "bf16", seed=7, n_param_sets=1)
     R0 = X.X.double().numpy()
