@@ -25,10 +25,11 @@
  *   Layout     Contiguous, row-major: state [N][n][d] (token, branch,
  *              channel); y, u [N][d]; s [N][n] (always fp32); gamma [n][d];
  *              W_down [r][n*d]; W_up [n*d][r]; W_write [n][n*d].  The vec()
- *              index of (branch i, channel c) is i*d + c.  Weights and gamma
- *              have the state dtype.
- *   Alignment  Every pointer 16-byte aligned; d a multiple of 8 (bf16) or 4
- *              (fp32).
+ *              index of (branch i, channel c) is i*d + c.  Weights, gamma, y
+ *              and u have the state dtype, except with GR_FP8_E4M3, where
+ *              only the state is fp8 and they are bf16.
+ *   Alignment  Every pointer 16-byte aligned; d a multiple of 8 (bf16), 4
+ *              (fp32) or 16 (fp8 state).
  *   Sizes      1 <= n <= 8, d >= 1, 0 <= r <= 512, N >= 0.  r == 0 means a
  *              unit gate (G == 1).  W_write == NULL means s == 1 (the value
  *              of 2 sigmoid(0)).  eps is added inside the square root.
@@ -56,8 +57,12 @@ extern "C" {
 #endif
 
 typedef enum gr_dtype {
-    GR_F32 = 0,   /* fp32 state and weights, fp32 arithmetic */
-    GR_BF16 = 1   /* bf16 state and weights, fp32 accumulation */
+    GR_F32 = 0,       /* fp32 state and weights, fp32 arithmetic */
+    GR_BF16 = 1,      /* bf16 state and weights, fp32 accumulation */
+    GR_FP8_E4M3 = 2   /* fp8 branch state (OCP e4m3, values saturate at +-448;
+                         "Paper reading: Qwen3.8 Flash Next", part 2 Residual,
+                         sec. 7 names an FP8 state), bf16 y, u, gains and
+                         weights, fp32 accumulation.  Read, write and fused only. */
 } gr_dtype;
 
 typedef enum gr_status {
@@ -98,7 +103,8 @@ gr_status gr_read(const void *state, gr_dtype dt, int64_t N, const gr_layer *L,
 /*
  * gr_write -- eq:write, in place: state[t][i][c] += s[t][i] * y[t][c],
  * computed as one fp32 fused multiply-add (the exact value rounded once to
- * fp32) and stored in the state dtype (round to nearest even).
+ * fp32) and stored in the state dtype (round to nearest even; an fp8 state
+ * saturates at +-448).
  *   state  in/out [N][n][d];  y in [N][d];  s in [N][n] fp32
  */
 gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int64_t N,
@@ -120,6 +126,7 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
  * residual_add_rmsnorm -- n = 1 fused residual add + RMSNorm ("Residual",
  * LLM inference, sec. 3.3): h = x + y stored in place of x, then
  * out = w (.) h / sqrt(mean(h^2) + eps), the mean taken over the stored h.
+ * dtype GR_F32 or GR_BF16 (GR_FP8_E4M3 returns GR_ERROR_NOT_SUPPORTED).
  *   x in/out [N][d];  y in [N][d];  w in [d];  out out [N][d] (may equal y)
  */
 gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
@@ -140,7 +147,7 @@ const char *gr_last_error(void);
 /* ---- measurement support (not part of the GR method) ------------------ */
 
 /* The chained workload's elementwise sublayer stand-in: y = 0.1 tanh(u),
- * computed in fp32 and stored in the state dtype.  u, y [count]. */
+ * computed in fp32 and stored in dtype (GR_F32 or GR_BF16).  u, y [count]. */
 gr_status gr_bench_tanh_standin(const void *u, void *y, gr_dtype dt, int64_t count,
                                 void *stream);
 

@@ -98,6 +98,18 @@ def test_fp32_width_rule(L):
     assert call_read(L, dt=0, lay=layer(d=6)) == NOT_SUPPORTED
 
 
+def test_fp8_state_rules(L):
+    """fp8 (e4m3) is a state dtype: d must be a multiple of 16; the n = 1
+    add+RMSNorm and the tanh stand-in (one dtype for all tensors) refuse it."""
+    assert call_read(L, dt=2, lay=layer(d=24)) == NOT_SUPPORTED
+    assert L.gr_write(FAKE, FAKE, FAKE, 2, 4, 4, 40, None) == NOT_SUPPORTED
+    assert L.residual_add_rmsnorm(FAKE, FAKE, FAKE, 1e-6, FAKE + 16, 2, 4, 64, None) == NOT_SUPPORTED
+    assert L.gr_bench_tanh_standin(FAKE, FAKE, 2, 16, None) == NOT_SUPPORTED
+    assert L.gr_last_error() != b""
+    nbytes = ctypes.c_size_t(1)
+    assert L.gr_workspace_size(1, 2, 256, ctypes.byref(layer(d=64)), ctypes.byref(nbytes)) == 0
+
+
 def test_write_and_addnorm_reject_bad_arguments(L):
     assert L.gr_write(FAKE, FAKE, FAKE, 1, 4, 0, 64, None) == INVALID
     assert L.gr_write(FAKE, FAKE, FAKE, 1, 4, 4, 60, None) == NOT_SUPPORTED

@@ -89,6 +89,30 @@ def test_shapes(N, n, d, r, dtype):
     run_read_write_fused(X, f"N{N}-n{n}-d{d}-r{r}-{dtype}")
 
 
+@pytest.mark.parametrize("N,n,d,r", [
+    (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (17, 3, 64, 5), (70, 4, 512, 32),
+    (130, 4, 1024, 48), (300, 4, 192, 32), (129, 4, 384, 96), (257, 4, 320, 128), (64, 4, 256, 0),
+])
+def test_fp8_state_shapes(N, n, d, r):
+    """fp8 (e4m3) branch state, bf16 everything else: read, write and fused
+    against the oracle on the same stored e4m3 values (state bit for bit,
+    u at the bf16 tolerance)."""
+    X = inputs.make_gr_inputs(N, n, d, r, "fp8", seed=3 * N + 5 * n + d + r, w_std=0.05,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0)[:n] if n == 4 else None)
+    run_read_write_fused(X, f"fp8-N{N}-n{n}-d{d}-r{r}")
+
+
+def test_fp8_state_saturates():
+    """Writes that overflow e4m3 store +-448 (the saturation reading)."""
+    X = inputs.make_gr_inputs(20, 4, 64, 8, "fp8", seed=77, x_std=100.0, y_std=200.0)
+    R = X.X.to(DEV)
+    s = torch.full((20, 4), 2.0, device=DEV)
+    gr.write(R, X.y.to(DEV), s)
+    oR = oracle.write(X.X, X.y, s.cpu().double().numpy(), "fp8")
+    check_exact("fp8 saturating write", R, oR)
+    assert np.abs(oR).max() == 448.0 and torch.isfinite(R.float()).all()
+
+
 @pytest.mark.parametrize("N,d,r,w_std", [
     (37, 256, 16, 0.05), (1, 4096, 64, 0.05), (130, 1024, 48, 0.3), (300, 192, 32, 0.05),
     (129, 384, 96, 0.2), (257, 320, 128, 0.05), (2500, 4096, 64, 0.05), (1200, 8192, 32, 0.5),

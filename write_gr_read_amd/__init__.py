@@ -27,7 +27,7 @@ __all__ = ["read", "write", "fused_write_read", "residual_add_rmsnorm", "tanh_st
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgr.so")
 
-GR_F32, GR_BF16 = 0, 1
+GR_F32, GR_BF16, GR_FP8_E4M3 = 0, 1, 2
 GR_OP_READ, GR_OP_FUSED_WRITE_READ = 0, 1
 
 
@@ -96,7 +96,14 @@ def _dt(t: torch.Tensor) -> int:
         return GR_F32
     if t.dtype == torch.bfloat16:
         return GR_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float8_e4m3fn:
+        return GR_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16, or float8_e4m3fn state)")
+
+
+def _pdt(state: torch.Tensor) -> torch.dtype:
+    """dtype of y, u, gamma and weights for a given state (bf16 with an fp8 state)."""
+    return torch.bfloat16 if state.dtype == torch.float8_e4m3fn else state.dtype
 
 
 def _dev(t: torch.Tensor, name: str, shape, dtype, device) -> int:
@@ -155,8 +162,8 @@ def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
                    has_write: bool = True) -> int:
     L = _Layer(n, d, r, 1e-6, None, None, None, 16 if has_write else None)
     out = ctypes.c_size_t(0)
-    _call("gr_workspace_size", op, GR_BF16 if dtype == torch.bfloat16 else GR_F32, N,
-          ctypes.byref(L), ctypes.byref(out))
+    code = {torch.bfloat16: GR_BF16, torch.float8_e4m3fn: GR_FP8_E4M3}.get(dtype, GR_F32)
+    _call("gr_workspace_size", op, code, N, ctypes.byref(L), ctypes.byref(out))
     return out.value
 
 
@@ -164,17 +171,19 @@ def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
 
 def read(state: torch.Tensor, layer, eps: float = 1e-6, u: Optional[torch.Tensor] = None,
          s: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """GR read of ``state`` [N, n, d]: returns (u [N, d], s [N, n] fp32)."""
+    """GR read of ``state`` [N, n, d]: returns (u [N, d], s [N, n] fp32).
+    An fp8 (float8_e4m3fn) state takes bf16 parameters and gives a bf16 u."""
     N, n, d = state.shape
-    dev, dt = state.device, state.dtype
+    dev = state.device
     _dt(state)
-    sp = _dev(state, "state", (N, n, d), dt, None)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    dt = _pdt(state)
     L = _layer(layer, n, d, dt, dev, eps)
     u = torch.empty((N, d), dtype=dt, device=dev) if u is None else u
     s = torch.empty((N, n), dtype=torch.float32, device=dev) if s is None else s
     up = _dev(u, "u", (N, d), dt, dev)
     spo = _dev(s, "s", (N, n), torch.float32, dev)
-    need = workspace_size(GR_OP_READ, dt, N, n, d, L.r, layer.w_write is not None)
+    need = workspace_size(GR_OP_READ, state.dtype, N, n, d, L.r, layer.w_write is not None)
     wp, wn = _workspace(dev, need)
     _call("gr_read", sp, _dt(state), N, ctypes.byref(L), up, spo, wp, wn, _stream(dev))
     return u, s
@@ -183,10 +192,10 @@ def read(state: torch.Tensor, layer, eps: float = 1e-6, u: Optional[torch.Tensor
 def write(state: torch.Tensor, y: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
     """GR write, in place: state[t, i, :] += s[t, i] * y[t, :].  Returns state."""
     N, n, d = state.shape
-    dev, dt = state.device, state.dtype
+    dev = state.device
     _dt(state)
-    sp = _dev(state, "state", (N, n, d), dt, None)
-    yp = _dev(y, "y", (N, d), dt, dev)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    yp = _dev(y, "y", (N, d), _pdt(state), dev)
     s_p = _dev(s, "s", (N, n), torch.float32, dev)
     _call("gr_write", sp, yp, s_p, _dt(state), N, n, d, _stream(dev))
     return state
@@ -198,9 +207,10 @@ def fused_write_read(state: torch.Tensor, y: torch.Tensor, s_in: torch.Tensor, l
     """Write (y, s_in) into ``state`` in place, then read it with ``layer``:
     returns (u_next [N, d], s_next [N, n])."""
     N, n, d = state.shape
-    dev, dt = state.device, state.dtype
+    dev = state.device
     _dt(state)
-    sp = _dev(state, "state", (N, n, d), dt, None)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    dt = _pdt(state)
     yp = _dev(y, "y", (N, d), dt, dev)
     sip = _dev(s_in, "s_in", (N, n), torch.float32, dev)
     L = _layer(layer, n, d, dt, dev, eps)
@@ -208,7 +218,7 @@ def fused_write_read(state: torch.Tensor, y: torch.Tensor, s_in: torch.Tensor, l
     s = torch.empty((N, n), dtype=torch.float32, device=dev) if s is None else s
     up = _dev(u, "u_next", (N, d), dt, dev)
     spo = _dev(s, "s_next", (N, n), torch.float32, dev)
-    need = workspace_size(GR_OP_FUSED_WRITE_READ, dt, N, n, d, L.r, layer.w_write is not None)
+    need = workspace_size(GR_OP_FUSED_WRITE_READ, state.dtype, N, n, d, L.r, layer.w_write is not None)
     wp, wn = _workspace(dev, need)
     _call("gr_fused_write_read", sp, yp, sip, _dt(state), N, ctypes.byref(L), up, spo, wp, wn,
           _stream(dev))

@@ -33,7 +33,16 @@ gr_status ok() {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 gr_status check_dtype(gr_dtype dt, const char *fn) {
-    if (dt != GR_F32 && dt != GR_BF16) return fail(GR_ERROR_INVALID_VALUE, "%s: unknown dtype %d", fn, (int)dt);
+    if (dt != GR_F32 && dt != GR_BF16 && dt != GR_FP8_E4M3)
+        return fail(GR_ERROR_INVALID_VALUE, "%s: unknown dtype %d", fn, (int)dt);
+    return GR_SUCCESS;
+}
+
+// Calls whose tensors all share one dtype (no fp8 state).
+gr_status check_plain_dtype(gr_dtype dt, const char *fn) {
+    gr_status st = check_dtype(dt, fn);
+    if (st) return st;
+    if (dt == GR_FP8_E4M3) return fail(GR_ERROR_NOT_SUPPORTED, "%s: fp8 is a state dtype only", fn);
     return GR_SUCCESS;
 }
 
@@ -45,7 +54,7 @@ gr_status check_ptr(const void *p, const char *what, const char *fn) {
 
 gr_status check_width(gr_dtype dt, int64_t d, const char *fn) {
     if (d < 1) return fail(GR_ERROR_INVALID_VALUE, "%s: d = %lld must be >= 1", fn, (long long)d);
-    const int vec = dt == GR_BF16 ? 8 : 4;
+    const int vec = dt == GR_FP8_E4M3 ? 16 : dt == GR_BF16 ? 8 : 4;
     if (d % vec)
         return fail(GR_ERROR_NOT_SUPPORTED, "%s: d = %lld must be a multiple of %d for this dtype", fn,
                     (long long)d, vec);
@@ -98,7 +107,8 @@ int k2_variant() {
 
 size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
     grk::ReadArgs a{};
-    a.bf16 = dt == GR_BF16;
+    a.bf16 = dt != GR_F32;
+    a.fp8 = dt == GR_FP8_E4M3;
     a.N = N; a.n = L->n; a.d = L->d; a.r = L->r;
     a.ww = L->w_write;
     return grk::fast_path_ok(a) && !force_generic() ? grk::fast_workspace_bytes(N, L->n, L->d, L->r) : 0;
@@ -111,7 +121,7 @@ gr_status launched(hipError_t e, const char *fn) {
 
 gr_status run_read(grk::ReadArgs &a, const gr_layer *L, size_t ws_bytes, hipStream_t st,
                    const char *fn) {
-    const gr_dtype dt = a.bf16 ? GR_BF16 : GR_F32;
+    const gr_dtype dt = a.fp8 ? GR_FP8_E4M3 : a.bf16 ? GR_BF16 : GR_F32;
     const size_t need = read_workspace(dt, a.N, L);
     if (need > 0) {
         if (ws_bytes < need)
@@ -145,7 +155,8 @@ gr_status gr_read(const void *state, gr_dtype dt, int64_t N, const gr_layer *L, 
         (st = check_ptr(s, "s", fn)))
         return st;
     grk::ReadArgs a{};
-    a.bf16 = dt == GR_BF16;
+    a.bf16 = dt != GR_F32;
+    a.fp8 = dt == GR_FP8_E4M3;
     a.fused = false;
     a.state = const_cast<void *>(state);
     a.N = N;
@@ -167,7 +178,8 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
         (st = check_ptr(s_next, "s_next", fn)))
         return st;
     grk::ReadArgs a{};
-    a.bf16 = dt == GR_BF16;
+    a.bf16 = dt != GR_F32;
+    a.fp8 = dt == GR_FP8_E4M3;
     a.fused = true;
     a.state = state; a.y = y; a.s_in = s_in;
     a.N = N;
@@ -188,14 +200,15 @@ gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int6
         (st = check_ptr(s, "s", fn)))
         return st;
     (void)hipGetLastError();
-    return launched(grk::launch_write(state, y, s, dt == GR_BF16, N, n, d, (hipStream_t)stream), fn);
+    return launched(grk::launch_write(state, y, s, dt != GR_F32, dt == GR_FP8_E4M3, N, n, d,
+                                      (hipStream_t)stream), fn);
 }
 
 gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
                                gr_dtype dt, int64_t N, int32_t d, void *stream) {
     const char *fn = "residual_add_rmsnorm";
     gr_status st;
-    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if ((st = check_plain_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
     if (N == 0) return ok();
     if ((st = check_width(dt, d, fn))) return st;
     if (!(eps >= 0.f) || !isfinite(eps))
@@ -241,7 +254,7 @@ const char *gr_last_error(void) { return g_err; }
 gr_status gr_bench_tanh_standin(const void *u, void *y, gr_dtype dt, int64_t count, void *stream) {
     const char *fn = "gr_bench_tanh_standin";
     gr_status st;
-    if ((st = check_dtype(dt, fn)) || (st = check_tokens(count, fn))) return st;
+    if ((st = check_plain_dtype(dt, fn)) || (st = check_tokens(count, fn))) return st;
     if (count == 0) return ok();
     if ((st = check_ptr(u, "u", fn)) || (st = check_ptr(y, "y", fn))) return st;
     (void)hipGetLastError();

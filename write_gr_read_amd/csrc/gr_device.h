@@ -11,6 +11,7 @@
 namespace grk {
 
 typedef uint16_t bf16_t;  // bf16 storage word
+typedef uint8_t fp8_t;    // OCP e4m3 (e4m3fn) storage byte
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -35,6 +36,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ bf16_t f32_to_bf16(float a) {
     return __builtin_bit_cast(bf16_t, (__bf16)a);
 }
+
+// ---- fp8 (OCP e4m3) <-> fp32 --------------------------------------------
+// gfx950's conversions are OCP e4m3fn with round to nearest even; values that
+// round beyond 448 would become NaN, so stores clamp to +-448 first
+// (saturating, v_med3).  Every e4m3 value is exact in bf16 and fp32.
+constexpr float kFp8Max = 448.0f;
+__device__ __forceinline__ float fp8_sat(float x) { return __builtin_amdgcn_fmed3f(x, -kFp8Max, kFp8Max); }
+// four floats -> e4m3 bytes 0..3 of a word (byte 0 = a)
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat(a), fp8_sat(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat(c), fp8_sat(d), w, true);
+    return (uint32_t)w;
+}
+// bytes (0,1) or (2,3) of a word -> two floats
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false); }
+__device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true); }
 
 // eq:write for eight bf16 elements: packed y and r words (low half = even
 // channel) -> packed words of r + s y, formed by one fp32 FMA and rounded to
@@ -62,6 +80,16 @@ template <> struct Store<bf16_t> {
     // eq:write: one fp32 fused multiply-add, rounded to bf16 (stored value, widened)
     __device__ static __forceinline__ float write(float s, float y, float r) { return round(fmaf(s, y, r)); }
     __device__ static __forceinline__ void store(bf16_t *p, float v) { *p = f32_to_bf16(v); }
+};
+template <> struct Store<fp8_t> {
+    __device__ static __forceinline__ float load(const fp8_t *p) { return __builtin_amdgcn_cvt_f32_fp8((int)*p, 0); }
+    __device__ static __forceinline__ uint32_t enc(float v) {
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat(v), 0.f, 0, false) & 0xffu;
+    }
+    __device__ static __forceinline__ float round(float v) { return __builtin_amdgcn_cvt_f32_fp8((int)enc(v), 0); }
+    __device__ static __forceinline__ void store(fp8_t *p, float v) { *p = (fp8_t)enc(v); }
+    // eq:write: one fp32 fused multiply-add, rounded to e4m3 (stored value, widened)
+    __device__ static __forceinline__ float write(float s, float y, float r) { return round(fmaf(s, y, r)); }
 };
 
 // ---- activations ----------------------------------------------------------

@@ -955,7 +955,7 @@ constexpr int64_t kResidentMinTokens = 4096;
 }  // namespace
 
 bool fast_path_ok(const ReadArgs &a) {
-    if (!a.bf16 || a.n != 4) return false;
+    if (!a.bf16 || a.fp8 || a.n != 4) return false;
     if (a.r < 16 || a.r % 16 || a.r > 128) return false;
     if (a.d % kIter) return false;
     const int rows = a.r + (a.ww ? a.n : 0);

@@ -1,8 +1,9 @@
 // gr_generic.hip -- shape-generic kernels of the GR library.
 //
 // These cover every shape the C ABI accepts (1 <= n <= 8, any d with the
-// vector alignment, 0 <= r <= 512, fp32 or bf16) with plain VALU code: one
-// workgroup per token, fp32 arithmetic.  The MFMA fast path of the widened
+// vector alignment, 0 <= r <= 512, fp32, bf16 or an fp8 state with bf16
+// activations and weights) with plain VALU code: one workgroup per token,
+// fp32 arithmetic.  The MFMA fast path of the widened
 // bf16 state lives in gr_fast.hip; these are the fallback and the fp32 path.
 //
 // Method: "Paper reading: Qwen3.8 Flash Next", part 2 (Residual), sec. 4
@@ -23,12 +24,13 @@ constexpr int kRowsPerPass = 8;  // projection rows accumulated per sweep
 // wrote itself.
 //   FUSED: R' = R + s_in y is computed (one fp32 FMA), rounded to the state
 //   dtype, stored, and the read then uses the stored R'.
-template <typename T, bool FUSED>
+// T: state storage type; W: storage type of y, u, gamma and the weights.
+template <typename T, typename W, bool FUSED>
 __global__ void __launch_bounds__(kGenThreads)
-k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__restrict__ s_in,
-               int n, int d, int r, float eps, const T *__restrict__ gamma,
-               const T *__restrict__ wd, const T *__restrict__ wu, const T *__restrict__ ww,
-               T *__restrict__ u, float *__restrict__ s_out) {
+k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__restrict__ s_in,
+               int n, int d, int r, float eps, const W *__restrict__ gamma,
+               const W *__restrict__ wd, const W *__restrict__ wu, const W *__restrict__ ww,
+               W *__restrict__ u, float *__restrict__ s_out) {
     __shared__ float red[kGenThreads / 64];
     __shared__ float rho[8];
     __shared__ float proj[512 + 8];  // z (then SiLU) for k < r, write logits after
@@ -44,7 +46,7 @@ k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__re
         for (int c = tid; c < d; c += kGenThreads) {
             float v = Store<T>::load(Rt + (int64_t)i * d + c);
             if (FUSED) {
-                v = Store<T>::write(si, Store<T>::load(y + t * d + c), v);
+                v = Store<T>::write(si, Store<W>::load(y + t * d + c), v);
                 Store<T>::store(Rt + (int64_t)i * d + c, v);
             }
             ss = fmaf(v, v, ss);
@@ -65,13 +67,13 @@ k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__re
             const float ri = rho[i];
             for (int c = tid; c < d; c += kGenThreads) {
                 const int64_t j = (int64_t)i * d + c;
-                const float v = Store<T>::load(gamma + j) * Store<T>::load(Rt + j) * ri;
+                const float v = Store<W>::load(gamma + j) * Store<T>::load(Rt + j) * ri;
 #pragma unroll
                 for (int q = 0; q < kRowsPerPass; ++q) {
                     const int k = k0 + q;
                     if (k < rows) {
-                        const T *wrow = k < r ? wd + (int64_t)k * nd : ww + (int64_t)(k - r) * nd;
-                        acc[q] = fmaf(Store<T>::load(wrow + j), v, acc[q]);
+                        const W *wrow = k < r ? wd + (int64_t)k * nd : ww + (int64_t)(k - r) * nd;
+                        acc[q] = fmaf(Store<W>::load(wrow + j), v, acc[q]);
                     }
                 }
             }
@@ -94,14 +96,14 @@ k_read_generic(T *__restrict__ state, const T *__restrict__ y, const float *__re
             float g = 1.0f;
             if (r > 0) {
                 float l = 0.f;
-                const T *wrow = wu + j * r;
-                for (int k = 0; k < r; ++k) l = fmaf(Store<T>::load(wrow + k), proj[k], l);
+                const W *wrow = wu + j * r;
+                for (int k = 0; k < r; ++k) l = fmaf(Store<W>::load(wrow + k), proj[k], l);
                 g = sigmoid_f(l);
             }
-            const float v = Store<T>::load(gamma + j) * Store<T>::load(Rt + j) * rho[i];
+            const float v = Store<W>::load(gamma + j) * Store<T>::load(Rt + j) * rho[i];
             acc_u = fmaf(g, v, acc_u);
         }
-        Store<T>::store(u + t * d + c, acc_u / (float)n);
+        Store<W>::store(u + t * d + c, acc_u / (float)n);
     }
     if (s_out && tid < n) s_out[t * n + tid] = ww ? 2.0f * sigmoid_f(proj[r + tid]) : 1.0f;
 }
@@ -129,6 +131,32 @@ k_write(T *__restrict__ state, const T *__restrict__ y, const float *__restrict_
                 rv[e] = __float_as_uint(fmaf(si, __uint_as_float(yv[e]), __uint_as_float(rv[e])));
         }
         *reinterpret_cast<u32x4 *>(state + q * VEC) = rv;
+    }
+}
+
+// The same for an fp8 state and bf16 y: 16 channels (16 state bytes, 32 y
+// bytes) per item; eq:write in fp32, stored as e4m3 (saturating).
+__global__ void __launch_bounds__(256)
+k_write_fp8(fp8_t *__restrict__ state, const bf16_t *__restrict__ y, const float *__restrict__ s,
+            int64_t chunks, int n, int dv /* d / 16 */) {
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < chunks;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t cv = q % dv;
+        const int64_t ti = q / dv;  // t * n + i
+        const int64_t t = ti / n;
+        const float si = s[ti];
+        u32x4 rv = *reinterpret_cast<const u32x4 *>(state + q * 16);
+        const u32x4 *yp = reinterpret_cast<const u32x4 *>(y + (t * dv + cv) * 16);
+        const u32x4 y0 = yp[0], y1 = yp[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const u32x4 &yv = e < 2 ? y0 : y1;
+            const uint32_t ya = yv[(2 * e) & 3], yb = yv[(2 * e + 1) & 3];  // channels 4e .. 4e+3
+            const f32x2 r01 = fp8x2_lo(rv[e]), r23 = fp8x2_hi(rv[e]);
+            rv[e] = pack_fp8x4(fmaf(si, bf16_lo(ya), r01[0]), fmaf(si, bf16_hi(ya), r01[1]),
+                               fmaf(si, bf16_lo(yb), r23[0]), fmaf(si, bf16_hi(yb), r23[1]));
+        }
+        *reinterpret_cast<u32x4 *>(state + q * 16) = rv;
     }
 }
 
@@ -237,28 +265,36 @@ static unsigned grid_for(int64_t items, int64_t per_block, int64_t cap = 1 << 16
     return (unsigned)g;
 }
 
-template <typename T>
+template <typename T, typename W>
 static hipError_t read_generic_t(const ReadArgs &a, hipStream_t st) {
     T *state = (T *)a.state;
     if (a.fused)
-        hipLaunchKernelGGL((k_read_generic<T, true>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
-                           st, state, (const T *)a.y, a.s_in, a.n, a.d, a.r, a.eps,
-                           (const T *)a.gamma, (const T *)a.wd, (const T *)a.wu,
-                           (const T *)a.ww, (T *)a.u, a.s_out);
+        hipLaunchKernelGGL((k_read_generic<T, W, true>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
+                           st, state, (const W *)a.y, a.s_in, a.n, a.d, a.r, a.eps,
+                           (const W *)a.gamma, (const W *)a.wd, (const W *)a.wu,
+                           (const W *)a.ww, (W *)a.u, a.s_out);
     else
-        hipLaunchKernelGGL((k_read_generic<T, false>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
-                           st, state, (const T *)nullptr, (const float *)nullptr, a.n, a.d, a.r,
-                           a.eps, (const T *)a.gamma, (const T *)a.wd, (const T *)a.wu,
-                           (const T *)a.ww, (T *)a.u, a.s_out);
+        hipLaunchKernelGGL((k_read_generic<T, W, false>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
+                           st, state, (const W *)nullptr, (const float *)nullptr, a.n, a.d, a.r,
+                           a.eps, (const W *)a.gamma, (const W *)a.wd, (const W *)a.wu,
+                           (const W *)a.ww, (W *)a.u, a.s_out);
     return hipGetLastError();
 }
 
 hipError_t launch_read_generic(const ReadArgs &a, hipStream_t st) {
-    return a.bf16 ? read_generic_t<bf16_t>(a, st) : read_generic_t<float>(a, st);
+    if (a.fp8) return read_generic_t<fp8_t, bf16_t>(a, st);
+    return a.bf16 ? read_generic_t<bf16_t, bf16_t>(a, st) : read_generic_t<float, float>(a, st);
 }
 
-hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, int64_t N, int n,
-                        int d, hipStream_t st) {
+hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, bool fp8, int64_t N,
+                        int n, int d, hipStream_t st) {
+    if (fp8) {
+        const int64_t chunks = N * n * (int64_t)(d / 16);
+        const unsigned g = grid_for(chunks, 256, 256 * 64);
+        hipLaunchKernelGGL(k_write_fp8, dim3(g), dim3(256), 0, st, (fp8_t *)state, (const bf16_t *)y, s,
+                           chunks, n, d / 16);
+        return hipGetLastError();
+    }
     const int vec = bf16 ? 8 : 4;
     const int64_t chunks = N * n * (int64_t)(d / vec);
     const unsigned g = grid_for(chunks, 256, 256 * 64);

@@ -9,7 +9,8 @@ namespace grk {
 
 // Arguments of a read or fused write+read, already validated by the API.
 struct ReadArgs {
-    bool bf16;
+    bool bf16;           // y, u, gamma and weights are bf16 (else fp32)
+    bool fp8;            // the state is fp8 e4m3 (then bf16 is set too)
     bool fused;          // run eq:write with (y, s_in) first, in place
     void *state;         // [N][n][d]
     const void *y;       // [N][d]   (fused only)
@@ -26,8 +27,8 @@ struct ReadArgs {
 };
 
 hipError_t launch_read_generic(const ReadArgs &a, hipStream_t st);
-hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, int64_t N, int n,
-                        int d, hipStream_t st);
+hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, bool fp8, int64_t N,
+                        int n, int d, hipStream_t st);
 hipError_t launch_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
                               bool bf16, int64_t N, int d, hipStream_t st);
 hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count, hipStream_t st);

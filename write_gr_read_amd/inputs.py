@@ -10,7 +10,10 @@ Recipe (the same for every workload):
     parameter set (gamma, W_down, W_up, W_write).
   * ``standard_normal`` in float64, times the stated standard deviation (plus
     the stated mean), rounded to float32, then to bfloat16 by round-to-nearest-
-    even (torch's conversion) when the storage dtype is bfloat16.
+    even (torch's conversion) when the storage dtype is bfloat16.  Storage
+    dtype "fp8": the state X in OCP e4m3 (torch's float8_e4m3fn conversion,
+    round to nearest even, values clamped to +-448 first), everything else in
+    bfloat16.
   * Shapes follow the pages' notation: state ``[N, n, d]`` (token, branch,
     channel), ``gamma [n, d]``, ``W_down [r, n*d]``, ``W_up [n*d, r]``,
     ``W_write [n, n*d]`` (the vec index of branch i, channel c is ``i*d + c``).
@@ -35,7 +38,14 @@ def _dtype(name: str) -> torch.dtype:
         return torch.float32
     if name == "bf16":
         return torch.bfloat16
+    if name == "fp8":
+        return torch.float8_e4m3fn
     raise ValueError(f"unknown storage dtype {name!r}")
+
+
+def param_dtype(name: str) -> str:
+    """Storage dtype of y, u, gains and weights for a state dtype."""
+    return "bf16" if name == "fp8" else name
 
 
 def normal(rng: np.random.Generator, shape: Sequence[int], std: float,
@@ -65,6 +75,8 @@ def normal(rng: np.random.Generator, shape: Sequence[int], std: float,
         if mean:
             v = v + mean
         t = torch.from_numpy(v.astype(np.float32))
+        if out.dtype == torch.float8_e4m3fn:
+            t = t.clamp(-448.0, 448.0)
         out[pos:pos + cnt] = t.to(out.dtype)
         pos += cnt
     return out.view(shape)
@@ -130,8 +142,9 @@ def make_gr_inputs(N: int, n: int, d: int, r: int, dtype: str = "bf16", seed: in
     children = np.random.SeedSequence(seed).spawn(2 + 4 * n_param_sets)
     rngs = [np.random.Generator(np.random.PCG64(c)) for c in children]
     X = normal(rngs[0], (N, n, d), x_std, dtype=dtype, scale_rows=branch_scale)
-    y = normal(rngs[1], (N, d), y_std, dtype=dtype) if with_y else None
-    params = [make_layer(rngs[2 + 4 * p: 6 + 4 * p], n, d, r, dtype, w_std, gamma_std,
+    pdt = param_dtype(dtype)
+    y = normal(rngs[1], (N, d), y_std, dtype=pdt) if with_y else None
+    params = [make_layer(rngs[2 + 4 * p: 6 + 4 * p], n, d, r, pdt, w_std, gamma_std,
                          with_write) for p in range(n_param_sets)]
     return GRInputs(N, n, d, r, dtype, eps, X, y, params)
 
@@ -171,6 +184,9 @@ WORKLOADS = {
             y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
     5: dict(name="gr_chain32_bf16", kind="chain", N=32768, n=4, d=2048, r=32, dtype="bf16",
             layers=32, branch_scale=None, param_sets=32),
+    # the prefill shape with an fp8 (e4m3) branch state: the pages' FP8 state
+    6: dict(name="gr_prefill_fp8", kind="gr", N=16384, n=4, d=4096, r=64, dtype="fp8",
+            y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
 }
 
 
