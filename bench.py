@@ -9,9 +9,10 @@ step of the hot path.  Inputs are seeded synthetic tensors already resident in
 HBM.  Prints one JSON line on stdout; progress goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload {prefill,decode,addnorm,chain,tiny,all}
+       python bench.py --workload {prefill,prefill_fp8,decode,addnorm,chain,tiny,all}
 The default (prefill) line is the headline; the other workloads print their own
-line (decode: us per call with the state warm in cache, back to back; addnorm:
+line (prefill_fp8: the same shape with an e4m3 branch state; decode: us per
+call with the state warm in cache, back to back; addnorm:
 the n = 1 fused residual add + RMSNorm; chain: 32 sublayers of read -> F ->
 fused write+read -> ... -> write with the elementwise F stand-in).
 """
@@ -32,10 +33,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(N, n, d, r, elt=2, has_write=True):
+def algorithmic_bytes(N, n, d, r, elt=2, has_write=True, state_elt=None):
     """Bytes the fused write+read must move: state in and out, y in, u out,
-    s in and out (fp32), plus gamma and the gate/write weights once."""
-    per_token = 2 * n * d * elt + 2 * d * elt + 2 * n * 4
+    s in and out (fp32), plus gamma and the gate/write weights once.  `elt` is
+    the size of y, u and the weights; `state_elt` that of the branch state
+    (default: the same; 1 for an e4m3 state)."""
+    se = elt if state_elt is None else state_elt
+    per_token = 2 * n * d * se + 2 * d * elt + 2 * n * 4
     weights = n * d * elt + 2 * r * n * d * elt + (n * n * d * elt if has_write else 0)
     return N * per_token + weights
 
@@ -141,6 +145,25 @@ def bench_other(which, args, dev):
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "cache": "warm, back-to-back"},
                     dtype=Xin.dtype, higher=False, tokens_per_s=N / (ms * 1e-3),
                     roofline=roofline(alg, ms, "gr_fused_write_read"))
+    if which == "prefill_fp8":
+        W = inputs.WORKLOADS[6]
+        log(f"generating workload {W['name']} ...")
+        Xin = inputs.workload(6)
+        N, n, d, r = Xin.N, Xin.n, Xin.d, Xin.r
+        p0, p1 = Xin.params[0].to(dev), Xin.params[1].to(dev)
+        X, y = Xin.X.to(dev), Xin.y.to(dev)
+        u = torch.empty((N, d), dtype=y.dtype, device=dev)
+        so = torch.empty((N, n), dtype=torch.float32, device=dev)
+        _, s_in = gr.read(X, p0)
+        ms = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so), args.steps, args.warmup, stream)
+        alg = algorithmic_bytes(N, n, d, r, 2, state_elt=1)
+        log(f"prefill_fp8: {ms * 1e3:.1f} us/call, {N / (ms * 1e-3) / 1e6:.2f} M tok/s")
+        return line(f"GR fused write+read tokens/s (prefill, d={d}, n={n}, r={r}, e4m3 state)",
+                    N / (ms * 1e-3), "tokens/s", args.steps, args.warmup, ms,
+                    {"workload": W["name"], "N": N, "d": d, "n": n, "r": r,
+                     "state_dtype": "e4m3", "activation_dtype": "bf16", "accumulation": "fp32"},
+                    dtype="bf16", roofline=roofline(alg, ms, "gr_fused_write_read",
+                                                    stored_traffic("gr_fused_write_read_fp8")))
     if which == "addnorm":
         W = inputs.WORKLOADS[2]
         A = inputs.workload(2)
@@ -207,7 +230,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "addnorm", "chain", "tiny", "all"])
+                    choices=["prefill", "prefill_fp8", "decode", "addnorm", "chain", "tiny", "all"])
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
 
@@ -223,7 +246,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload != "prefill":
-        names = ["decode", "addnorm", "chain", "tiny"] if args.workload == "all" else [args.workload]
+        names = (["prefill_fp8", "decode", "addnorm", "chain", "tiny"] if args.workload == "all"
+                 else [args.workload])
         for w in names:
             print(json.dumps(bench_other(w, args, dev)), flush=True)
         if args.workload != "all":

@@ -92,14 +92,32 @@ def test_shapes(N, n, d, r, dtype):
 @pytest.mark.parametrize("N,n,d,r", [
     (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (17, 3, 64, 5), (70, 4, 512, 32),
     (130, 4, 1024, 48), (300, 4, 192, 32), (129, 4, 384, 96), (257, 4, 320, 128), (64, 4, 256, 0),
+    (256, 4, 4096, 64),
 ])
-def test_fp8_state_shapes(N, n, d, r):
+@pytest.mark.parametrize("path", ["default", "generic"])
+def test_fp8_state_shapes(N, n, d, r, path, monkeypatch):
     """fp8 (e4m3) branch state, bf16 everything else: read, write and fused
     against the oracle on the same stored e4m3 values (state bit for bit,
-    u at the bf16 tolerance)."""
+    u at the bf16 tolerance).  "default" takes the MFMA kernels wherever the
+    shape allows (n = 4, r a multiple of 16, d a multiple of 64), including a
+    last channel range of one 64-channel unit (d = 192, 320), every k-step
+    count of the up projection and the channel-split kernel 1 of few tokens;
+    "generic" forces the shape-generic kernels on the same shapes."""
+    if path == "generic":
+        monkeypatch.setenv("GR_KERNEL_VARIANT", "generic")
     X = inputs.make_gr_inputs(N, n, d, r, "fp8", seed=3 * N + 5 * n + d + r, w_std=0.05,
                               branch_scale=(1.0, 0.5, 2.0, 1.0)[:n] if n == 4 else None)
-    run_read_write_fused(X, f"fp8-N{N}-n{n}-d{d}-r{r}")
+    run_read_write_fused(X, f"fp8-{path}-N{N}-n{n}-d{d}-r{r}")
+
+
+@pytest.mark.parametrize("N,d,r,w_std", [(2500, 4096, 64, 0.05), (1200, 8192, 32, 0.5),
+                                         (3000, 192, 16, 0.3), (700, 2560, 96, 0.2)])
+def test_fp8_state_many_tiles(N, d, r, w_std):
+    """fp8 state with more token tiles than kernel-2 workgroups, so each
+    workgroup walks several tiles (and, at d = 192, a range of one unit)."""
+    X = inputs.make_gr_inputs(N, 4, d, r, "fp8", seed=11 * N + d + r, w_std=w_std,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"fp8-tiles-N{N}-d{d}-r{r}")
 
 
 def test_fp8_state_saturates():
@@ -292,6 +310,18 @@ def test_prefill_workload_full_sampled():
     """Workload 3 at its full size (N=16384), 96 sampled tokens."""
     Xin = inputs.workload(3)
     sampled_read_parity(Xin, sample_tokens(Xin.N, 96, seed=3), "prefill-16384")
+
+
+def test_prefill_fp8_workload_subset():
+    """Workload 6 (the prefill shape with an e4m3 state), first 1024 tokens,
+    every token compared."""
+    run_read_write_fused(inputs.workload(6, N=1024), "prefill-fp8-1024")
+
+
+def test_prefill_fp8_workload_full_sampled():
+    """Workload 6 at its full size (N=16384), 96 sampled tokens."""
+    Xin = inputs.workload(6)
+    sampled_read_parity(Xin, sample_tokens(Xin.N, 96, seed=6), "prefill-fp8-16384")
 
 
 def test_decode_workload():

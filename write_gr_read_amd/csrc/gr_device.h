@@ -65,6 +65,31 @@ __device__ __forceinline__ u32x4 write8_bf16(float s, u32x4 y, u32x4 r) {
     return o;
 }
 
+// eq:write for eight e4m3 elements: r holds bytes 0..7 (channel order), y four
+// packed bf16 words -> the stored bytes of r + s y (one fp32 FMA, saturated,
+// rounded to e4m3, nearest even).
+__device__ __forceinline__ u32x2 write8_fp8(float s, u32x4 y, u32x2 r) {
+    u32x2 o;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const f32x2 a = fp8x2_lo(r[k]), b = fp8x2_hi(r[k]);
+        o[k] = pack_fp8x4(fmaf(s, bf16_lo(y[2 * k]), a.x), fmaf(s, bf16_hi(y[2 * k]), a.y),
+                          fmaf(s, bf16_lo(y[2 * k + 1]), b.x), fmaf(s, bf16_hi(y[2 * k + 1]), b.y));
+    }
+    return o;
+}
+// Eight e4m3 bytes -> four packed bf16 words of the same values (exact).
+__device__ __forceinline__ u32x4 widen8_fp8_bf16(u32x2 r) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const f32x2 a = fp8x2_lo(r[k]), b = fp8x2_hi(r[k]);
+        w[2 * k] = pack_bf16x2(a.x, a.y);
+        w[2 * k + 1] = pack_bf16x2(b.x, b.y);
+    }
+    return w;
+}
+
 // Storage-type adapters for the generic kernels.
 template <typename T> struct Store;
 template <> struct Store<float> {

@@ -209,6 +209,10 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
     }
 }
 
+// State element type of the fast path: bf16 words or e4m3 bytes.
+template <bool F8> struct StateT { using type = bf16_t; using vec8 = u32x4; };
+template <> struct StateT<true> { using type = fp8_t; using vec8 = u32x2; };
+
 // ---------------------------------------------------------------------------
 #ifndef GR_K1_WAVES_PER_SIMD
 #define GR_K1_WAVES_PER_SIMD 4
@@ -233,10 +237,14 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
 // call (PREP = true: every token tile would otherwise redo the same split).
 // It is staged in a double-buffered LDS slot per chunk: the chunk after next
 // is loaded into registers while a chunk is used, with one barrier per chunk.
-// DEPTH rounds of state / y loads are in flight ahead of the round in use.
-template <bool FUSED, int NRB, int DEPTH, bool PREP, int TG>
+// DEPTH > 0: DEPTH rounds of state / y loads are in flight ahead of the round
+// in use.  DEPTH = 0: the next round's state loads are issued as soon as the
+// element phase has freed their registers, so they fly during the MFMA phase
+// at no register cost; y (mostly an L2 hit: the n workgroups of a tile share
+// it) is loaded at the start of its round.
+template <bool FUSED, int NRB, int DEPTH, bool PREP, int TG, bool F8>
 __global__ void __launch_bounds__(64 * (kWaves / TG), (NRB <= 5 && TG == 1 && PREP) ? GR_K1_WAVES_PER_SIMD : 2)
-k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
+k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
               FastShape sh) {
@@ -251,6 +259,8 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     constexpr int WV = PREP ? (2 * NV + THREADS - 1) / THREADS  // hi and lo planes, ready-made
                             : (NV + THREADS - 1) / THREADS;     // W and gamma, split here
     constexpr int NSLOT = DEPTH + 1;
+    using T = typename StateT<F8>::type;
+    using SV = typename StateT<F8>::vec8;              // 8 channels of the state
     static_assert(PCS == 16, "a round is 16 pieces of 8 channels per token");
     // [buffer][hi/lo][row][k]
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
@@ -341,21 +351,22 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     }
     // addresses: a wave-uniform base (token t0, this branch and split) plus a
     // 32-bit lane offset; instruction q adds 4q tokens, round rd adds rd*RC
-    bf16_t *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
+    T *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
     const bf16_t *const ybase = FUSED ? y + t0 * (int64_t)d + c_base : nullptr;
     const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
     const int64_t qstride = 4 * nd, qystride = 4 * (int64_t)d;
 
-    u32x4 rr[NSLOT][NQ], yy[NSLOT][NQ];
-    auto load_round = [&](int rd, int slot) {
+    SV rr[NSLOT][NQ];
+    u32x4 yy[NSLOT][NQ];
+    auto load_round = [&](int rd, int slot, bool ds = true, bool dy = true) {
         const bool in = rd < nround && rd * RC + 8 * m16 < chan;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            rr[slot][q] = u32x4{0u, 0u, 0u, 0u};
-            yy[slot][q] = u32x4{0u, 0u, 0u, 0u};
+            if (ds) rr[slot][q] = SV{};
+            if (dy) yy[slot][q] = u32x4{0u, 0u, 0u, 0u};
             if (vq[q] && in) {
-                rr[slot][q] = *reinterpret_cast<const u32x4 *>(sbase + q * qstride + rd * RC + soff);
-                if (FUSED) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff);
+                if (ds) rr[slot][q] = *reinterpret_cast<const SV *>(sbase + q * qstride + rd * RC + soff);
+                if (FUSED && dy) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff);
             }
         }
     };
@@ -372,17 +383,29 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     load_w(1);
 #pragma unroll
     for (int q = 0; q < DEPTH; ++q) load_round(q, q);
+    if (DEPTH == 0) load_round(0, 0, true, false);
     __syncthreads();
     for (int rd = 0; rd < nround; ++rd) {
-        load_round(rd + DEPTH, DEPTH);
+        if (DEPTH > 0) load_round(rd + DEPTH, DEPTH);
+        else load_round(rd, 0, false, true);
         // eq:write in the load layout: store, sum of squares, LDS tile
         const bool in = rd * RC + 8 * m16 < chan;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            u32x4 w = rr[0][q];
-            if (FUSED) {
-                w = write8_bf16(sq[q], yy[0][q], rr[0][q]);
-                if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+            u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
+            if constexpr (F8) {
+                u32x2 o = rr[0][q];
+                if (FUSED) {
+                    o = write8_fp8(sq[q], yy[0][q], rr[0][q]);
+                    if (vq[q] && in) *reinterpret_cast<u32x2 *>(sbase + q * qstride + rd * RC + soff) = o;
+                }
+                w = widen8_fp8_bf16(o);
+            } else {
+                w = rr[0][q];
+                if (FUSED) {
+                    w = write8_bf16(sq[q], yy[0][q], rr[0][q]);
+                    if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) ss[q] = dot2_bf16(w[e], w[e], ss[q]);
@@ -392,6 +415,7 @@ k_stream_proj(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         // instructions of a wave execute in order); keep the phases apart so
         // the element work and the MFMA operands are not live together
         __builtin_amdgcn_sched_barrier(0);
+        if (DEPTH == 0) load_round(rd + 1, 0, true, false);
 #pragma unroll
         for (int h = 0; h < RC / kIter; ++h) {
             const int it = rd * (RC / kIter) + h;
@@ -871,8 +895,158 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
     }
 }
 
-template <bool FUSED>
+// ---------------------------------------------------------------------------
+// Kernel 2 for an e4m3 state, resident form.  Same walk as above, but a step
+// is one 64-channel unit: a 64-byte half line of the state per token and
+// branch, of which lane group g owns channels 16g .. 16g + 15 (one 16-byte
+// word of e4m3).  The W_up rows of a unit sit in LDS so that block h
+// (h = 0..3) of the up projection lands there: LDS row 16h + 4g + m of a unit
+// holds channel 16g + 4h + m, and tl[m] of block h is element 4h + m of the
+// lane's word.  Each branch's word of the next step is fetched as soon as the
+// current step has used it.  (Two units per step, one whole 128-byte line,
+// needs 16 more VGPRs than the two-workgroups-per-CU budget allows and
+// measured slower.)
+constexpr int kF8Unit = 64;
+
+template <int NB, int RKS, int CH>
+__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? GR_K2R_WAVES_PER_SIMD : 2)
+k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+                            const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
+                            FastShape sh, int ranges, int P) {
+    constexpr int NU = CH / kF8Unit;                   // units per range
+    constexpr int RK = RKS * 32;
+    constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
+    __shared__ __attribute__((aligned(16))) bf16_t lds_u[NB * CH * kPitch];
+    __shared__ __attribute__((aligned(16))) float lds_g[NB * CH];
+
+    const int d = sh.d, r = sh.r;
+    const int range = (int)(blockIdx.x % ranges);
+    const int64_t p = blockIdx.x / ranges;
+    const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
+    if (p >= tiles) return;                            // whole workgroup
+    const int c_begin = range * CH;
+    const int nchan = (d - c_begin) < CH ? (d - c_begin) : CH;   // a multiple of kF8Unit
+    const int nsteps = nchan / kF8Unit;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m16 = lane & 15;
+    const float inv_n = 1.0f / (float)NB;
+
+    auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
+    auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
+        const int64_t t = token(T);
+        const bool ok = t < sh.N;
+#pragma unroll
+        for (int ks = 0; ks < RKS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+            if (ok) {
+                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
+                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
+            }
+            hi[ks] = as_bf16x8(v);
+            lo[ks] = as_bf16x8(vl);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+    };
+    // e4m3 word of branch i, step st of tile T
+    auto load_state = [&](int64_t T, int st, int i) {
+        const int64_t t = token(T);
+        if (t >= sh.N) return u32x4{0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4 *>(state + t * (int64_t)NB * d + (int64_t)i * d + c_begin +
+                                                st * kF8Unit + 16 * g);
+    };
+
+    bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
+    float rms[NB], nrms[NB];
+    u32x4 sv[NB];
+    int64_t T = p;
+    int st = 0;
+    load_act(T, bop, bopl, rms);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) sv[i] = load_state(T, 0, i);
+
+    // stage W_up rows (branch i, channel cc of the range) and gamma/n
+    for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
+        const int row = v / (RK / 8), kv = v % (RK / 8);
+        const int i = row / CH, cc = row % CH, c64 = cc % kF8Unit;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (cc < nchan && kv * 8 < r)
+            w = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8);
+        const int pos = (i * NU + cc / kF8Unit) * kF8Unit + 16 * ((c64 >> 2) & 3) + 4 * (c64 >> 4) + (c64 & 3);
+        *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w;
+    }
+    for (int v = tid; v < NB * CH; v += kResThreads) {
+        const int i = v / CH, cc = v % CH;
+        lds_g[v] = cc < nchan ? bf16_to_f32(f32_to_bf16(bf16_to_f32(gamma[(int64_t)i * d + c_begin + cc]) * inv_n))
+                              : 0.f;
+    }
+    __syncthreads();
+
+    for (;;) {
+        int64_t Tn = T;
+        int sn = st + 1;
+        if (sn == nsteps) { sn = 0; Tn = T + P; }
+        const bool more = Tn < tiles;
+        if (sn == 0 && more) load_act(Tn, nbop, nbopl, nrms);
+
+        float uacc[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) uacc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                f32x4 tl = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t *ap = &lds_u[((i * NU + st) * kF8Unit + 16 * h + m16) * kPitch + 8 * g];
+#pragma unroll
+                for (int ks = 0; ks < RKS; ++ks) {
+                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                }
+                // tl[m] = -log2(e) * l for channel 16g + 4h + m of the unit, branch i
+                const f32x2 x01 = fp8x2_lo(sv[i][h]), x23 = fp8x2_hi(sv[i][h]);
+                const float x[4] = {x01.x, x01.y, x23.x, x23.y};
+                const float *gp = &lds_g[i * CH + st * kF8Unit + 16 * g + 4 * h];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = 4 * h + m;
+                    const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                    uacc[e] = fmaf(x[m] * gp[m], __builtin_amdgcn_rcpf(den), uacc[e]);
+                }
+            }
+            // materialise per branch (else the element work sinks into the store's branch)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) asm volatile("" : "+v"(uacc[e]));
+            // branch i of this step is consumed: fetch it for the next step
+            if (more) sv[i] = load_state(Tn, sn, i);
+        }
+        const int64_t t = token(T);
+        if (t < sh.N) {
+            bf16_t *q = u + t * (int64_t)d + c_begin + st * kF8Unit + 16 * g;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[8 * k + 2 * e], uacc[8 * k + 2 * e + 1]);
+                *reinterpret_cast<u32x4 *>(q + 8 * k) = o;
+            }
+        }
+        if (!more) break;
+        if (sn == 0) {
+#pragma unroll
+            for (int ks = 0; ks < RKS; ++ks) { bop[ks] = nbop[ks]; bopl[ks] = nbopl[ks]; }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) rms[i] = nrms[i];
+        }
+        T = Tn;
+        st = sn;
+    }
+}
+
+template <bool FUSED, bool F8>
 hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    using T = typename StateT<F8>::type;
     const int64_t tiles8 = (sh.tiles + 7) / 8 * 8;
     const unsigned grid = (unsigned)(tiles8 * sh.n * sh.ksplit);
     const bf16_t *y = (const bf16_t *)a.y;
@@ -887,12 +1061,12 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
         if (sh.prep)                                                                        \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, true, kTG>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
-                               (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, true, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
+                               (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         else                                                                                \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepthSplit, false, kTG>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
-                               (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
+            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepthSplit, false, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
+                               (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;
     switch (sh.row_blocks) {
@@ -936,6 +1110,33 @@ hipError_t launch_k2_resident_rks(const ReadArgs &a, const FastShape &sh, const 
     return hipGetLastError();
 }
 
+template <int NB, int RKS>
+hipError_t launch_k2_resident_fp8_rks(const ReadArgs &a, const FastShape &sh, const Workspace &w,
+                                      hipStream_t st) {
+    constexpr int CH = ResidentCfg<RKS>::CH;
+    const int ranges = (sh.d + CH - 1) / CH;
+    const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
+    int64_t P = (kResWgsTarget + ranges / 2) / ranges;
+    if (P > tiles) P = tiles;
+    if (P < 1) P = 1;
+    hipLaunchKernelGGL((k_gate_combine_resident_fp8<NB, RKS, CH>), dim3((unsigned)(ranges * P)),
+                       dim3(kResThreads), 0, st, (const fp8_t *)a.state, (const bf16_t *)a.gamma,
+                       (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges, (int)P);
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_k2_resident_fp8(const ReadArgs &a, const FastShape &sh, const Workspace &w,
+                                  hipStream_t st) {
+    switch (sh.rk / 32) {
+    case 1: return launch_k2_resident_fp8_rks<NB, 1>(a, sh, w, st);
+    case 2: return launch_k2_resident_fp8_rks<NB, 2>(a, sh, w, st);
+    case 3: return launch_k2_resident_fp8_rks<NB, 3>(a, sh, w, st);
+    case 4: return launch_k2_resident_fp8_rks<NB, 4>(a, sh, w, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int NB>
 hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                               hipStream_t st) {
@@ -955,7 +1156,7 @@ constexpr int64_t kResidentMinTokens = 4096;
 }  // namespace
 
 bool fast_path_ok(const ReadArgs &a) {
-    if (!a.bf16 || a.fp8 || a.n != 4) return false;
+    if (!a.bf16 || a.n != 4) return false;
     if (a.r < 16 || a.r % 16 || a.r > 128) return false;
     if (a.d % kIter) return false;
     const int rows = a.r + (a.ww ? a.n : 0);
@@ -973,7 +1174,8 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     const FastShape sh = shape_of(a);
     Workspace w;
     workspace_layout(sh, (char *)a.ws, &w);
-    hipError_t e = a.fused ? launch_k1<true>(a, sh, w, st) : launch_k1<false>(a, sh, w, st);
+    hipError_t e = a.fp8 ? (a.fused ? launch_k1<true, true>(a, sh, w, st) : launch_k1<false, true>(a, sh, w, st))
+                         : (a.fused ? launch_k1<true, false>(a, sh, w, st) : launch_k1<false, false>(a, sh, w, st));
     if (e != hipSuccess) return e;
     const dim3 rgrid((unsigned)((sh.N + kRedWaves - 1) / kRedWaves)), rblock(64 * kRedWaves);
     switch (sh.ksplit) {
@@ -985,6 +1187,8 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // (an e4m3 state has the resident form only)
+    if (a.fp8) return launch_k2_resident_fp8<4>(a, sh, w, st);
     const bool resident = a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
     return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }
