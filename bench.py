@@ -9,9 +9,10 @@ step of the hot path.  Inputs are seeded synthetic tensors already resident in
 HBM.  Prints one JSON line on stdout; progress goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload {prefill,prefill_fp8,decode,addnorm,chain,tiny,all}
+       python bench.py --workload {prefill,prefill_fp8,prefill_r320,decode,addnorm,chain,tiny,all}
 The default (prefill) line is the headline; the other workloads print their own
-line (prefill_fp8: the same shape with an e4m3 branch state; decode: us per
+line (prefill_fp8: the same shape with an e4m3 branch state; prefill_r320: the
+pages' model shape d = 2560 with gate rank r = d/8 = 320; decode: us per
 call with the state warm in cache, back to back; addnorm:
 the n = 1 fused residual add + RMSNorm; chain: 32 sublayers of read -> F ->
 fused write+read -> ... -> write with the elementwise F stand-in).
@@ -42,6 +43,12 @@ def algorithmic_bytes(N, n, d, r, elt=2, has_write=True, state_elt=None):
     per_token = 2 * n * d * se + 2 * d * elt + 2 * n * 4
     weights = n * d * elt + 2 * r * n * d * elt + (n * n * d * elt if has_write else 0)
     return N * per_token + weights
+
+
+def gate_flops(N, n, d, r, has_write=True):
+    """Contraction flops of one read: down and up projections of the gate
+    (2 r n d each) and the write projection (2 n n d), per token."""
+    return N * (4 * r * n * d + (2 * n * n * d if has_write else 0))
 
 
 def kernel_source_digest():
@@ -145,10 +152,11 @@ def bench_other(which, args, dev):
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "cache": "warm, back-to-back"},
                     dtype=Xin.dtype, higher=False, tokens_per_s=N / (ms * 1e-3),
                     roofline=roofline(alg, ms, "gr_fused_write_read"))
-    if which == "prefill_fp8":
-        W = inputs.WORKLOADS[6]
+    if which in ("prefill_fp8", "prefill_r320"):
+        k = 6 if which == "prefill_fp8" else 7
+        W = inputs.WORKLOADS[k]
         log(f"generating workload {W['name']} ...")
-        Xin = inputs.workload(6)
+        Xin = inputs.workload(k)
         N, n, d, r = Xin.N, Xin.n, Xin.d, Xin.r
         p0, p1 = Xin.params[0].to(dev), Xin.params[1].to(dev)
         X, y = Xin.X.to(dev), Xin.y.to(dev)
@@ -156,14 +164,17 @@ def bench_other(which, args, dev):
         so = torch.empty((N, n), dtype=torch.float32, device=dev)
         _, s_in = gr.read(X, p0)
         ms = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so), args.steps, args.warmup, stream)
-        alg = algorithmic_bytes(N, n, d, r, 2, state_elt=1)
-        log(f"prefill_fp8: {ms * 1e3:.1f} us/call, {N / (ms * 1e-3) / 1e6:.2f} M tok/s")
-        return line(f"GR fused write+read tokens/s (prefill, d={d}, n={n}, r={r}, e4m3 state)",
+        f8 = which == "prefill_fp8"
+        alg = algorithmic_bytes(N, n, d, r, 2, state_elt=1 if f8 else 2)
+        log(f"{which}: {ms * 1e3:.1f} us/call, {N / (ms * 1e-3) / 1e6:.2f} M tok/s")
+        sdt = "e4m3" if f8 else "bf16"
+        return line(f"GR fused write+read tokens/s (prefill, d={d}, n={n}, r={r}, {sdt} state)",
                     N / (ms * 1e-3), "tokens/s", args.steps, args.warmup, ms,
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r,
-                     "state_dtype": "e4m3", "activation_dtype": "bf16", "accumulation": "fp32"},
-                    dtype="bf16", roofline=roofline(alg, ms, "gr_fused_write_read",
-                                                    stored_traffic("gr_fused_write_read_fp8")))
+                     "state_dtype": sdt, "activation_dtype": "bf16", "accumulation": "fp32"},
+                    dtype="bf16", gate_tflops=gate_flops(N, n, d, r) / (ms * 1e-3) / 1e12,
+                    roofline=roofline(alg, ms, "gr_fused_write_read",
+                                      stored_traffic("gr_fused_write_read_" + ("fp8" if f8 else "r320"))))
     if which == "addnorm":
         W = inputs.WORKLOADS[2]
         A = inputs.workload(2)
@@ -230,7 +241,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "prefill_fp8", "decode", "addnorm", "chain", "tiny", "all"])
+                    choices=["prefill", "prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny",
+                             "all"])
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
 
@@ -246,7 +258,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload != "prefill":
-        names = (["prefill_fp8", "decode", "addnorm", "chain", "tiny"] if args.workload == "all"
+        names = (["prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny"] if args.workload == "all"
                  else [args.workload])
         for w in names:
             print(json.dumps(bench_other(w, args, dev)), flush=True)

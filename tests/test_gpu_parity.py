@@ -324,6 +324,18 @@ def test_prefill_fp8_workload_full_sampled():
     sampled_read_parity(Xin, sample_tokens(Xin.N, 96, seed=6), "prefill-fp8-16384")
 
 
+def test_real_shape_r320_subset():
+    """Workload 7 (the pages' model shape: d = 2560, r = d/8 = 320), first
+    256 tokens, every token compared."""
+    run_read_write_fused(inputs.workload(7, N=256), "d2560-r320-256")
+
+
+def test_real_shape_r320_full_sampled():
+    """Workload 7 at its full size (N=16384), 64 sampled tokens."""
+    Xin = inputs.workload(7)
+    sampled_read_parity(Xin, sample_tokens(Xin.N, 64, seed=7), "d2560-r320-16384")
+
+
 def test_decode_workload():
     """Workload 4 (N=256), every token."""
     run_read_write_fused(inputs.workload(4), "decode-256")

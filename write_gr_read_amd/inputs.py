@@ -18,9 +18,10 @@ Recipe (the same for every workload):
     channel), ``gamma [n, d]``, ``W_down [r, n*d]``, ``W_up [n*d, r]``,
     ``W_write [n, n*d]`` (the vec index of branch i, channel c is ``i*d + c``).
 
-Workload sizes are the five synthetic configurations the GR measurements use
+Workload sizes are the synthetic configurations the GR measurements use
 (tiny fp32 read/write, n=1 fused add+RMSNorm, prefill, decode, a 32-sublayer
-chain). No dataset is involved anywhere.
+chain, the prefill shape with an e4m3 state, and the pages' own model shape
+d = 2560 with gate rank r = d/8 = 320). No dataset is involved anywhere.
 """
 from __future__ import annotations
 
@@ -172,7 +173,7 @@ def make_addnorm_inputs(N: int, d: int, dtype: str = "bf16", seed: int = 0,
     return AddNormInputs(N, d, dtype, eps, x, y, w)
 
 
-# The five synthetic workloads, by number. Seed of workload k is 1000*k.
+# The synthetic workloads, by number. Seed of workload k is 1000*k.
 WORKLOADS = {
     1: dict(name="gr_tiny_f32", kind="gr", N=64, n=4, d=256, r=16, dtype="f32",
             y_std=0.1, branch_scale=None, param_sets=2),
@@ -187,6 +188,9 @@ WORKLOADS = {
     # the prefill shape with an fp8 (e4m3) branch state: the pages' FP8 state
     6: dict(name="gr_prefill_fp8", kind="gr", N=16384, n=4, d=4096, r=64, dtype="fp8",
             y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
+    # the pages' own model shape: d = 2560 and the gate rank r = d/8 = 320
+    7: dict(name="gr_prefill_d2560_r320", kind="gr", N=16384, n=4, d=2560, r=320, dtype="bf16",
+            y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
 }
 
 
@@ -194,7 +198,7 @@ def workload(k: int, N: Optional[int] = None):
     """Inputs of workload ``k`` (optionally with fewer tokens, same recipe).
 
     Parameter set 0 feeds the untimed read that produces the write strengths of
-    the fused call; parameter set 1 is the next sublayer's (workloads 1, 3, 4).
+    the fused call; parameter set 1 is the next sublayer's (workloads 1, 3, 4, 6, 7).
     Workload 5 has one parameter set per sublayer and no y (F makes it).
     """
     w = WORKLOADS[k]
