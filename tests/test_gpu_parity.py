@@ -182,6 +182,30 @@ def test_workspace_needs_no_initialisation():
     assert torch.isfinite(runs[0][1].float()).all()
 
 
+@pytest.mark.parametrize("N,d,r,w_std", [
+    (1, 2560, 320, 0.05), (64, 2560, 320, 0.05), (37, 512, 144, 0.05), (130, 1024, 256, 0.2),
+    (300, 640, 320, 0.05), (129, 2560, 160, 0.3), (200, 448, 224, 0.5),
+])
+def test_wide_gate_shapes(N, d, r, w_std):
+    """Gate ranks beyond 124 (r + n > 128 projection rows): kernel 1's wide
+    form (raw weights in LDS, gamma . R' split into hi / lo on the state side)
+    and kernel 2's 32-channel resident form.  Ragged token tiles, channel
+    splits at few tokens (N = 1, 64), r from 144 to 320, and large weights
+    (w_std = 0.5) so the gate spans (0, 1)."""
+    X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=13 * N + d + r, w_std=w_std,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"wide-N{N}-d{d}-r{r}")
+
+
+def test_wide_gate_without_write_projection():
+    """r = 320 with no W_write: 320 projection rows (20 blocks), s == 1."""
+    X = inputs.make_gr_inputs(100, 4, 1280, 320, "bf16", seed=43, with_write=False)
+    u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))
+    assert torch.all(s == 1.0)
+    ou, _, A = orc_read(X.X, X.params[0], "bf16")
+    check("wide no-write u", u, ou, "bf16", scale=A)
+
+
 def test_no_write_projection_gives_unit_strength():
     X = inputs.make_gr_inputs(40, 4, 256, 16, "bf16", seed=41, with_write=False)
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))

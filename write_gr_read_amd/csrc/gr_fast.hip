@@ -77,7 +77,9 @@ constexpr int kK2Tile = 16 * kK2Waves;                 // tokens per kernel-2 wo
 #define GR_K2_SUB 1
 #endif
 constexpr int kK2Sub = GR_K2_SUB;  // 32-channel chunks per kernel-2 iteration (whole 128-byte lines)
-constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128
+constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128 (narrow gate)
+constexpr int kMaxWideRowBlocks = 21;     // wide gate (kernel 1 wide form): r + n up to 336
+constexpr int kMaxWideRKS = 10;           // wide gate: r up to 320 (k-steps of 32 of the up projection)
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 #ifndef GR_SPLIT_TARGET
 #define GR_SPLIT_TARGET 64
@@ -100,6 +102,7 @@ struct FastShape {
     int k2_chan;         // channels per kernel-2 workgroup (multiple of kChunk)
     int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
     bool prep;           // W' split once per call by k_prep_wprime (enough token tiles)
+    bool wide;           // r + n beyond 128: kernel 1's wide form (gamma on the state side, no W')
     int64_t N, tiles;
 };
 
@@ -126,7 +129,8 @@ FastShape shape_of(const ReadArgs &a) {
     const int64_t tiles2 = (a.N + kK2Tile - 1) / kK2Tile;
     while (tiles2 * ((s.d + c2 - 1) / c2) < 1024 && c2 > kChunk && (c2 / 2) % kChunk == 0) c2 /= 2;
     s.k2_chan = c2;
-    s.prep = s.tiles >= kPrepMinTiles;
+    s.wide = s.row_blocks > kMaxRowBlocks;
+    s.prep = !s.wide && s.tiles >= kPrepMinTiles;
     return s;
 }
 
@@ -135,7 +139,7 @@ FastShape shape_of(const ReadArgs &a) {
 //   partial   [N][n][ksplit][pstride] f32: ss at [0], projection rows at [4 ..]
 //   act       [N][2][rk] bf16     -log2(e) SiLU(z) as hi, lo words, zero-padded
 //   rms       [N][n] f32          1/rho
-//   wprime    [n][2][16*row_blocks][d] bf16   W' hi and lo planes (when prep)
+//   wprime    [n][2][16*row_blocks][d] bf16   W' hi and lo planes (narrow gate only)
 struct Workspace {
     float *partial;
     bf16_t *act;
@@ -151,7 +155,7 @@ size_t workspace_layout(const FastShape &s, char *base, Workspace *w) {
     size_t o_par = take(sizeof(float) * s.N * s.n * s.ksplit * s.pstride);
     size_t o_act = take(sizeof(bf16_t) * s.N * 2 * s.rk);
     size_t o_rms = take(sizeof(float) * s.N * s.n);
-    size_t o_wp = take(sizeof(bf16_t) * (size_t)s.n * 2 * 16 * s.row_blocks * s.d);
+    size_t o_wp = take(s.wide ? 0 : sizeof(bf16_t) * (size_t)s.n * 2 * 16 * s.row_blocks * s.d);
     if (w) {
         w->partial = (float *)(base + o_par);
         w->act = (bf16_t *)(base + o_act);
@@ -477,6 +481,184 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     }
 }
 
+// Kernel 1, wide form (r + n > 128, bf16 state).  Same walk, load layout,
+// eq:write and records as k_stream_proj, but the contraction is arranged so
+// that the weights cost one LDS plane instead of two:
+//   P_i = W^{(i)} (gamma_i . R'_i),
+// with W^{(i)} the raw W_down / W_write columns of branch i (exact bf16, the
+// MFMA A operand, staged 32 channels at a time, double-buffered) and
+// gamma_i . R'_i -- exact in fp32, 16 significant bits -- carried as two bf16
+// words hi + lo in two wave-private LDS tiles (the B operand; the same split as
+// W' above, applied on the state side).  Every A fragment read from LDS then
+// feeds two MFMAs.  One workgroup per CU (the W chunks and B tiles take
+// ~123 KB of LDS); NRB * 4 accumulators per lane.
+template <bool FUSED, int NRB>
+__global__ void __launch_bounds__(kThreads, 2)
+k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
+                   const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
+                   const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
+                   FastShape sh) {
+    constexpr int NQ = 4;                              // load instructions per round (4 tokens each)
+    constexpr int RC = 128;                            // channels per round
+    constexpr int PCS = RC / 8;                        // 16-byte pieces per token row and round
+    constexpr int KW = kChunk;                         // channels per W chunk (one MFMA k-step)
+    constexpr int CPR = RC / KW;                       // W chunks per round
+    constexpr int kPitch = KW + 8;                     // bf16 per staged W row (odd number of 16-byte units)
+    constexpr int NV = NRB * 16 * (KW / 8);            // 16-byte vectors of W per chunk
+    constexpr int WV = (NV + kThreads - 1) / kThreads;
+    constexpr int RP = PCS + 1;                        // B tile pitch in pieces (odd: no bank conflicts)
+    __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][NRB * 16 * kPitch];
+    __shared__ __attribute__((aligned(16))) u32x4 lds_b[kWaves][2][16 * RP];   // hi, lo
+
+    const int n = sh.n, d = sh.d, S = sh.ksplit;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = (b / 8 / (n * S)) * 8 + (b % 8);
+    const int br = (int)((b / 8) % (n * S)) / S;
+    const int split = (int)((b / 8) % S);
+    if (tile >= sh.tiles) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, m16 = lane & 15;
+    const int64_t t0 = tile * kTile + wave * 16;        // first token of this wave
+    const int64_t nd = (int64_t)n * d;
+    const int chan = sh.ksplit_chan;                    // channels of this split (multiple of 64)
+    const int nit = chan / KW;                          // W chunks
+    const int nround = (chan + RC - 1) / RC;
+    const int c_base = split * chan;
+
+    // W staging: row j < r from W_down, r .. r+nw-1 from W_write, the rest zero
+    u32x4 wreg[WV];
+    auto load_w = [&](int it) {
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
+            const int row = v / (KW / 8), cv = v % (KW / 8);
+            const bf16_t *src = nullptr;
+            if (v < NV && it < nit) {
+                if (row < sh.r) src = wd + (int64_t)row * nd;
+                else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
+            }
+            wreg[q] = src ? *reinterpret_cast<const u32x4 *>(src + (int64_t)br * d + c_base + it * KW + cv * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_w = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < WV; ++q) {
+            const int v = tid + q * kThreads;
+            if (v < NV) {
+                const int row = v / (KW / 8), cv = v % (KW / 8);
+                *reinterpret_cast<u32x4 *>(&lds_w[buf][row * kPitch + cv * 8]) = wreg[q];
+            }
+        }
+    };
+
+    // load instruction q: token t0 + 4q + g, piece m16 (channels 8*m16 .. +7 of the round)
+    bool vq[NQ];
+    float sq[NQ], ss[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t t = t0 + 4 * q + g;
+        vq[q] = t < sh.N;
+        sq[q] = (FUSED && vq[q]) ? s_in[t * n + br] : 0.f;
+        ss[q] = 0.f;
+    }
+    bf16_t *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
+    const bf16_t *const ybase = FUSED ? y + t0 * (int64_t)d + c_base : nullptr;
+    const bf16_t *const gbase = gamma + (int64_t)br * d + c_base + 8 * m16;
+    const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
+    const int64_t qstride = 4 * nd, qystride = 4 * (int64_t)d;
+
+    u32x4 rr[NQ], yy[NQ];
+    auto load_state = [&](int rd) {
+        const bool in = rd < nround && rd * RC + 8 * m16 < chan;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            rr[q] = (vq[q] && in) ? *reinterpret_cast<const u32x4 *>(sbase + q * qstride + rd * RC + soff)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto load_y = [&](int rd) {
+        const bool in = rd < nround && rd * RC + 8 * m16 < chan;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            yy[q] = (FUSED && vq[q] && in) ? *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff)
+                                           : u32x4{0u, 0u, 0u, 0u};
+    };
+
+    f32x4 acc[NRB];
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 *my_hi = lds_b[wave][0], *my_lo = lds_b[wave][1];
+
+    load_w(0);
+    store_w(0);
+    load_w(1);
+    load_state(0);
+    __syncthreads();
+    for (int rd = 0; rd < nround; ++rd) {
+        load_y(rd);
+        const bool in = rd * RC + 8 * m16 < chan;
+        const u32x4 gm = in ? *reinterpret_cast<const u32x4 *>(gbase + rd * RC) : u32x4{0u, 0u, 0u, 0u};
+        // eq:write in the load layout: store, sum of squares, gamma . R' as hi / lo tiles
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            u32x4 w = rr[q];
+            if (FUSED) {
+                w = write8_bf16(sq[q], yy[q], rr[q]);
+                if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss[q] = dot2_bf16(w[e], w[e], ss[q]);
+            u32x4 hi, lo;
+            split_wprime(w, gm, hi, lo);
+            my_hi[(4 * q + g) * RP + m16] = hi;
+            my_lo[(4 * q + g) * RP + m16] = lo;
+        }
+        // the wave's LDS writes above complete before its reads below (LDS
+        // instructions of a wave execute in order); the next round's state
+        // loads go out now, their registers being free, and fly during the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        load_state(rd + 1);
+#pragma unroll
+        for (int h = 0; h < CPR; ++h) {
+            const int it = rd * CPR + h;
+            if (it < nit) {
+                const int cur = it & 1;
+                const int pc = h * (KW / 8) + g;             // piece of this lane group
+                const bf16x8 bh = as_bf16x8(my_hi[m16 * RP + pc]);
+                const bf16x8 bl = as_bf16x8(my_lo[m16 * RP + pc]);
+                const bf16_t *wp = &lds_w[cur][m16 * kPitch + 8 * g];
+#pragma unroll
+                for (int k = 0; k < NRB; ++k) {
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(wp + k * 16 * kPitch));
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[k], 0, 0, 0);
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[k], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (it + 1 < nit) store_w(cur ^ 1);
+                load_w(it + 2);
+                __syncthreads();
+            }
+        }
+    }
+
+    // the record (ss, P) of this (token, branch, split)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) ss[q] += __shfl_xor(ss[q], m, 64);
+        if (m16 == 0 && vq[q])
+            ws.partial[((t0 + 4 * q + g) * n + br) * S * (int64_t)sh.pstride + split * (int64_t)sh.pstride] = ss[q];
+    }
+    const int64_t t = t0 + m16;  // MFMA column of this lane
+    if (t < sh.N) {
+        float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
+    }
+}
+
 // Kernel 1b: combine the partial records written by k_stream_proj.  One wave
 // per token, four tokens per workgroup: lanes 0..NB-1 sum the squares over
 // the splits (rho_i, rms_i; shared by shuffles), then each lane owns outputs
@@ -726,11 +908,12 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 // that branch: the prefetch costs no registers beyond one step's state.  The
 // activations and rms of the next tile are loaded before the state of its
 // first step, so waiting for them never waits for that state.
-constexpr int kResStep = 64;   // channels per step (a 128-byte line of bf16)
-
 template <int RKS> struct ResidentCfg {
-    // channels per workgroup: keeps the staged W_up near 72 KiB (two per CU)
-    static constexpr int CH = RKS <= 2 ? 128 : 64;
+    // channels per workgroup: keeps the staged W_up near 72 KiB (two per CU);
+    // a wide gate (RKS > 4) gets 32 channels, ~84 KiB (one per CU)
+    static constexpr int CH = RKS <= 2 ? 128 : (RKS <= 4 ? 64 : 32);
+    // 32-channel chunks per step: two (one 128-byte line of bf16) when the range allows
+    static constexpr int SC = CH >= 64 ? 2 : 1;
 };
 
 #ifndef GR_K2R_WAVES
@@ -744,7 +927,7 @@ constexpr int kResThreads = 64 * kResWaves;
 constexpr int kResTile = 16 * kResWaves;         // tokens per tile
 constexpr int kResWgsTarget = 512;               // workgroups wanted (two per CU)
 
-template <int NB, int RKS, int CH>
+template <int NB, int RKS, int CH, int SC>
 __global__ void __launch_bounds__(kResThreads, RKS <= 2 ? GR_K2R_WAVES_PER_SIMD : 2)
 k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                         const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
@@ -761,6 +944,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
     const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
     if (p >= tiles) return;                            // whole workgroup
     const int c_begin = range * CH;
+    constexpr int kResStep = SC * kChunk;             // channels per step
     const int nchan = (d - c_begin) < CH ? (d - c_begin) : CH;
     const int nsteps = nchan / kResStep;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -784,19 +968,19 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
 #pragma unroll
         for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
     };
-    // state of branch i, step st of tile T: two 16-byte words per lane
-    auto load_state = [&](int64_t T, int st, int i, u32x4 (&sv)[2]) {
+    // state of branch i, step st of tile T: SC 16-byte words per lane
+    auto load_state = [&](int64_t T, int st, int i, u32x4 (&sv)[SC]) {
         const int64_t t = token(T);
         const bf16_t *q = state + t * (int64_t)NB * d + (int64_t)i * d + c_begin + st * kResStep + 8 * g;
         const bool ok = t < sh.N;
 #pragma unroll
-        for (int sc = 0; sc < 2; ++sc)
+        for (int sc = 0; sc < SC; ++sc)
             sv[sc] = ok ? *reinterpret_cast<const u32x4 *>(q + sc * kChunk) : u32x4{0u, 0u, 0u, 0u};
     };
 
     bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
     float rms[NB], nrms[NB];
-    u32x4 sv[NB][2];
+    u32x4 sv[NB][SC];
     int64_t T = p;
     int st = 0;
     load_act(T, bop, bopl, rms);
@@ -831,16 +1015,16 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
         const bool more = Tn < tiles;
         if (sn == 0 && more) load_act(Tn, nbop, nbopl, nrms);
 
-        float uacc[2][8];
+        float uacc[SC][8];
 #pragma unroll
-        for (int sc = 0; sc < 2; ++sc)
+        for (int sc = 0; sc < SC; ++sc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) uacc[sc][e] = 0.f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
 #pragma unroll
-            for (int sc = 0; sc < 2; ++sc) {
-                const int chunk = i * NC + st * 2 + sc;
+            for (int sc = 0; sc < SC; ++sc) {
+                const int chunk = i * NC + st * SC + sc;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     f32x4 tl = {0.f, 0.f, 0.f, 0.f};
@@ -852,7 +1036,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
                         tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
                     }
                     // tl[m] = -log2(e) * l for channel 8g + 4h + m of the chunk, branch i
-                    const uint32_t *gp = &lds_g[i * CH + (st * 2 + sc) * kChunk + 8 * g + 4 * h];
+                    const uint32_t *gp = &lds_g[i * CH + (st * SC + sc) * kChunk + 8 * g + 4 * h];
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const int e = 4 * h + m;
@@ -866,7 +1050,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
             // step's element work into the (token < N) store below and keeps
             // every MFMA result live at once.
 #pragma unroll
-            for (int sc = 0; sc < 2; ++sc)
+            for (int sc = 0; sc < SC; ++sc)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(uacc[sc][e]));
             // branch i of this step is consumed: fetch it for the next step
@@ -876,7 +1060,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
         if (t < sh.N) {
             bf16_t *q = u + t * (int64_t)d + c_begin + st * kResStep + 8 * g;
 #pragma unroll
-            for (int sc = 0; sc < 2; ++sc) {
+            for (int sc = 0; sc < SC; ++sc) {
                 u32x4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[sc][2 * e], uacc[sc][2 * e + 1]);
@@ -1069,6 +1253,22 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                                (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;
+    if (sh.wide) {
+        if (F8) return hipErrorInvalidValue;   // (an e4m3 state has the narrow gate only)
+#define GR_K1W(NRB)                                                                         \
+    case NRB:                                                                               \
+        hipLaunchKernelGGL((k_stream_proj_wide<FUSED, NRB>), dim3(grid), dim3(kThreads), 0, st, \
+                           (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,           \
+                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
+        break;
+        switch (sh.row_blocks) {
+            GR_K1W(9) GR_K1W(10) GR_K1W(11) GR_K1W(12) GR_K1W(13) GR_K1W(14) GR_K1W(15)
+            GR_K1W(16) GR_K1W(17) GR_K1W(18) GR_K1W(19) GR_K1W(20) GR_K1W(21)
+        default: return hipErrorInvalidValue;
+        }
+#undef GR_K1W
+        return hipGetLastError();
+    }
     switch (sh.row_blocks) {
         GR_K1(1) GR_K1(2) GR_K1(3) GR_K1(4) GR_K1(5) GR_K1(6) GR_K1(7) GR_K1(8)
     default: return hipErrorInvalidValue;
@@ -1104,7 +1304,7 @@ hipError_t launch_k2_resident_rks(const ReadArgs &a, const FastShape &sh, const 
     int64_t P = (kResWgsTarget + ranges / 2) / ranges;
     if (P > tiles) P = tiles;
     if (P < 1) P = 1;
-    hipLaunchKernelGGL((k_gate_combine_resident<NB, RKS, CH>), dim3((unsigned)(ranges * P)),
+    hipLaunchKernelGGL((k_gate_combine_resident<NB, RKS, CH, ResidentCfg<RKS>::SC>), dim3((unsigned)(ranges * P)),
                        dim3(kResThreads), 0, st, (const bf16_t *)a.state, (const bf16_t *)a.gamma,
                        (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges, (int)P);
     return hipGetLastError();
@@ -1145,6 +1345,12 @@ hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Work
     case 2: return launch_k2_resident_rks<NB, 2>(a, sh, w, st);
     case 3: return launch_k2_resident_rks<NB, 3>(a, sh, w, st);
     case 4: return launch_k2_resident_rks<NB, 4>(a, sh, w, st);
+    case 5: return launch_k2_resident_rks<NB, 5>(a, sh, w, st);
+    case 6: return launch_k2_resident_rks<NB, 6>(a, sh, w, st);
+    case 7: return launch_k2_resident_rks<NB, 7>(a, sh, w, st);
+    case 8: return launch_k2_resident_rks<NB, 8>(a, sh, w, st);
+    case 9: return launch_k2_resident_rks<NB, 9>(a, sh, w, st);
+    case 10: return launch_k2_resident_rks<NB, 10>(a, sh, w, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1157,10 +1363,13 @@ constexpr int64_t kResidentMinTokens = 4096;
 
 bool fast_path_ok(const ReadArgs &a) {
     if (!a.bf16 || a.n != 4) return false;
-    if (a.r < 16 || a.r % 16 || a.r > 128) return false;
+    if (a.r < 16 || a.r % 16 || a.r > 32 * kMaxWideRKS) return false;
     if (a.d % kIter) return false;
     const int rows = a.r + (a.ww ? a.n : 0);
-    return (rows + 15) / 16 <= kMaxRowBlocks;
+    const int nrb = (rows + 15) / 16;
+    if (nrb <= kMaxRowBlocks && a.r <= 128) return true;
+    // wide gate: bf16 state only
+    return !a.fp8 && nrb <= kMaxWideRowBlocks;
 }
 
 size_t fast_workspace_bytes(int64_t N, int n, int d, int r) {
@@ -1189,7 +1398,8 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // (an e4m3 state has the resident form only)
     if (a.fp8) return launch_k2_resident_fp8<4>(a, sh, w, st);
-    const bool resident = a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
+    // (a wide gate, more than four k-steps, has the resident form only)
+    const bool resident = sh.rk > 128 || a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
     return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }
 
