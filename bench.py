@@ -126,6 +126,19 @@ def roofline(alg_bytes, ms, kernel, traffic=None):
             "algorithmic_bytes_per_launch": alg_bytes}
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def mfma_roofline(flops, ms, kernel, traffic=None):
+    """Roofline of a contraction-heavy call: algorithmic flops (the gate's
+    down, up and write projections once each; the hi/lo operand split of the
+    kernels doubles the MFMA work actually issued) over the bf16 MFMA peak."""
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel,
+            "algorithmic_flops_per_launch": flops}
+
+
 def bench_other(which, args, dev):
     """Lines for the non-headline workloads."""
     import torch
@@ -173,8 +186,10 @@ def bench_other(which, args, dev):
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r,
                      "state_dtype": sdt, "activation_dtype": "bf16", "accumulation": "fp32"},
                     dtype="bf16", gate_tflops=gate_flops(N, n, d, r) / (ms * 1e-3) / 1e12,
-                    roofline=roofline(alg, ms, "gr_fused_write_read",
-                                      stored_traffic("gr_fused_write_read_" + ("fp8" if f8 else "r320"))))
+                    hbm_GBps_algorithmic=alg / (ms * 1e-3) / 1e9,
+                    roofline=(roofline(alg, ms, "gr_fused_write_read", stored_traffic("gr_fused_write_read_fp8"))
+                              if f8 else mfma_roofline(gate_flops(N, n, d, r), ms, "gr_fused_write_read",
+                                                       stored_traffic("gr_fused_write_read_r320"))))
     if which == "addnorm":
         W = inputs.WORKLOADS[2]
         A = inputs.workload(2)

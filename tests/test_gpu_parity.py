@@ -197,6 +197,20 @@ def test_wide_gate_shapes(N, d, r, w_std):
     run_read_write_fused(X, f"wide-N{N}-d{d}-r{r}")
 
 
+@pytest.mark.parametrize("N,d,r,w_std", [(4300, 256, 320, 0.2), (4200, 384, 192, 0.05)])
+@pytest.mark.parametrize("form", ["default", "resident"])
+def test_wide_gate_many_tokens(N, d, r, w_std, form, monkeypatch):
+    """Wide gates at 4096 tokens and more, every token compared: by default
+    kernel 2 walks XCD by XCD (token tiles T = x, x + 8, ... on XCD x, each
+    workgroup taking its share of (channel range, tile) units and restaging
+    W_up per range); "resident" forces the plain range-per-workgroup walk."""
+    if form == "resident":
+        monkeypatch.setenv("GR_KERNEL_VARIANT", "resident")
+    X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=17 * N + d + r, w_std=w_std,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"wide-{form}-N{N}-d{d}-r{r}")
+
+
 def test_wide_gate_without_write_projection():
     """r = 320 with no W_write: 320 projection rows (20 blocks), s == 1."""
     X = inputs.make_gr_inputs(100, 4, 1280, 320, "bf16", seed=43, with_write=False)

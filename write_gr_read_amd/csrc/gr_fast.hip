@@ -491,7 +491,9 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // words hi + lo in two wave-private LDS tiles (the B operand; the same split as
 // W' above, applied on the state side).  Every A fragment read from LDS then
 // feeds two MFMAs.  One workgroup per CU (the W chunks and B tiles take
-// ~123 KB of LDS); NRB * 4 accumulators per lane.
+// ~123 KB of LDS); NRB * 4 accumulators per lane, so two waves per SIMD: the
+// state / y words of the next two rounds are kept in flight (two register
+// slots, each refilled as soon as its round's element phase is done).
 template <bool FUSED, int NRB>
 __global__ void __launch_bounds__(kThreads, 2)
 k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
@@ -570,20 +572,18 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
     const int64_t qstride = 4 * nd, qystride = 4 * (int64_t)d;
 
-    u32x4 rr[NQ], yy[NQ];
-    auto load_state = [&](int rd) {
+    // two slots of state / y words: round rd uses slot rd % 2, and the loads
+    // of round rd + 2 go into that slot as soon as its element phase is done
+    u32x4 rrA[NQ], yyA[NQ], rrB[NQ], yyB[NQ];
+    auto load_round = [&](int rd, u32x4 (&rr)[NQ], u32x4 (&yy)[NQ]) {
         const bool in = rd < nround && rd * RC + 8 * m16 < chan;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
+        for (int q = 0; q < NQ; ++q) {
             rr[q] = (vq[q] && in) ? *reinterpret_cast<const u32x4 *>(sbase + q * qstride + rd * RC + soff)
                                   : u32x4{0u, 0u, 0u, 0u};
-    };
-    auto load_y = [&](int rd) {
-        const bool in = rd < nround && rd * RC + 8 * m16 < chan;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
             yy[q] = (FUSED && vq[q] && in) ? *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff)
                                            : u32x4{0u, 0u, 0u, 0u};
+        }
     };
 
     f32x4 acc[NRB];
@@ -591,13 +591,7 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 *my_hi = lds_b[wave][0], *my_lo = lds_b[wave][1];
 
-    load_w(0);
-    store_w(0);
-    load_w(1);
-    load_state(0);
-    __syncthreads();
-    for (int rd = 0; rd < nround; ++rd) {
-        load_y(rd);
+    auto do_round = [&](int rd, u32x4 (&rr)[NQ], u32x4 (&yy)[NQ]) {
         const bool in = rd * RC + 8 * m16 < chan;
         const u32x4 gm = in ? *reinterpret_cast<const u32x4 *>(gbase + rd * RC) : u32x4{0u, 0u, 0u, 0u};
         // eq:write in the load layout: store, sum of squares, gamma . R' as hi / lo tiles
@@ -615,11 +609,8 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
             my_hi[(4 * q + g) * RP + m16] = hi;
             my_lo[(4 * q + g) * RP + m16] = lo;
         }
-        // the wave's LDS writes above complete before its reads below (LDS
-        // instructions of a wave execute in order); the next round's state
-        // loads go out now, their registers being free, and fly during the MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        load_state(rd + 1);
+        load_round(rd + 2, rr, yy);
 #pragma unroll
         for (int h = 0; h < CPR; ++h) {
             const int it = rd * CPR + h;
@@ -641,6 +632,17 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
                 __syncthreads();
             }
         }
+    };
+
+    load_w(0);
+    store_w(0);
+    load_w(1);
+    load_round(0, rrA, yyA);
+    load_round(1, rrB, yyB);
+    __syncthreads();
+    for (int rd = 0; rd < nround; rd += 2) {
+        do_round(rd, rrA, yyA);
+        if (rd + 1 < nround) do_round(rd + 1, rrB, yyB);
     }
 
     // the record (ss, P) of this (token, branch, split)
@@ -1080,6 +1082,161 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 2, wide gate (more than four k-steps, r > 128), many tokens.  The
+// up projection's B operand -- -log2(e) a as hi / lo words, RKS * 8 VGPRs per
+// lane -- is the largest input of a (channel range, token tile) unit once r is
+// large, and every range reads it again.  So the walk is made XCD-aware: one
+// workgroup per CU, blockIdx % 8 taken as the XCD (round-robin dispatch), XCD
+// x taking the token tiles T = x, x + 8, ... and its workgroups splitting the
+// (range, tile) units of those tiles range by range.  The activations of an
+// XCD's tiles (a few MB) then stay in its L2 while all ranges pass over them.
+// A unit is one step of kernel 2's resident form at 32 channels per range,
+// i.e. half of each 128-byte line of a state row; so workgroups come in
+// pairs, 2m and 2m + 1 of an XCD taking ranges 2p and 2p + 1 of the same
+// tiles in the same order, and each line's second half is an L2 hit.  The
+// W_up rows of a range (NB * 32 rows, MFMA row order) are restaged in LDS
+// whenever a workgroup moves on to its next range.
+template <int NB, int RKS>
+__global__ void __launch_bounds__(kResThreads, 2)
+k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+                    const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
+                    FastShape sh, int ranges, int wgs_per_xcd) {
+    constexpr int CH = kChunk;                         // channels per range
+    constexpr int RK = RKS * 32;
+    constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
+    __shared__ __attribute__((aligned(16))) bf16_t lds_u[NB * CH * kPitch];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_g[NB * CH];
+
+    const int d = sh.d, r = sh.r;
+    const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+    const int pair = j >> 1, side = j & 1, pairs = wgs_per_xcd / 2;
+    const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
+    const int64_t ntx = tiles > xcd ? (tiles - xcd + 7) / 8 : 0;   // tiles xcd + 8k of this XCD
+    const int64_t units = (int64_t)(ranges / 2) * ntx;             // (range pair, tile) units
+    if (pair >= pairs) return;                         // whole workgroup (odd count: the last one idles)
+    const int64_t u0 = units * pair / pairs, u1 = units * (pair + 1) / pairs;
+    if (u0 >= u1) return;                              // whole workgroup
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, m16 = lane & 15;
+    const float inv_n = 1.0f / (float)NB;
+
+    auto unit_tile = [&](int64_t q) { return (int64_t)xcd + 8 * (q % ntx); };
+    auto unit_range = [&](int64_t q) { return 2 * (int)(q / ntx) + side; };
+    auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
+    auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
+        const int64_t t = token(T);
+        const bool ok = t < sh.N;
+#pragma unroll
+        for (int ks = 0; ks < RKS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+            if (ok) {
+                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
+                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
+            }
+            hi[ks] = as_bf16x8(v);
+            lo[ks] = as_bf16x8(vl);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+    };
+    // state of branch i, range rg of tile T: one 16-byte word per lane
+    auto load_state = [&](int64_t T, int rg, int i) {
+        const int64_t t = token(T);
+        if (t >= sh.N) return u32x4{0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4 *>(state + t * (int64_t)NB * d + (int64_t)i * d + rg * CH + 8 * g);
+    };
+    // W_up rows (branch i, channel cc of range rg) in MFMA row order, and gamma/n
+    auto stage = [&](int rg) {
+        const int c_begin = rg * CH;
+        for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
+            const int row = v / (RK / 8), kv = v % (RK / 8);
+            const int i = row / CH, cc = row % CH;
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (kv * 8 < r)
+                w = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8);
+            const int pos = i * CH + 16 * ((cc >> 2) & 1) + 4 * (cc >> 3) + (cc & 3);
+            *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w;
+        }
+        for (int v = tid; v < NB * CH; v += kResThreads) {
+            const int i = v / CH, cc = v % CH;
+            const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)i * d + c_begin + cc]) * inv_n);
+            lds_g[v] = (cc & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+        }
+    };
+
+    bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
+    float rms[NB], nrms[NB];
+    u32x4 sv[NB];
+    int64_t q = u0;
+    int64_t T = unit_tile(q);
+    int rg = unit_range(q);
+    load_act(T, bop, bopl, rms);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) sv[i] = load_state(T, rg, i);
+    stage(rg);
+    __syncthreads();
+
+    for (;;) {
+        const bool more = q + 1 < u1;
+        const int64_t Tn = more ? unit_tile(q + 1) : T;
+        const int rn = more ? unit_range(q + 1) : rg;
+        if (more) load_act(Tn, nbop, nbopl, nrms);
+
+        float uacc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 tl = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t *ap = &lds_u[(i * CH + 16 * h + m16) * kPitch + 8 * g];
+#pragma unroll
+                for (int ks = 0; ks < RKS; ++ks) {
+                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
+                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                }
+                // tl[m] = -log2(e) * l for channel 8g + 4h + m of the range, branch i
+                const uint32_t *gp = &lds_g[i * CH + 8 * g + 4 * h];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = 4 * h + m;
+                    const float bterm = dot2_bf16(sv[i][e >> 1], gp[m], 0.f);
+                    const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                    uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
+                }
+            }
+            // materialise per branch (else the element work sinks into the store's branch)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(uacc[e]));
+            // branch i of this unit is consumed: fetch it for the next unit
+            if (more) sv[i] = load_state(Tn, rn, i);
+        }
+        const int64_t t = token(T);
+        if (t < sh.N) {
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(uacc[2 * e], uacc[2 * e + 1]);
+            *reinterpret_cast<u32x4 *>(u + t * (int64_t)d + rg * CH + 8 * g) = o;
+        }
+        if (!more) break;
+        if (rn != rg) {  // next range: every wave is done with this one's rows
+            __syncthreads();
+            stage(rn);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int ks = 0; ks < RKS; ++ks) { bop[ks] = nbop[ks]; bopl[ks] = nbopl[ks]; }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rms[i] = nrms[i];
+        T = Tn;
+        rg = rn;
+        ++q;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2 for an e4m3 state, resident form.  Same walk as above, but a step
 // is one 64-channel unit: a 64-byte half line of the state per token and
 // branch, of which lane group g owns channels 16g .. 16g + 15 (one 16-byte
@@ -1337,6 +1494,42 @@ hipError_t launch_k2_resident_fp8(const ReadArgs &a, const FastShape &sh, const 
     }
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+template <int NB, int RKS>
+hipError_t launch_k2_wide_rks(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    const int ranges = sh.d / kChunk;                  // even: d is a multiple of 64
+    const int per_xcd = (cu_count() + 7) / 8;
+    hipLaunchKernelGGL((k_gate_combine_wide<NB, RKS>), dim3((unsigned)(8 * per_xcd)), dim3(kResThreads), 0, st,
+                       (const bf16_t *)a.state, (const bf16_t *)a.gamma, (const bf16_t *)a.wu,
+                       (bf16_t *)a.u, w, sh, ranges, per_xcd);
+    return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_k2_wide(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    switch (sh.rk / 32) {
+    case 5: return launch_k2_wide_rks<NB, 5>(a, sh, w, st);
+    case 6: return launch_k2_wide_rks<NB, 6>(a, sh, w, st);
+    case 7: return launch_k2_wide_rks<NB, 7>(a, sh, w, st);
+    case 8: return launch_k2_wide_rks<NB, 8>(a, sh, w, st);
+    case 9: return launch_k2_wide_rks<NB, 9>(a, sh, w, st);
+    case 10: return launch_k2_wide_rks<NB, 10>(a, sh, w, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int NB>
 hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                               hipStream_t st) {
@@ -1358,6 +1551,8 @@ hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Work
 // The resident kernel 2 pays a one-off W_up staging per workgroup; it wins
 // once every workgroup walks a few token tiles.
 constexpr int64_t kResidentMinTokens = 4096;
+// The XCD-aware walk of a wide gate's kernel 2 wants several tiles per XCD.
+constexpr int64_t kWideXcdMinTokens = 8 * 4 * kResTile;
 
 }  // namespace
 
@@ -1398,7 +1593,9 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // (an e4m3 state has the resident form only)
     if (a.fp8) return launch_k2_resident_fp8<4>(a, sh, w, st);
-    // (a wide gate, more than four k-steps, has the resident form only)
+    // a wide gate (more than four k-steps) has the resident form only, walked
+    // XCD by XCD once every XCD has several token tiles
+    if (sh.rk > 128 && sh.N >= kWideXcdMinTokens && a.k2_variant != 2) return launch_k2_wide<4>(a, sh, w, st);
     const bool resident = sh.rk > 128 || a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
     return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }
