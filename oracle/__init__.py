@@ -19,6 +19,14 @@ Every function follows a passage of the pages:
   chain                 -- the same page of the paper reading, sec. 4 (one GR
                            module around each sublayer) and sec. 6 (each branch
                            accumulates the writes, eq:rcv).
+  expand                -- the paper reading, sec. 6 (eq:rcv: branches start at
+                           the token embedding).
+  static_read,          -- the paper reading, sec. 1 (the AltUp-style widened
+  round_robin_write        stream: eq:input, eq:output).
+  write_per_channel     -- the architecture notes, sec. 3 (a per-channel write
+                           was tried); strengths a learned [n, d] parameter.
+  collapse              -- read-out after the last block: sum of the branches,
+                           then RMSNorm (a reading; the GR pages give none).
 """
 from __future__ import annotations
 
@@ -61,12 +69,18 @@ def _load():
         lib.gro_fused.argtypes = [I64, I, I, I, D, I, P, P, P, P, P, P, P, P, P]
         lib.gro_add_rmsnorm.argtypes = [I64, I, D, I, P, P, P, P]
         lib.gro_tanh_standin.argtypes = [I64, I, P, P]
+        lib.gro_expand.argtypes = [I64, I, I, I, P, P]
+        lib.gro_static_read.argtypes = [I64, I, I, I, P, P, P]
+        lib.gro_round_robin_write.argtypes = [I64, I, I, I, I, P, P]
+        lib.gro_write_per_channel.argtypes = [I64, I, I, I, P, P, P]
+        lib.gro_collapse.argtypes = [I64, I, I, D, I, P, P, P]
         lib.orc_round_bf16.argtypes = [D]
         lib.orc_round_bf16.restype = D
         lib.orc_round_e4m3.argtypes = [D]
         lib.orc_round_e4m3.restype = D
         for f in (lib.gro_read, lib.gro_write, lib.gro_fused, lib.gro_add_rmsnorm,
-                  lib.gro_tanh_standin):
+                  lib.gro_tanh_standin, lib.gro_expand, lib.gro_static_read,
+                  lib.gro_round_robin_write, lib.gro_write_per_channel, lib.gro_collapse):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -168,6 +182,56 @@ def tanh_standin(u, dtype: str = "bf16") -> np.ndarray:
     y = np.empty_like(u)
     _check(_load().gro_tanh_standin(u.size, _DT[dtype], _p(u), _p(y)), "tanh_standin")
     return y
+
+
+def expand(e, n: int, dtype: str = "bf16") -> np.ndarray:
+    """Every branch starts as the embedding e [N, d] (eq:rcv): returns [N, n, d]."""
+    e = _f64(e)
+    N, d = e.shape
+    R = np.empty((N, n, d))
+    _check(_load().gro_expand(N, n, d, _DT[dtype], _p(e), _p(R)), "expand")
+    return R
+
+
+def static_read(R, h, dtype: str = "bf16") -> np.ndarray:
+    """AltUp-style static read (eq:input): u = sum_i h_i R_i."""
+    R = _f64(R)
+    N, n, d = R.shape
+    h = _f64(h, (n,))
+    u = np.empty((N, d))
+    _check(_load().gro_static_read(N, n, d, _DT[dtype], _p(R), _p(h), _p(u)), "static_read")
+    return u
+
+
+def round_robin_write(R, y, layer: int, dtype: str = "bf16") -> np.ndarray:
+    """Round-robin write (eq:output): y added to branch layer mod n only."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    _check(_load().gro_round_robin_write(N, n, d, int(layer), _DT[dtype], _p(R), _p(y)),
+           "round_robin_write")
+    return R
+
+
+def write_per_channel(R, y, s, dtype: str = "bf16") -> np.ndarray:
+    """Per-channel write with a learned [n, d] strength: R'_ic = R_ic + s_ic y_c."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    s = _f64(s, (n, d))
+    _check(_load().gro_write_per_channel(N, n, d, _DT[dtype], _p(R), _p(y), _p(s)),
+           "write_per_channel")
+    return R
+
+
+def collapse(R, w, eps: float = 1e-6, dtype: str = "bf16") -> np.ndarray:
+    """Read-out of the widened stream: RMSNorm(sum_i R_i; w)."""
+    R = _f64(R)
+    N, n, d = R.shape
+    w = _f64(w, (d,))
+    out = np.empty((N, d))
+    _check(_load().gro_collapse(N, n, d, eps, _DT[dtype], _p(R), _p(w), _p(out)), "collapse")
+    return out
 
 
 def chain(X0, params: Sequence, eps: float = 1e-6, dtype: str = "bf16",

@@ -16,6 +16,8 @@
  *          the same equations restated with n_r = 4.
  *   [RES]  "Residual" (rainlin-net.pages.dev, LLM inference), section 2.2
  *          (Pre-Norm) and section 3.3 (fused residual add + RMSNorm).
+ *   [QFN sec. 1] the AltUp-style static read (eq:input) and round-robin write
+ *          (eq:output); [QFN sec. 6] eq:rcv (branches start at the embedding).
  *
  * Conventions adopted where the pages leave a point open:
  *   - RMSNorm(x; g)_c = g_c * x_c / sqrt(mean(x^2) + eps), eps inside the root;
@@ -235,6 +237,109 @@ int gro_add_rmsnorm(int64_t N, int d, double eps, int dtype, double *x,
         double inv = 1.0 / sqrt(ss / d + eps);
         for (int c = 0; c < d; ++c) out[t * d + c] = store_round(w[c] * h[c] * inv, dtype);
     }
+    return 0;
+}
+
+/*
+ * Variants on the same widened state (the f4 row of the hot-path table).
+ *
+ * Expand  [QFN sec. 6, eq:rcv: the initial value of every branch is the token
+ * embedding]: R[t][i][c] = e[t][c] for every branch i, stored in the state
+ * dtype.  e [N][d], R [N][n][d].
+ */
+int gro_expand(int64_t N, int n, int d, int dtype, const double *e, double *R)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    for (int64_t t = 0; t < N; ++t)
+        for (int i = 0; i < n; ++i)
+            for (int c = 0; c < d; ++c)
+                R[(t * n + i) * (int64_t)d + c] = store_state(e[t * d + c], dtype);
+    return 0;
+}
+
+/*
+ * Static read  [QFN sec. 1, eq:input: the AltUp-style block input is a
+ * weighted sum of the branches with n learned scalars]:
+ *   u[t][c] = sum_i h[i] R[t][i][c], stored in the dtype of u.
+ */
+int gro_static_read(int64_t N, int n, int d, int dtype, const double *R, const double *h,
+                    double *u)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    for (int64_t t = 0; t < N; ++t)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i) acc += h[i] * R[(t * n + i) * (int64_t)d + c];
+            u[t * d + c] = store_round(acc, dtype);
+        }
+    return 0;
+}
+
+/*
+ * Round-robin write  [QFN sec. 1, eq:output: the block output is added to one
+ * branch, chosen by depth in turn, the others unchanged]:
+ *   R[t][layer mod n][c] += y[t][c].
+ * The sum is rounded as eq:write's (through fp32, then the state dtype).
+ */
+int gro_round_robin_write(int64_t N, int n, int d, int layer, int dtype, double *R,
+                          const double *y)
+{
+    if (N < 0 || n < 1 || d < 1 || layer < 0) return -1;
+    const int i = layer % n;
+    for (int64_t t = 0; t < N; ++t)
+        for (int c = 0; c < d; ++c) {
+            double *p = R + (t * n + i) * (int64_t)d + c;
+            const double sum = *p + y[t * d + c];
+            *p = store_state(dtype == ORC_F64 ? sum : orc_round_f32(sum), dtype);
+        }
+    return 0;
+}
+
+/*
+ * Per-channel write  [NOTES sec. 3: a per-channel write was tried in place of
+ * the per-branch scalar]: the pages give no formula for predicting per-channel
+ * strengths, so they are a learned [n][d] parameter here:
+ *   R'[t][i][c] = R[t][i][c] + s[i][c] y[t][c],
+ * rounded as eq:write's.
+ */
+int gro_write_per_channel(int64_t N, int n, int d, int dtype, double *R, const double *y,
+                          const double *s)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    for (int64_t t = 0; t < N; ++t)
+        for (int i = 0; i < n; ++i)
+            for (int c = 0; c < d; ++c) {
+                double *p = R + (t * n + i) * (int64_t)d + c;
+                const double sum = *p + s[i * (int64_t)d + c] * y[t * d + c];
+                *p = store_state(dtype == ORC_F64 ? sum : orc_round_f32(sum), dtype);
+            }
+    return 0;
+}
+
+/*
+ * Collapse  (the pages describe no read-out of the widened stream after the
+ * last GR block; the nearest statement, for a four-stream residual, sums the
+ * streams and then applies RMSNorm): h = sum_i R_i (not stored), then
+ *   out[t][c] = w[c] h[c] / sqrt(mean_c h^2 + eps), stored in the dtype of u.
+ */
+int gro_collapse(int64_t N, int n, int d, double eps, int dtype, const double *R,
+                 const double *w, double *out)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    double *h = malloc(sizeof(double) * d);
+    if (!h) return -1;
+    for (int64_t t = 0; t < N; ++t) {
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i) acc += R[(t * n + i) * (int64_t)d + c];
+            h[c] = acc;
+            ss += acc * acc;
+        }
+        const double inv = 1.0 / sqrt(ss / d + eps);
+        for (int c = 0; c < d; ++c) out[t * d + c] = store_round(w[c] * h[c] * inv, dtype);
+    }
+    free(h);
     return 0;
 }
 

@@ -397,3 +397,84 @@ def test_scalar_brute_force(orc):
         G = sig(wu * z * sig(z))
         assert abs(u[0, 0] - G * rh) < 1e-15
         assert abs(s[0, 0] - 2 * sig(ww * rh)) < 1e-15
+
+
+# ---------------------------------------------------------------- variants on the same state
+# "Paper reading: Qwen3.8 Flash Next", part 2: sec. 1 (AltUp-style static read
+# eq:input, round-robin write eq:output), sec. 6 (eq:rcv: every branch starts at
+# the embedding); "... architecture notes, 06 Residual", sec. 3 (per-channel
+# write tried).  Collapse: sum of the branches, then RMSNorm (a reading).
+
+def _bf16(shape, std, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g, dtype=torch.float64) * std).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_expand_copies_the_embedding_into_every_branch(orc, dtype):
+    e = _bf16((9, 48), 1.5, 1)
+    R = orc.expand(e, 4, dtype)
+    want = e.double() if dtype == "bf16" else e.float().clamp(-448, 448).to(torch.float8_e4m3fn).double()
+    for i in range(4):
+        np.testing.assert_array_equal(R[:, i, :], want.numpy())
+    # then a unit-gate read of identical branches (gains 1) is RMSNorm(e)
+    gamma = np.ones((4, 48))
+    u, s = orc.read(R, gamma, None, None, None, 1e-6, "f64")
+    np.testing.assert_allclose(u, rmsnorm_lib(R[:, 0, :], np.ones(48), 1e-6), rtol=1e-13)
+    assert np.all(s == 1.0)
+
+
+def test_static_read_closed_forms(orc):
+    R = _bf16((11, 4, 40), 1.0, 2).double()
+    for k in range(4):   # a one-hot h picks one branch exactly
+        h = np.eye(4)[k]
+        np.testing.assert_array_equal(orc.static_read(R, h, "bf16"), R[:, k, :].numpy())
+    # the branch mean, stored as bf16: torch's mean in fp64, rounded to nearest even
+    u = orc.static_read(R, np.full(4, 0.25), "bf16")
+    np.testing.assert_array_equal(u, R.mean(dim=1).to(torch.bfloat16).double().numpy())
+    # linear in h, exactly, before the store
+    h1, h2 = np.array([0.5, -1.0, 2.0, 0.25]), np.array([1.0, 0.5, -0.75, 3.0])
+    a = orc.static_read(R, h1, "f64") + orc.static_read(R, h2, "f64")
+    np.testing.assert_allclose(orc.static_read(R, h1 + h2, "f64"), a, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 5, 11])
+def test_round_robin_write_touches_one_branch(orc, layer):
+    R = _bf16((7, 4, 32), 1.0, 3)
+    y = _bf16((7, 32), 0.3, 4)
+    R2 = orc.round_robin_write(R, y, layer, "bf16")
+    k = layer % 4
+    for i in range(4):
+        if i == k:   # fp32 add, then bf16 round to nearest even (torch's casts)
+            want = (R[:, i, :].float() + y.float()).to(torch.bfloat16).double().numpy()
+        else:
+            want = R[:, i, :].double().numpy()
+        np.testing.assert_array_equal(R2[:, i, :], want)
+
+
+def test_per_channel_write_closed_forms(orc):
+    R = _bf16((6, 4, 24), 1.0, 5)
+    y = _bf16((6, 24), 0.2, 6)
+    s = torch.rand(4, 24, generator=torch.Generator().manual_seed(7), dtype=torch.float64).float() * 2
+    got = orc.write_per_channel(R, y, s, "bf16")
+    # exact product and sum in fp64, rounded to fp32 then bf16 (torch's casts)
+    exact = R.double() + s.double()[None] * y.double()[:, None, :]
+    np.testing.assert_array_equal(got, exact.float().to(torch.bfloat16).double().numpy())
+    # strengths constant along channels are the per-branch scalar write
+    sb = torch.tensor([0.5, 1.25, 2.0, 0.0]).float()
+    got2 = orc.write_per_channel(R, y, sb[:, None].expand(4, 24), "bf16")
+    np.testing.assert_array_equal(got2, orc.write(R, y, sb[None].expand(6, 4), "bf16"))
+
+
+def test_collapse_closed_forms(orc):
+    w = (1 + 0.05 * torch.randn(40, generator=torch.Generator().manual_seed(8), dtype=torch.float64)).numpy()
+    R = _bf16((5, 1, 40), 1.0, 9).double().numpy()
+    # one branch: the library RMSNorm
+    np.testing.assert_allclose(orc.collapse(R, w, 1e-6, "f64"), rmsnorm_lib(R[:, 0, :], w, 1e-6), rtol=1e-13)
+    # four branches: RMSNorm of their sum
+    R4 = _bf16((5, 4, 40), 1.0, 10).double().numpy()
+    np.testing.assert_allclose(orc.collapse(R4, w, 1e-6, "f64"), rmsnorm_lib(R4.sum(axis=1), w, 1e-6), rtol=1e-13)
+    # expand then collapse is RMSNorm(e) when eps = 0 (scale invariance: sum = n e)
+    e = _bf16((5, 40), 0.7, 11)
+    out = orc.collapse(orc.expand(e, 4, "bf16"), w, 0.0, "f64")
+    np.testing.assert_allclose(out, rmsnorm_lib(e.double().numpy(), w, 0.0), rtol=1e-13)
