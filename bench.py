@@ -9,10 +9,12 @@ step of the hot path.  Inputs are seeded synthetic tensors already resident in
 HBM.  Prints one JSON line on stdout; progress goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload {prefill,prefill_fp8,prefill_r320,decode,addnorm,chain,tiny,all}
+       python bench.py --workload {prefill,prefill_fp8,prefill_r320,decode,addnorm,chain,tiny,variants,all}
 The default (prefill) line is the headline; the other workloads print their own
 line (prefill_fp8: the same shape with an e4m3 branch state; prefill_r320: the
-pages' model shape d = 2560 with gate rank r = d/8 = 320; decode: us per
+pages' model shape d = 2560 with gate rank r = d/8 = 320; variants: expand,
+static read, round-robin write, per-channel write and collapse at the prefill
+shape, one line each; decode: us per
 call with the state warm in cache, back to back; addnorm:
 the n = 1 fused residual add + RMSNorm; chain: 32 sublayers of read -> F ->
 fused write+read -> ... -> write with the elementwise F stand-in).
@@ -190,6 +192,33 @@ def bench_other(which, args, dev):
                     roofline=(roofline(alg, ms, "gr_fused_write_read", stored_traffic("gr_fused_write_read_fp8"))
                               if f8 else mfma_roofline(gate_flops(N, n, d, r), ms, "gr_fused_write_read",
                                                        stored_traffic("gr_fused_write_read_r320"))))
+    if which == "variants":
+        # the variants on the widened state at the prefill shape, bf16: one line each
+        N, n, d = 16384, 4, 4096
+        V = inputs.make_variant_inputs(N, n, d, "bf16", seed=8000, branch_scale=(1.0, 0.5, 2.0, 1.0))
+        X, e, y = V.X.to(dev), V.e.to(dev), V.y.to(dev)
+        h, sc, w = V.h.to(dev), V.s.to(dev), V.w.to(dev)
+        u = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+        st = torch.empty_like(X)
+        steps = args.steps if args.steps_given else 50
+        ops = {
+            "expand": (lambda: gr.expand(e, n, state=st), N * d * 2 + N * n * d * 2),
+            "static_read": (lambda: gr.static_read(X, h, u=u), N * n * d * 2 + N * d * 2),
+            "round_robin_write": (lambda: gr.round_robin_write(X, y, 1), 3 * N * d * 2),
+            "write_per_channel": (lambda: gr.write_per_channel(X, y, sc),
+                                  2 * N * n * d * 2 + N * d * 2 + n * d * 4),
+            "collapse": (lambda: gr.collapse(X, w, out=u), N * n * d * 2 + N * d * 2 + d * 2),
+        }
+        lines = []
+        for name, (fn, alg) in ops.items():
+            ms = timed(fn, steps, args.warmup, stream)
+            log(f"{name}: {ms * 1e3:.1f} us/call, {alg / (ms * 1e-3) / 1e9:.0f} GB/s")
+            lines.append(line(f"GR variant {name} tokens/s (N={N}, d={d}, n={n}, bf16 state)",
+                              N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
+                              {"workload": f"variant_{name}", "N": N, "d": d, "n": n,
+                               "state_dtype": "bf16"},
+                              roofline=roofline(alg, ms, f"gr_{name}")))
+        return lines
     if which == "addnorm":
         W = inputs.WORKLOADS[2]
         A = inputs.workload(2)
@@ -257,7 +286,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny",
-                             "all"])
+                             "variants", "all"])
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
 
@@ -273,10 +302,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload != "prefill":
-        names = (["prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny"] if args.workload == "all"
-                 else [args.workload])
+        names = (["prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny", "variants"]
+                 if args.workload == "all" else [args.workload])
         for w in names:
-            print(json.dumps(bench_other(w, args, dev)), flush=True)
+            res = bench_other(w, args, dev)
+            for one in (res if isinstance(res, list) else [res]):
+                print(json.dumps(one), flush=True)
         if args.workload != "all":
             return
     W = inputs.WORKLOADS[3]

@@ -132,6 +132,60 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
 gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps, void *out,
                                gr_dtype dt, int64_t N, int32_t d, void *stream);
 
+/*
+ * Variants on the same widened state.  Same conventions as above; "act dtype"
+ * is the state dtype, or bf16 with GR_FP8_E4M3.  Sums and products in fp32,
+ * one store rounded to nearest even (an fp8 state saturating at +-448).
+ *
+ * gr_expand -- the stream's start ("Paper reading: Qwen3.8 Flash Next",
+ * part 2 Residual, sec. 6, eq:rcv: every branch's initial value is the token
+ * embedding): state[t][i][c] = e[t][c] for every branch i.
+ *   e in [N][d] (act dtype);  state out [N][n][d]
+ */
+gr_status gr_expand(const void *e, void *state, gr_dtype dt, int64_t N, int32_t n, int32_t d,
+                    void *stream);
+
+/*
+ * gr_static_read -- the AltUp-style read of the widened stream (same page,
+ * sec. 1, eq:input): u[t][c] = sum_i h[i] state[t][i][c], with n learned
+ * scalars h (no normalisation).
+ *   state in [N][n][d];  h in [n] fp32 (device);  u out [N][d] (act dtype)
+ */
+gr_status gr_static_read(const void *state, const float *h, void *u, gr_dtype dt, int64_t N,
+                         int32_t n, int32_t d, void *stream);
+
+/*
+ * gr_round_robin_write -- the AltUp-style write (same page, sec. 1,
+ * eq:output): the block output is added to the one branch layer mod n, in
+ * place, the other branches untouched: state[t][layer % n][c] += y[t][c]
+ * (one fp32 add, then the store).  layer >= 0.
+ *   state in/out [N][n][d];  y in [N][d] (act dtype)
+ */
+gr_status gr_round_robin_write(void *state, const void *y, int32_t layer, gr_dtype dt, int64_t N,
+                               int32_t n, int32_t d, void *stream);
+
+/*
+ * gr_write_per_channel -- eq:write with per-channel strengths ("Qwen3.8-
+ * Flash-Next architecture notes, 06 Residual", sec. 3: a per-channel write
+ * was tried in place of the per-branch scalar).  The pages give no formula
+ * for predicting per-channel strengths; here they are a learned [n][d]
+ * parameter: state[t][i][c] += s[i][c] * y[t][c] (one fp32 FMA, then the
+ * store), in place.
+ *   state in/out [N][n][d];  y in [N][d] (act dtype);  s in [n][d] fp32
+ */
+gr_status gr_write_per_channel(void *state, const void *y, const float *s, gr_dtype dt, int64_t N,
+                               int32_t n, int32_t d, void *stream);
+
+/*
+ * gr_collapse -- read-out of the widened stream after the last block: the
+ * branches summed in fp32 (h, not stored), then out = w (.) h /
+ * sqrt(mean(h^2) + eps).  (The GR pages describe no read-out; the sum-then-
+ * RMSNorm form is the one given for another four-stream residual.)
+ *   state in [N][n][d];  w in [d] (act dtype);  out out [N][d] (act dtype)
+ */
+gr_status gr_collapse(const void *state, const void *w, float eps, void *out, gr_dtype dt, int64_t N,
+                      int32_t n, int32_t d, void *stream);
+
 /* Bytes of workspace `op` needs for N tokens of layer L (may be 0).
  * The workspace needs no initialisation: a call writes every byte it reads.
  * Calls that share a workspace must not run concurrently (same stream, or

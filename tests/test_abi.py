@@ -146,3 +146,26 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gr.residual_add_rmsnorm(x, x.clone(), torch.ones(64, dtype=torch.bfloat16))
+
+
+def test_variant_calls_reject_bad_arguments(L):
+    """expand / static read / round-robin write / per-channel write / collapse:
+    host-side checks only (no launch)."""
+    for dt in (0, 1, 2):
+        assert L.gr_expand(None, None, dt, 0, 4, 64, None) == 0          # N = 0
+    assert L.gr_expand(FAKE, FAKE, 1, 4, 0, 64, None) == INVALID          # n < 1
+    assert L.gr_expand(FAKE, FAKE, 1, 4, 9, 64, None) == INVALID          # n > 8
+    assert L.gr_expand(FAKE, FAKE, 1, 4, 4, 60, None) == NOT_SUPPORTED    # d % 8
+    assert L.gr_expand(FAKE, FAKE, 2, 4, 4, 40, None) == NOT_SUPPORTED    # fp8: d % 16
+    assert L.gr_expand(FAKE, FAKE, 7, 4, 4, 64, None) == INVALID          # dtype
+    assert L.gr_expand(None, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_static_read(FAKE, MISALIGNED, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_static_read(FAKE, FAKE, None, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_round_robin_write(FAKE, FAKE, -1, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_round_robin_write(FAKE, None, 3, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_write_per_channel(FAKE, FAKE, None, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_write_per_channel(FAKE, FAKE, FAKE, 0, 4, 4, 62, None) == NOT_SUPPORTED
+    assert L.gr_collapse(FAKE, FAKE, -1.0, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_collapse(FAKE, FAKE, float("nan"), FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_collapse(FAKE, None, 1e-6, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_last_error() != b""

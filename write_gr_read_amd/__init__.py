@@ -70,6 +70,11 @@ def lib():
         L.residual_add_rmsnorm.argtypes = [P, P, P, F, P, ctypes.c_int, I64, I32, P]
         L.gr_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, I64, LP,
                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.gr_expand.argtypes = [P, P, ctypes.c_int, I64, I32, I32, P]
+        L.gr_static_read.argtypes = [P, P, P, ctypes.c_int, I64, I32, I32, P]
+        L.gr_round_robin_write.argtypes = [P, P, I32, ctypes.c_int, I64, I32, I32, P]
+        L.gr_write_per_channel.argtypes = [P, P, P, ctypes.c_int, I64, I32, I32, P]
+        L.gr_collapse.argtypes = [P, P, F, P, ctypes.c_int, I64, I32, I32, P]
         L.gr_bench_tanh_standin.argtypes = [P, P, ctypes.c_int, I64, P]
         L.gr_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
         L.gr_status_string.argtypes = [ctypes.c_int]
@@ -77,7 +82,8 @@ def lib():
         L.gr_last_error.argtypes = []
         L.gr_last_error.restype = ctypes.c_char_p
         for f in ("gr_read", "gr_write", "gr_fused_write_read", "residual_add_rmsnorm",
-                  "gr_workspace_size", "gr_bench_tanh_standin", "gr_bench_copy"):
+                  "gr_workspace_size", "gr_bench_tanh_standin", "gr_bench_copy", "gr_expand",
+                  "gr_static_read", "gr_round_robin_write", "gr_write_per_channel", "gr_collapse"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,6 +243,73 @@ def residual_add_rmsnorm(x: torch.Tensor, y: torch.Tensor, w: torch.Tensor, eps:
     out = torch.empty_like(x) if out is None else out
     op = _dev(out, "out", (N, d), dt, dev)
     _call("residual_add_rmsnorm", xp, yp, wp, float(eps), op, _dt(x), N, d, _stream(dev))
+    return out
+
+
+# ------------------------------------------------------------------ variants
+def expand(e: torch.Tensor, n: int, dtype: Optional[torch.dtype] = None,
+           state: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Every branch starts at the embedding: returns state [N, n, d] with
+    state[:, i] = e for all i.  ``dtype`` is the state dtype (default e's;
+    torch.float8_e4m3fn takes a bf16 e)."""
+    N, d = e.shape
+    dev = e.device
+    dtype = e.dtype if dtype is None else dtype
+    if state is None:
+        state = torch.empty((N, n, d), dtype=dtype, device=dev)
+    sp = _dev(state, "state", (N, n, d), dtype, dev)
+    ep = _dev(e, "e", (N, d), _pdt(state), dev)
+    _call("gr_expand", ep, sp, _dt(state), N, n, d, _stream(dev))
+    return state
+
+
+def static_read(state: torch.Tensor, h: torch.Tensor, u: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """AltUp-style static read: u = sum_i h[i] * state[:, i] (h: n fp32 values)."""
+    N, n, d = state.shape
+    dev = state.device
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    hp = _dev(h, "h", (n,), torch.float32, dev)
+    u = torch.empty((N, d), dtype=_pdt(state), device=dev) if u is None else u
+    up = _dev(u, "u", (N, d), _pdt(state), dev)
+    _call("gr_static_read", sp, hp, up, _dt(state), N, n, d, _stream(dev))
+    return u
+
+
+def round_robin_write(state: torch.Tensor, y: torch.Tensor, layer: int) -> torch.Tensor:
+    """AltUp-style write, in place: state[:, layer % n] += y.  Returns state."""
+    N, n, d = state.shape
+    dev = state.device
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    yp = _dev(y, "y", (N, d), _pdt(state), dev)
+    _call("gr_round_robin_write", sp, yp, int(layer), _dt(state), N, n, d, _stream(dev))
+    return state
+
+
+def write_per_channel(state: torch.Tensor, y: torch.Tensor, s: torch.Tensor) -> torch.Tensor:
+    """Per-channel write, in place: state[t, i, c] += s[i, c] * y[t, c] (s: [n, d] fp32)."""
+    N, n, d = state.shape
+    dev = state.device
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    yp = _dev(y, "y", (N, d), _pdt(state), dev)
+    s_p = _dev(s, "s", (n, d), torch.float32, dev)
+    _call("gr_write_per_channel", sp, yp, s_p, _dt(state), N, n, d, _stream(dev))
+    return state
+
+
+def collapse(state: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read-out after the last block: RMSNorm(sum_i state[:, i]; w)."""
+    N, n, d = state.shape
+    dev = state.device
+    _dt(state)
+    sp = _dev(state, "state", (N, n, d), state.dtype, None)
+    wp = _dev(w, "w", (d,), _pdt(state), dev)
+    out = torch.empty((N, d), dtype=_pdt(state), device=dev) if out is None else out
+    op = _dev(out, "out", (N, d), _pdt(state), dev)
+    _call("gr_collapse", sp, wp, float(eps), op, _dt(state), N, n, d, _stream(dev))
     return out
 
 

@@ -140,6 +140,16 @@ void fill_layer(grk::ReadArgs &a, const gr_layer *L) {
     a.gamma = L->gamma; a.wd = L->w_down; a.wu = L->w_up; a.ww = L->w_write;
 }
 
+// Shared checks of the variant calls: dtype, N, n, d; 0 fp32, 1 bf16, 2 fp8 state.
+gr_status check_variant(gr_dtype dt, int64_t N, int32_t n, int32_t d, const char *fn, int *code) {
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (n < 1 || n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, n);
+    if ((st = check_width(dt, d, fn))) return st;
+    *code = dt == GR_F32 ? 0 : dt == GR_BF16 ? 1 : 2;
+    return GR_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +229,72 @@ gr_status residual_add_rmsnorm(void *x, const void *y, const void *w, float eps,
     if (out == x) return fail(GR_ERROR_INVALID_VALUE, "%s: out must not alias x", fn);
     (void)hipGetLastError();
     return launched(grk::launch_add_rmsnorm(x, y, w, eps, out, dt == GR_BF16, N, d, (hipStream_t)stream), fn);
+}
+
+gr_status gr_expand(const void *e, void *state, gr_dtype dt, int64_t N, int32_t n, int32_t d,
+                    void *stream) {
+    const char *fn = "gr_expand";
+    gr_status st;
+    int code = 0;
+    if ((st = check_variant(dt, N, n, d, fn, &code))) return st;
+    if (N == 0) return ok();
+    if ((st = check_ptr(e, "e", fn)) || (st = check_ptr(state, "state", fn))) return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_expand(e, state, code, N, n, d, (hipStream_t)stream), fn);
+}
+
+gr_status gr_static_read(const void *state, const float *h, void *u, gr_dtype dt, int64_t N,
+                         int32_t n, int32_t d, void *stream) {
+    const char *fn = "gr_static_read";
+    gr_status st;
+    int code = 0;
+    if ((st = check_variant(dt, N, n, d, fn, &code))) return st;
+    if (N == 0) return ok();
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(h, "h", fn)) || (st = check_ptr(u, "u", fn)))
+        return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_static_read(state, h, u, code, N, n, d, (hipStream_t)stream), fn);
+}
+
+gr_status gr_round_robin_write(void *state, const void *y, int32_t layer, gr_dtype dt, int64_t N,
+                               int32_t n, int32_t d, void *stream) {
+    const char *fn = "gr_round_robin_write";
+    gr_status st;
+    int code = 0;
+    if ((st = check_variant(dt, N, n, d, fn, &code))) return st;
+    if (layer < 0) return fail(GR_ERROR_INVALID_VALUE, "%s: layer = %d is negative", fn, layer);
+    if (N == 0) return ok();
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn))) return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_round_robin_write(state, y, code, N, n, d, layer, (hipStream_t)stream), fn);
+}
+
+gr_status gr_write_per_channel(void *state, const void *y, const float *s, gr_dtype dt, int64_t N,
+                               int32_t n, int32_t d, void *stream) {
+    const char *fn = "gr_write_per_channel";
+    gr_status st;
+    int code = 0;
+    if ((st = check_variant(dt, N, n, d, fn, &code))) return st;
+    if (N == 0) return ok();
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) || (st = check_ptr(s, "s", fn)))
+        return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_write_per_channel(state, y, s, code, N, n, d, (hipStream_t)stream), fn);
+}
+
+gr_status gr_collapse(const void *state, const void *w, float eps, void *out, gr_dtype dt, int64_t N,
+                      int32_t n, int32_t d, void *stream) {
+    const char *fn = "gr_collapse";
+    gr_status st;
+    int code = 0;
+    if ((st = check_variant(dt, N, n, d, fn, &code))) return st;
+    if (!(eps >= 0.f) || !isfinite(eps))
+        return fail(GR_ERROR_INVALID_VALUE, "%s: eps must be finite and >= 0", fn);
+    if (N == 0) return ok();
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(w, "w", fn)) || (st = check_ptr(out, "out", fn)))
+        return st;
+    (void)hipGetLastError();
+    return launched(grk::launch_collapse(state, w, eps, out, code, N, n, d, (hipStream_t)stream), fn);
 }
 
 gr_status gr_workspace_size(int op, gr_dtype dt, int64_t N, const gr_layer *L, size_t *bytes) {

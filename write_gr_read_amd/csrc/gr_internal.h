@@ -34,6 +34,18 @@ hipError_t launch_add_rmsnorm(void *x, const void *y, const void *w, float eps, 
 hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count, hipStream_t st);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t st);
 
+// Variants on the widened state (gr_variants.hip); dt: 0 fp32, 1 bf16,
+// 2 e4m3 state with bf16 activations.
+hipError_t launch_expand(const void *e, void *state, int dt, int64_t N, int n, int d, hipStream_t st);
+hipError_t launch_static_read(const void *state, const float *h, void *u, int dt, int64_t N, int n, int d,
+                              hipStream_t st);
+hipError_t launch_round_robin_write(void *state, const void *y, int dt, int64_t N, int n, int d, int layer,
+                                    hipStream_t st);
+hipError_t launch_write_per_channel(void *state, const void *y, const float *s, int dt, int64_t N, int n, int d,
+                                    hipStream_t st);
+hipError_t launch_collapse(const void *state, const void *w, float eps, void *out, int dt, int64_t N, int n,
+                           int d, hipStream_t st);
+
 // MFMA fast path for the bf16 widened state (gr_fast.hip).
 bool fast_path_ok(const ReadArgs &a);
 size_t fast_workspace_bytes(int64_t N, int n, int d, int r);

@@ -173,6 +173,40 @@ def make_addnorm_inputs(N: int, d: int, dtype: str = "bf16", seed: int = 0,
     return AddNormInputs(N, d, dtype, eps, x, y, w)
 
 
+@dataclass
+class VariantInputs:
+    """Inputs of the variants on the widened state (expand, static read,
+    round-robin write, per-channel write, collapse)."""
+    N: int
+    n: int
+    d: int
+    dtype: str               # state dtype
+    X: torch.Tensor          # [N, n, d] state
+    e: torch.Tensor          # [N, d]    embedding (activation dtype)
+    y: torch.Tensor          # [N, d]    sublayer output (activation dtype)
+    h: torch.Tensor          # [n]       static read weights, fp32
+    s: torch.Tensor          # [n, d]    per-channel write strengths, fp32
+    w: torch.Tensor          # [d]       collapse RMSNorm gain (activation dtype)
+
+
+def make_variant_inputs(N: int, n: int, d: int, dtype: str = "bf16", seed: int = 0,
+                        x_std: float = 1.0, y_std: float = 0.05,
+                        branch_scale: Optional[Sequence[float]] = None) -> VariantInputs:
+    """Seeded inputs of the variants: X ~ N(0, x_std^2) (per-branch scales
+    optional), e ~ N(0, 1), y ~ N(0, y_std^2), h ~ N(1/n, (0.5/n)^2) and
+    s ~ N(1, 0.25^2) in fp32, w = 1 + N(0, 0.01^2)."""
+    children = np.random.SeedSequence(seed).spawn(6)
+    rngs = [np.random.Generator(np.random.PCG64(c)) for c in children]
+    pdt = param_dtype(dtype)
+    X = normal(rngs[0], (N, n, d), x_std, dtype=dtype, scale_rows=branch_scale)
+    e = normal(rngs[1], (N, d), 1.0, dtype=pdt)
+    y = normal(rngs[2], (N, d), y_std, dtype=pdt)
+    h = normal(rngs[3], (n,), 0.5 / n, mean=1.0 / n, dtype="f32")
+    s = normal(rngs[4], (n, d), 0.25, mean=1.0, dtype="f32")
+    w = normal(rngs[5], (d,), 0.01, mean=1.0, dtype=pdt)
+    return VariantInputs(N, n, d, dtype, X, e, y, h, s, w)
+
+
 # The synthetic workloads, by number. Seed of workload k is 1000*k.
 WORKLOADS = {
     1: dict(name="gr_tiny_f32", kind="gr", N=64, n=4, d=256, r=16, dtype="f32",
