@@ -1,10 +1,15 @@
 // gr_fast.hip -- MFMA fast path of the GR read / fused write+read for a bf16
-// widened state ("Paper reading: Qwen3.8 Flash Next", part 2 Residual,
-// sec. 4 Gated Residual: eq:rms, eq:gate, eq:use_gate, eq:s; eq:write first
-// when fused; sec. 7: read fused into one traversal with Group RMSNorm).
+// or e4m3 widened state ("Paper reading: Qwen3.8 Flash Next", part 2
+// Residual, sec. 4 Gated Residual: eq:rms, eq:gate, eq:use_gate, eq:s;
+// eq:write first when fused; sec. 7: read fused into one traversal with Group
+// RMSNorm, and the FP8 state).
 //
 // Four kernels in stream order, no inter-workgroup waiting (so no
-// co-residency assumption):
+// co-residency assumption).  Below, the narrow-gate (r + n <= 128) forms;
+// an e4m3 state uses the same kernel 1 template and its own kernel 2
+// (k_gate_combine_resident_fp8), and a wide gate (r up to 320, the pages'
+// r = d/8 at d = 2560) has its own kernel 1 and 2 (k_stream_proj_wide,
+// k_gate_combine_wide), each described where it is defined.
 //
 // k_prep_wprime   (many tokens) W' = (W_down ; W_write) . gamma per branch,
 //                 split once into bf16 hi / lo planes for the whole call.
