@@ -119,6 +119,45 @@ def timed(fn, steps, warmup, stream):
     return a.elapsed_time(b) / steps
 
 
+def per_call_ms(fn, reps, stream, between=None):
+    """Duration of each of ``reps`` calls (HIP events around every call, on
+    the call's stream); ``between`` runs untimed before each call."""
+    import torch
+    evs = []
+    for _ in range(reps):
+        if between is not None:
+            between()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def percentiles(ms_list):
+    import numpy as np
+    q = np.percentile(np.asarray(ms_list), [10, 50, 90])
+    return {"ms_p10": float(q[0]), "ms_p50": float(q[1]), "ms_p90": float(q[2])}
+
+
+def graph_replay_ms(fn, steps, warmup, stream):
+    """Average ms of ``fn`` captured once in a HIP graph and replayed."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()                      # eager calls on the capture stream first (workspace)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        fn()
+    return timed(graph.replay, steps, warmup, stream)
+
+
 def line(metric, value, unit, steps, warmup, ms, config, dtype="bf16", higher=True, **extra):
     out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps,
            "warmup": warmup, "ms_per_step": ms, "higher_is_better": higher, "scaling": "weak",
@@ -164,15 +203,27 @@ def bench_other(which, args, dev):
         so = torch.empty((N, n), dtype=torch.float32, device=dev)
         _, s_in = gr.read(X, p0)
         steps = args.steps if args.steps_given else 2000
-        ms = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so), steps, args.warmup, stream)
+        call = lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so)
+        ms = timed(call, steps, args.warmup, stream)
         elt = 2 if Xin.dtype == "bf16" else 4
         alg = algorithmic_bytes(N, n, d, r, elt)
+        extra = {}
+        if which == "decode":
+            # per call warm, cold (512 MiB written between calls so nothing of the
+            # call's data is left in the caches), and replayed from a HIP graph
+            flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+            extra["warm"] = percentiles(per_call_ms(call, 200, stream))
+            extra["cold"] = percentiles(per_call_ms(call, 50, stream, between=lambda: flush.fill_(1)))
+            extra["graph_replay_us_per_call"] = graph_replay_ms(call, steps, args.warmup, stream) * 1e3
+            del flush
+            log(f"decode: warm p50 {extra['warm']['ms_p50'] * 1e3:.1f} us, cold p50 "
+                f"{extra['cold']['ms_p50'] * 1e3:.1f} us, graph replay {extra['graph_replay_us_per_call']:.1f} us")
         log(f"{which}: {ms * 1e3:.2f} us/call")
         return line(f"GR fused write+read us/call ({which}, N={N}, d={d}, n={n}, r={r})",
                     ms * 1e3, "us/call", steps, args.warmup, ms,
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "cache": "warm, back-to-back"},
                     dtype=Xin.dtype, higher=False, tokens_per_s=N / (ms * 1e-3),
-                    roofline=roofline(alg, ms, "gr_fused_write_read"))
+                    roofline=roofline(alg, ms, "gr_fused_write_read"), **extra)
     if which in ("prefill_fp8", "prefill_r320"):
         k = 6 if which == "prefill_fp8" else 7
         W = inputs.WORKLOADS[k]
@@ -370,6 +421,10 @@ def main():
                      "frac": gbps / PEAK_HBM_GBPS, "traffic": stored_traffic(kname),
                      "kernel": kname, "algorithmic_bytes_per_launch": alg},
     }
+
+    # spread of single calls (HIP events around each; not part of the timed region)
+    out.update(percentiles(per_call_ms(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next),
+                                       args.steps, stream)))
 
     if args.copy_probe:
         nbytes = 1 << 30

@@ -450,3 +450,39 @@ def test_chain_workload_full_sampled():
     idx = sample_tokens(Xin.N, 32, seed=5)
     oR, ss, ys = oracle.chain(Xin.X[idx], Xin.params, Xin.eps, "bf16", record=True)
     check_chain("chain-full final state (sampled)", R[idx], oR, chain_scale(Xin.X[idx], ss, ys))
+
+
+def test_graph_replay_matches_eager():
+    """The fused call captured in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed three times, with eager work and synchronisations in between:
+    every replay gives the eager result bit for bit (state, u, s).  The
+    kernels record no memset, so the graph holds kernel nodes only."""
+    X = inputs.make_gr_inputs(300, 4, 1024, 64, "bf16", seed=21, branch_scale=(1.0, 0.5, 2.0, 1.0))
+    p = dev_params(X.params[1])
+    R0, y = X.X.to(DEV), X.y.to(DEV)
+    s_in = torch.rand(300, 4, device=DEV) * 2
+    # eager reference
+    Re = R0.clone()
+    ue, se = gr.fused_write_read(Re, y, s_in, p)
+    # static buffers for the graph; one eager call first (no allocation inside the capture)
+    Rg = R0.clone()
+    ug = torch.empty_like(ue)
+    sg = torch.empty_like(se)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gr.fused_write_read(Rg, y, s_in, p, u=ug, s=sg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):     # the warmed-up stream: same workspace
+        gr.fused_write_read(Rg, y, s_in, p, u=ug, s=sg)
+    for k in range(3):
+        Rg.copy_(R0)                                # eager work between replays
+        ug.zero_(); sg.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Rg, Re), f"replay {k}: state differs"
+        assert torch.equal(ug, ue), f"replay {k}: u differs"
+        assert torch.equal(sg, se), f"replay {k}: s differs"

@@ -153,14 +153,18 @@ _workspaces = {}
 
 
 def _workspace(device, nbytes: int) -> Tuple[int, int]:
-    """Per-device scratch buffer, grown on demand (used on the current stream;
-    the library needs no initialisation of it)."""
+    """Scratch buffer per (device, stream), grown on demand: calls on one
+    stream are ordered, so they may share it; calls on different streams get
+    their own.  The library needs no initialisation of it.  (Under graph
+    capture, make one eager call first so that no allocation happens inside
+    the capture.)"""
     if nbytes == 0:
         return 0, 0
-    buf = _workspaces.get(device)
+    key = (device, _stream(device))
+    buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _workspaces[device] = buf
+        _workspaces[key] = buf
     return buf.data_ptr(), buf.numel()
 
 
