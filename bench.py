@@ -9,10 +9,12 @@ step of the hot path.  Inputs are seeded synthetic tensors already resident in
 HBM.  Prints one JSON line on stdout; progress goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       python bench.py --workload {prefill,prefill_fp8,prefill_r320,decode,addnorm,chain,tiny,variants,all}
+       python bench.py --workload {prefill,prefill_fp8,prefill_r320,prefill_fp8_r320,decode,addnorm,
+                                   chain,tiny,variants,all}
 The default (prefill) line is the headline; the other workloads print their own
 line (prefill_fp8: the same shape with an e4m3 branch state; prefill_r320: the
-pages' model shape d = 2560 with gate rank r = d/8 = 320; variants: expand,
+pages' model shape d = 2560 with gate rank r = d/8 = 320; prefill_fp8_r320:
+that shape with an e4m3 state; variants: expand,
 static read, round-robin write, per-channel write and collapse at the prefill
 shape, one line each; decode: us per
 call with the state warm in cache, back to back; addnorm:
@@ -224,8 +226,8 @@ def bench_other(which, args, dev):
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "cache": "warm, back-to-back"},
                     dtype=Xin.dtype, higher=False, tokens_per_s=N / (ms * 1e-3),
                     roofline=roofline(alg, ms, "gr_fused_write_read"), **extra)
-    if which in ("prefill_fp8", "prefill_r320"):
-        k = 6 if which == "prefill_fp8" else 7
+    if which in ("prefill_fp8", "prefill_r320", "prefill_fp8_r320"):
+        k = {"prefill_fp8": 6, "prefill_r320": 7, "prefill_fp8_r320": 8}[which]
         W = inputs.WORKLOADS[k]
         log(f"generating workload {W['name']} ...")
         Xin = inputs.workload(k)
@@ -236,7 +238,7 @@ def bench_other(which, args, dev):
         so = torch.empty((N, n), dtype=torch.float32, device=dev)
         _, s_in = gr.read(X, p0)
         ms = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=so), args.steps, args.warmup, stream)
-        f8 = which == "prefill_fp8"
+        f8 = Xin.dtype == "fp8"
         alg = algorithmic_bytes(N, n, d, r, 2, state_elt=1 if f8 else 2)
         log(f"{which}: {ms * 1e3:.1f} us/call, {N / (ms * 1e-3) / 1e6:.2f} M tok/s")
         sdt = "e4m3" if f8 else "bf16"
@@ -247,8 +249,9 @@ def bench_other(which, args, dev):
                     dtype="bf16", gate_tflops=gate_flops(N, n, d, r) / (ms * 1e-3) / 1e12,
                     hbm_GBps_algorithmic=alg / (ms * 1e-3) / 1e9,
                     roofline=(roofline(alg, ms, "gr_fused_write_read", stored_traffic("gr_fused_write_read_fp8"))
-                              if f8 else mfma_roofline(gate_flops(N, n, d, r), ms, "gr_fused_write_read",
-                                                       stored_traffic("gr_fused_write_read_r320"))))
+                              if which == "prefill_fp8" else
+                              mfma_roofline(gate_flops(N, n, d, r), ms, "gr_fused_write_read",
+                                            stored_traffic("gr_fused_write_read_" + which[len("prefill_"):]))))
     if which == "variants":
         # the variants on the widened state at the prefill shape, bf16: one line each
         N, n, d = 16384, 4, 4096
@@ -342,8 +345,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny",
-                             "variants", "all"])
+                    choices=["prefill", "prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm",
+                             "chain", "tiny", "variants", "all"])
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
 
@@ -359,7 +362,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload != "prefill":
-        names = (["prefill_fp8", "prefill_r320", "decode", "addnorm", "chain", "tiny", "variants"]
+        names = (["prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm", "chain", "tiny",
+                  "variants"]
                  if args.workload == "all" else [args.workload])
         for w in names:
             res = bench_other(w, args, dev)

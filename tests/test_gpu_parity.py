@@ -211,6 +211,21 @@ def test_wide_gate_many_tokens(N, d, r, w_std, form, monkeypatch):
     run_read_write_fused(X, f"wide-{form}-N{N}-d{d}-r{r}")
 
 
+@pytest.mark.parametrize("N,d,r,w_std", [
+    (1, 2560, 320, 0.05), (64, 2560, 320, 0.05), (37, 512, 144, 0.05), (130, 1024, 256, 0.2),
+    (300, 640, 320, 0.05), (129, 2560, 160, 0.3), (200, 384, 224, 0.5), (4300, 256, 320, 0.2),
+    (4200, 384, 192, 0.05), (50, 448, 224, 0.05),
+])
+def test_fp8_state_wide_gate(N, d, r, w_std):
+    """e4m3 state with a gate rank beyond 124: kernel 1's wide form on e4m3
+    rows and kernel 2's XCD walk with four 32-channel ranges (one 128-byte
+    line of e4m3) in lockstep, at few and many tokens; d = 448 is not a
+    multiple of 128 and takes the shape-generic kernels."""
+    X = inputs.make_gr_inputs(N, 4, d, r, "fp8", seed=19 * N + d + r, w_std=w_std,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"fp8-wide-N{N}-d{d}-r{r}")
+
+
 def test_wide_gate_without_write_projection():
     """r = 320 with no W_write: 320 projection rows (20 blocks), s == 1."""
     X = inputs.make_gr_inputs(100, 4, 1280, 320, "bf16", seed=43, with_write=False)
@@ -372,6 +387,18 @@ def test_real_shape_r320_full_sampled():
     """Workload 7 at its full size (N=16384), 64 sampled tokens."""
     Xin = inputs.workload(7)
     sampled_read_parity(Xin, sample_tokens(Xin.N, 64, seed=7), "d2560-r320-16384")
+
+
+def test_real_shape_fp8_subset():
+    """Workload 8 (d = 2560, r = 320, e4m3 state), first 256 tokens, every
+    token compared."""
+    run_read_write_fused(inputs.workload(8, N=256), "fp8-d2560-r320-256")
+
+
+def test_real_shape_fp8_full_sampled():
+    """Workload 8 at its full size (N=16384), 64 sampled tokens."""
+    Xin = inputs.workload(8)
+    sampled_read_parity(Xin, sample_tokens(Xin.N, 64, seed=8), "fp8-d2560-r320-16384")
 
 
 def test_decode_workload():

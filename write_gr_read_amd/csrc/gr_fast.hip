@@ -486,7 +486,8 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     }
 }
 
-// Kernel 1, wide form (r + n > 128, bf16 state).  Same walk, load layout,
+// Kernel 1, wide form (r + n > 128; bf16 or e4m3 state, loaded and written as
+// in k_stream_proj).  Same walk, load layout,
 // eq:write and records as k_stream_proj, but the contraction is arranged so
 // that the weights cost one LDS plane instead of two:
 //   P_i = W^{(i)} (gamma_i . R'_i),
@@ -499,9 +500,9 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // ~123 KB of LDS); NRB * 4 accumulators per lane, so two waves per SIMD: the
 // state / y words of the next two rounds are kept in flight (two register
 // slots, each refilled as soon as its round's element phase is done).
-template <bool FUSED, int NRB>
+template <bool FUSED, int NRB, bool F8>
 __global__ void __launch_bounds__(kThreads, 2)
-k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
+k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
                    const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
                    const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
                    FastShape sh) {
@@ -514,6 +515,8 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     constexpr int NV = NRB * 16 * (KW / 8);            // 16-byte vectors of W per chunk
     constexpr int WV = (NV + kThreads - 1) / kThreads;
     constexpr int RP = PCS + 1;                        // B tile pitch in pieces (odd: no bank conflicts)
+    using T = typename StateT<F8>::type;
+    using SV = typename StateT<F8>::vec8;              // 8 channels of the state
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][NRB * 16 * kPitch];
     __shared__ __attribute__((aligned(16))) u32x4 lds_b[kWaves][2][16 * RP];   // hi, lo
 
@@ -571,7 +574,7 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
         sq[q] = (FUSED && vq[q]) ? s_in[t * n + br] : 0.f;
         ss[q] = 0.f;
     }
-    bf16_t *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
+    T *const sbase = state + (t0 * n + br) * (int64_t)d + c_base;
     const bf16_t *const ybase = FUSED ? y + t0 * (int64_t)d + c_base : nullptr;
     const bf16_t *const gbase = gamma + (int64_t)br * d + c_base + 8 * m16;
     const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
@@ -579,13 +582,13 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
 
     // two slots of state / y words: round rd uses slot rd % 2, and the loads
     // of round rd + 2 go into that slot as soon as its element phase is done
-    u32x4 rrA[NQ], yyA[NQ], rrB[NQ], yyB[NQ];
-    auto load_round = [&](int rd, u32x4 (&rr)[NQ], u32x4 (&yy)[NQ]) {
+    SV rrA[NQ], rrB[NQ];
+    u32x4 yyA[NQ], yyB[NQ];
+    auto load_round = [&](int rd, SV (&rr)[NQ], u32x4 (&yy)[NQ]) {
         const bool in = rd < nround && rd * RC + 8 * m16 < chan;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            rr[q] = (vq[q] && in) ? *reinterpret_cast<const u32x4 *>(sbase + q * qstride + rd * RC + soff)
-                                  : u32x4{0u, 0u, 0u, 0u};
+            rr[q] = (vq[q] && in) ? *reinterpret_cast<const SV *>(sbase + q * qstride + rd * RC + soff) : SV{};
             yy[q] = (FUSED && vq[q] && in) ? *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff)
                                            : u32x4{0u, 0u, 0u, 0u};
         }
@@ -596,16 +599,26 @@ k_stream_proj_wide(bf16_t *__restrict__ state, const bf16_t *__restrict__ y,
     for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 *my_hi = lds_b[wave][0], *my_lo = lds_b[wave][1];
 
-    auto do_round = [&](int rd, u32x4 (&rr)[NQ], u32x4 (&yy)[NQ]) {
+    auto do_round = [&](int rd, SV (&rr)[NQ], u32x4 (&yy)[NQ]) {
         const bool in = rd * RC + 8 * m16 < chan;
         const u32x4 gm = in ? *reinterpret_cast<const u32x4 *>(gbase + rd * RC) : u32x4{0u, 0u, 0u, 0u};
         // eq:write in the load layout: store, sum of squares, gamma . R' as hi / lo tiles
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            u32x4 w = rr[q];
-            if (FUSED) {
-                w = write8_bf16(sq[q], yy[q], rr[q]);
-                if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+            u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
+            if constexpr (F8) {
+                u32x2 o = rr[q];
+                if (FUSED) {
+                    o = write8_fp8(sq[q], yy[q], rr[q]);
+                    if (vq[q] && in) *reinterpret_cast<u32x2 *>(sbase + q * qstride + rd * RC + soff) = o;
+                }
+                w = widen8_fp8_bf16(o);
+            } else {
+                w = rr[q];
+                if (FUSED) {
+                    w = write8_bf16(sq[q], yy[q], rr[q]);
+                    if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) ss[q] = dot2_bf16(w[e], w[e], ss[q]);
@@ -1101,9 +1114,9 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
 // tiles in the same order, and each line's second half is an L2 hit.  The
 // W_up rows of a range (NB * 32 rows, MFMA row order) are restaged in LDS
 // whenever a workgroup moves on to its next range.
-template <int NB, int RKS>
+template <int NB, int RKS, bool F8>
 __global__ void __launch_bounds__(kResThreads, 2)
-k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ gamma,
                     const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
                     FastShape sh, int ranges, int wgs_per_xcd) {
     constexpr int CH = kChunk;                         // channels per range
@@ -1114,19 +1127,22 @@ k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__
 
     const int d = sh.d, r = sh.r;
     const int xcd = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
-    const int pair = j >> 1, side = j & 1, pairs = wgs_per_xcd / 2;
+    // GS workgroups in lockstep cover one 128-byte line of the state rows
+    constexpr int GS = F8 ? 4 : 2;
+    using SV = typename StateT<F8>::vec8;              // 8 channels of the state
+    const int grp = j / GS, side = j % GS, groups = wgs_per_xcd / GS;
     const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
     const int64_t ntx = tiles > xcd ? (tiles - xcd + 7) / 8 : 0;   // tiles xcd + 8k of this XCD
-    const int64_t units = (int64_t)(ranges / 2) * ntx;             // (range pair, tile) units
-    if (pair >= pairs) return;                         // whole workgroup (odd count: the last one idles)
-    const int64_t u0 = units * pair / pairs, u1 = units * (pair + 1) / pairs;
+    const int64_t units = (int64_t)(ranges / GS) * ntx;            // (range group, tile) units
+    if (grp >= groups) return;                         // whole workgroup (the count's remainder idles)
+    const int64_t u0 = units * grp / groups, u1 = units * (grp + 1) / groups;
     if (u0 >= u1) return;                              // whole workgroup
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, m16 = lane & 15;
     const float inv_n = 1.0f / (float)NB;
 
     auto unit_tile = [&](int64_t q) { return (int64_t)xcd + 8 * (q % ntx); };
-    auto unit_range = [&](int64_t q) { return 2 * (int)(q / ntx) + side; };
+    auto unit_range = [&](int64_t q) { return GS * (int)(q / ntx) + side; };
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
     auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
         const int64_t t = token(T);
@@ -1144,11 +1160,11 @@ k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__
 #pragma unroll
         for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
     };
-    // state of branch i, range rg of tile T: one 16-byte word per lane
+    // state of branch i, range rg of tile T: 8 channels per lane
     auto load_state = [&](int64_t T, int rg, int i) {
         const int64_t t = token(T);
-        if (t >= sh.N) return u32x4{0u, 0u, 0u, 0u};
-        return *reinterpret_cast<const u32x4 *>(state + t * (int64_t)NB * d + (int64_t)i * d + rg * CH + 8 * g);
+        if (t >= sh.N) return SV{};
+        return *reinterpret_cast<const SV *>(state + t * (int64_t)NB * d + (int64_t)i * d + rg * CH + 8 * g);
     };
     // W_up rows (branch i, channel cc of range rg) in MFMA row order, and gamma/n
     auto stage = [&](int rg) {
@@ -1171,7 +1187,7 @@ k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__
 
     bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
     float rms[NB], nrms[NB];
-    u32x4 sv[NB];
+    SV sv[NB];
     int64_t q = u0;
     int64_t T = unit_tile(q);
     int rg = unit_range(q);
@@ -1204,10 +1220,19 @@ k_gate_combine_wide(const bf16_t *__restrict__ state, const bf16_t *__restrict__
                 }
                 // tl[m] = -log2(e) * l for channel 8g + 4h + m of the range, branch i
                 const uint32_t *gp = &lds_g[i * CH + 8 * g + 4 * h];
+                float xe[4];                              // e4m3: elements 4h .. 4h+3 of the lane's 8
+                if constexpr (F8) {
+                    const f32x2 a01 = fp8x2_lo(sv[i][h]), a23 = fp8x2_hi(sv[i][h]);
+                    xe[0] = a01.x; xe[1] = a01.y; xe[2] = a23.x; xe[3] = a23.y;
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int e = 4 * h + m;
-                    const float bterm = dot2_bf16(sv[i][e >> 1], gp[m], 0.f);
+                    float bterm;
+                    if constexpr (F8)   // (gamma/n) in the half word of this channel's parity
+                        bterm = xe[m] * ((m & 1) ? bf16_hi(gp[m]) : bf16_lo(gp[m]));
+                    else
+                        bterm = dot2_bf16(sv[i][e >> 1], gp[m], 0.f);
                     const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
                     uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
                 }
@@ -1416,11 +1441,10 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;
     if (sh.wide) {
-        if (F8) return hipErrorInvalidValue;   // (an e4m3 state has the narrow gate only)
 #define GR_K1W(NRB)                                                                         \
     case NRB:                                                                               \
-        hipLaunchKernelGGL((k_stream_proj_wide<FUSED, NRB>), dim3(grid), dim3(kThreads), 0, st, \
-                           (bf16_t *)a.state, y, a.s_in, (const bf16_t *)a.gamma,           \
+        hipLaunchKernelGGL((k_stream_proj_wide<FUSED, NRB, F8>), dim3(grid), dim3(kThreads), 0, st, \
+                           (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,                \
                            (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
         break;
         switch (sh.row_blocks) {
@@ -1512,25 +1536,27 @@ int cu_count() {
     return cached[dev];
 }
 
-template <int NB, int RKS>
+template <int NB, int RKS, bool F8>
 hipError_t launch_k2_wide_rks(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
-    const int ranges = sh.d / kChunk;                  // even: d is a multiple of 64
+    // ranges: d / 32, a multiple of the lockstep group (2 bf16, 4 e4m3): d is a
+    // multiple of 64 (bf16) or 128 (e4m3 wide gate)
+    const int ranges = sh.d / kChunk;
     const int per_xcd = (cu_count() + 7) / 8;
-    hipLaunchKernelGGL((k_gate_combine_wide<NB, RKS>), dim3((unsigned)(8 * per_xcd)), dim3(kResThreads), 0, st,
-                       (const bf16_t *)a.state, (const bf16_t *)a.gamma, (const bf16_t *)a.wu,
+    hipLaunchKernelGGL((k_gate_combine_wide<NB, RKS, F8>), dim3((unsigned)(8 * per_xcd)), dim3(kResThreads), 0, st,
+                       (const typename StateT<F8>::type *)a.state, (const bf16_t *)a.gamma, (const bf16_t *)a.wu,
                        (bf16_t *)a.u, w, sh, ranges, per_xcd);
     return hipGetLastError();
 }
 
-template <int NB>
+template <int NB, bool F8>
 hipError_t launch_k2_wide(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     switch (sh.rk / 32) {
-    case 5: return launch_k2_wide_rks<NB, 5>(a, sh, w, st);
-    case 6: return launch_k2_wide_rks<NB, 6>(a, sh, w, st);
-    case 7: return launch_k2_wide_rks<NB, 7>(a, sh, w, st);
-    case 8: return launch_k2_wide_rks<NB, 8>(a, sh, w, st);
-    case 9: return launch_k2_wide_rks<NB, 9>(a, sh, w, st);
-    case 10: return launch_k2_wide_rks<NB, 10>(a, sh, w, st);
+    case 5: return launch_k2_wide_rks<NB, 5, F8>(a, sh, w, st);
+    case 6: return launch_k2_wide_rks<NB, 6, F8>(a, sh, w, st);
+    case 7: return launch_k2_wide_rks<NB, 7, F8>(a, sh, w, st);
+    case 8: return launch_k2_wide_rks<NB, 8, F8>(a, sh, w, st);
+    case 9: return launch_k2_wide_rks<NB, 9, F8>(a, sh, w, st);
+    case 10: return launch_k2_wide_rks<NB, 10, F8>(a, sh, w, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1568,8 +1594,9 @@ bool fast_path_ok(const ReadArgs &a) {
     const int rows = a.r + (a.ww ? a.n : 0);
     const int nrb = (rows + 15) / 16;
     if (nrb <= kMaxRowBlocks && a.r <= 128) return true;
-    // wide gate: bf16 state only
-    return !a.fp8 && nrb <= kMaxWideRowBlocks;
+    // wide gate; an e4m3 state also needs d % 128 (kernel 2 covers whole
+    // 128-byte state lines with four 32-channel ranges in lockstep)
+    return nrb <= kMaxWideRowBlocks && (!a.fp8 || a.d % 128 == 0);
 }
 
 size_t fast_workspace_bytes(int64_t N, int n, int d, int r) {
@@ -1596,11 +1623,11 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // (an e4m3 state has the resident form only)
-    if (a.fp8) return launch_k2_resident_fp8<4>(a, sh, w, st);
+    // an e4m3 state: the resident form (narrow gate) or the XCD walk (wide gate)
+    if (a.fp8) return sh.rk > 128 ? launch_k2_wide<4, true>(a, sh, w, st) : launch_k2_resident_fp8<4>(a, sh, w, st);
     // a wide gate (more than four k-steps) has the resident form only, walked
     // XCD by XCD once every XCD has several token tiles
-    if (sh.rk > 128 && sh.N >= kWideXcdMinTokens && a.k2_variant != 2) return launch_k2_wide<4>(a, sh, w, st);
+    if (sh.rk > 128 && sh.N >= kWideXcdMinTokens && a.k2_variant != 2) return launch_k2_wide<4, false>(a, sh, w, st);
     const bool resident = sh.rk > 128 || a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
     return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
 }

@@ -225,6 +225,9 @@ WORKLOADS = {
     # the pages' own model shape: d = 2560 and the gate rank r = d/8 = 320
     7: dict(name="gr_prefill_d2560_r320", kind="gr", N=16384, n=4, d=2560, r=320, dtype="bf16",
             y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
+    # the pages' model shape with the FP8 (e4m3) branch state
+    8: dict(name="gr_prefill_fp8_d2560_r320", kind="gr", N=16384, n=4, d=2560, r=320, dtype="fp8",
+            y_std=0.05, branch_scale=(1.0, 0.5, 2.0, 1.0), param_sets=2),
 }
 
 
@@ -232,7 +235,7 @@ def workload(k: int, N: Optional[int] = None):
     """Inputs of workload ``k`` (optionally with fewer tokens, same recipe).
 
     Parameter set 0 feeds the untimed read that produces the write strengths of
-    the fused call; parameter set 1 is the next sublayer's (workloads 1, 3, 4, 6, 7).
+    the fused call; parameter set 1 is the next sublayer's (workloads 1, 3, 4, 6, 7, 8).
     Workload 5 has one parameter set per sublayer and no y (F makes it).
     """
     w = WORKLOADS[k]
