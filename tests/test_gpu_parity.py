@@ -161,6 +161,17 @@ def test_saturating_gate(N, d, r, w_std):
     run_read_write_fused(X, f"saturating-N{N}-d{d}-r{r}")
 
 
+@pytest.mark.parametrize("N,d,r", [(511, 1024, 48), (512, 4096, 64), (1000, 1024, 32), (1024, 2048, 64),
+                                   (2065, 1024, 16), (3000, 4096, 64)])
+def test_kernel1_forms_by_token_count(N, d, r):
+    """Kernel 1 takes its few-token form below 1024 tokens (n = 4) and the tile
+    walk with channel splits above, until the grid is full; both sides of each
+    switch, ragged tails, every token compared."""
+    X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=7 * N + d + r, w_std=0.2,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"k1-forms-N{N}-d{d}-r{r}")
+
+
 def test_workspace_needs_no_initialisation():
     """Every workspace byte a call reads is written earlier in the same call:
     a workspace full of 0xFF (NaN floats, huge counts) changes nothing."""
@@ -171,8 +182,9 @@ def test_workspace_needs_no_initialisation():
     s_in = torch.full((300, 4), 0.75, device=DEV)
     runs = []
     for fill in (0xFF, 0x00):
-        gr.read(R, p0)  # make sure the per-device workspace exists
-        gr._workspaces[torch.device(DEV)].fill_(fill)
+        gr.read(R, p0)  # make sure this stream's workspace exists
+        dev = torch.device(DEV)
+        gr._workspaces[(dev, gr._stream(dev))].fill_(fill)
         Rc = R.clone()
         u, s = gr.fused_write_read(Rc, y, s_in, p1)
         torch.cuda.synchronize()

@@ -111,7 +111,7 @@ size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
     a.fp8 = dt == GR_FP8_E4M3;
     a.N = N; a.n = L->n; a.d = L->d; a.r = L->r;
     a.ww = L->w_write;
-    return grk::fast_path_ok(a) && !force_generic() ? grk::fast_workspace_bytes(N, L->n, L->d, L->r) : 0;
+    return grk::fast_path_ok(a) && !force_generic() ? grk::fast_workspace_bytes(a) : 0;
 }
 
 gr_status launched(hipError_t e, const char *fn) {

@@ -87,7 +87,7 @@ constexpr int kMaxWideRowBlocks = 21;     // wide gate (kernel 1 wide form): r +
 constexpr int kMaxWideRKS = 10;           // wide gate: r up to 320 (k-steps of 32 of the up projection)
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 #ifndef GR_SPLIT_TARGET
-#define GR_SPLIT_TARGET 64
+#define GR_SPLIT_TARGET 256
 #endif
 constexpr int kSplitTarget = GR_SPLIT_TARGET;  // kernel-1 workgroups wanted before splitting channels
 constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power of two)
@@ -95,6 +95,19 @@ constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power
 #define GR_PREP_MIN_TILES 8
 #endif
 constexpr int kPrepMinTiles = GR_PREP_MIN_TILES;  // token tiles from which W' is split once per call
+#ifndef GR_K1_SMALL
+#define GR_K1_SMALL 1
+#endif
+constexpr bool kSmallK1 = GR_K1_SMALL;     // few tokens: kernel 1's few-token form
+#ifndef GR_SMALL_BELOW
+#define GR_SMALL_BELOW 32
+#endif
+constexpr int kSmallBelow = GR_SMALL_BELOW;  // ... used while (token tiles) x n is below this
+#ifndef GR_SMALL_TARGET
+#define GR_SMALL_TARGET 256
+#endif
+constexpr int kSmallTarget = GR_SMALL_TARGET;  // few-token kernel 1: workgroups wanted before splitting
+constexpr int kSmallWaves = 8;            // waves per few-token kernel-1 workgroup
 
 
 struct FastShape {
@@ -108,6 +121,8 @@ struct FastShape {
     int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
     bool prep;           // W' split once per call by k_prep_wprime (enough token tiles)
     bool wide;           // r + n beyond 128: kernel 1's wide form (gamma on the state side, no W')
+    bool small;          // few tokens: kernel 1's few-token form (k_stream_proj_small)
+    int small_kpw;       // ... its k-steps (32 channels) per wave
     int64_t N, tiles;
 };
 
@@ -136,6 +151,22 @@ FastShape shape_of(const ReadArgs &a) {
     s.k2_chan = c2;
     s.wide = s.row_blocks > kMaxRowBlocks;
     s.prep = !s.wide && s.tiles >= kPrepMinTiles;
+    // Few tokens, narrow gate: kernel 1's few-token form, whose workgroups are
+    // (16 tokens, branch, split); splits (a power of two, at most kMaxSplit)
+    // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
+    s.small = false;
+    s.small_kpw = 0;
+    if (kSmallK1 && !s.wide && s.tiles * s.n < kSmallBelow) {
+        const int64_t groups = (s.N + 15) / 16;
+        int sp = 1;
+        while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
+        const int per = kSmallWaves * kChunk * sp;   // channels covered per k-step of every wave
+        s.small = true;
+        s.ksplit = sp;
+        s.ksplit_chan = 0;
+        s.small_kpw = (s.d + per - 1) / per;
+        s.prep = false;
+    }
     return s;
 }
 
@@ -178,9 +209,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-// W' = W (.) gamma for 8 channels (one 16-byte vector of each), as bf16 hi
-// and lo words: hi = bf16(x), lo = bf16(x - hi); x = w * gamma is exact in fp32.
-__device__ __forceinline__ void split_wprime(u32x4 w, u32x4 gm, u32x4 &hi, u32x4 &lo) {
+// x = a (.) b for 8 bf16 channels (one 16-byte vector of each) -- W' = W . gamma,
+// or gamma . R' -- as bf16 hi and lo words: hi = bf16(x), lo = bf16(x - hi);
+// the product of two bf16 values is exact in fp32.
+__device__ __forceinline__ void split_product(u32x4 w, u32x4 gm, u32x4 &hi, u32x4 &lo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float x0 = bf16_lo(w[e]) * bf16_lo(gm[e]);
@@ -212,7 +244,7 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
             gm = *reinterpret_cast<const u32x4 *>(gamma + col);
         }
         u32x4 hi, lo;
-        split_wprime(w, gm, hi, lo);
+        split_product(w, gm, hi, lo);
         *reinterpret_cast<u32x4 *>(ws.wprime + ((int64_t)(i * 2) * rows_p + j) * sh.d + cv * 8) = hi;
         *reinterpret_cast<u32x4 *>(ws.wprime + ((int64_t)(i * 2 + 1) * rows_p + j) * sh.d + cv * 8) = lo;
     }
@@ -340,7 +372,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
             } else if (v < NV) {
                 const int row = v / (kIter / 8), cv = v % (kIter / 8);
                 u32x4 hi, lo;
-                split_wprime(wreg[q], greg[PREP ? 0 : q], hi, lo);
+                split_product(wreg[q], greg[PREP ? 0 : q], hi, lo);
                 *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kPitch + cv * 8]) = hi;
                 *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kPitch + cv * 8]) = lo;
             }
@@ -486,6 +518,134 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     }
 }
 
+// Kernel 1, few-token form.  With few tokens the tile walk above has too few
+// (tile, branch) units to fill the GPU, and each unit is a chain of rounds.
+// Here a workgroup takes 16 tokens of one branch and a split of the channels,
+// one slice of kpw k-steps (32 channels each) per wave, so a wave makes one
+// short pass.  A lane loads its state words straight in the MFMA B layout
+// (token = lane % 16, 8 channels of lane group lane / 16): eq:write, its store
+// and the sum of squares run there, with no LDS tile.  As in the wide form the
+// contraction is P_i = W^{(i)} (gamma_i . R'_i): the raw W_down / W_write rows
+// are the A operand, loaded straight from memory (row lane % 16 of each 16-row
+// block, the same 8 channels), and gamma . R' -- exact in fp32 -- is split into
+// bf16 hi + lo once per k-step as the B operand.  The waves' partial
+// projections and sums of squares are added in LDS in wave order and written as
+// the (token, branch, split) record that k_reduce_records expects.
+constexpr int kSmallKB = 4;               // k-steps loaded together (one batch)
+template <bool FUSED, int NRB, bool F8>
+__global__ void __launch_bounds__(64 * kSmallWaves, 2)
+k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
+                    const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
+                    const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
+                    FastShape sh) {
+    using T = typename StateT<F8>::type;
+    using SV = typename StateT<F8>::vec8;
+    constexpr int ACC = NRB * 4;                          // accumulator words per lane
+    __shared__ float lds_p[kSmallWaves][ACC + 1][64];     // per wave: accumulators, then ss
+    const int n = sh.n, d = sh.d, S = sh.ksplit, kpw = sh.small_kpw;
+    // blockIdx -> (token group, branch, split) with (branch, split) fastest, so
+    // the workgroups reading one slice of W sit on one XCD when n S % 8 == 0
+    const int64_t b = blockIdx.x;
+    const int bs = (int)(b % (n * S));
+    const int64_t tg = b / (n * S);
+    const int br = bs / S, split = bs % S;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, m16 = lane & 15;
+    const int64_t t = tg * 16 + m16;                      // this lane's token (MFMA column)
+    const bool valid = t < sh.N;
+    const int64_t nd = (int64_t)n * d;
+    const int c_wave = (split * kSmallWaves + wave) * kpw * kChunk;
+    const float sv = (FUSED && valid) ? s_in[t * n + br] : 0.f;
+    T *const srow = state + (t * n + br) * (int64_t)d;
+    const bf16_t *const yrow = FUSED ? y + t * (int64_t)d : nullptr;
+
+    f32x4 acc[NRB];
+#pragma unroll
+    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    for (int kb = 0; kb < kpw; kb += kSmallKB) {
+        SV rr[kSmallKB];
+        u32x4 yy[kSmallKB], gm[kSmallKB], wv[kSmallKB][NRB];
+        bool kin[kSmallKB];
+#pragma unroll
+        for (int ks = 0; ks < kSmallKB; ++ks) {
+            const int c0 = c_wave + (kb + ks) * kChunk;   // whole 32-channel chunk in or out (d % 32 == 0)
+            kin[ks] = kb + ks < kpw && c0 < d;
+            const int c = c0 + 8 * g;
+            rr[ks] = SV{};
+            yy[ks] = gm[ks] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int k = 0; k < NRB; ++k) wv[ks][k] = u32x4{0u, 0u, 0u, 0u};
+            if (kin[ks]) {
+                if (valid) {
+                    rr[ks] = *reinterpret_cast<const SV *>(srow + c);
+                    if (FUSED) yy[ks] = *reinterpret_cast<const u32x4 *>(yrow + c);
+                }
+                gm[ks] = *reinterpret_cast<const u32x4 *>(gamma + (int64_t)br * d + c);
+#pragma unroll
+                for (int k = 0; k < NRB; ++k) {
+                    const int row = 16 * k + m16;
+                    const bf16_t *src = row < sh.r ? wd + (int64_t)row * nd
+                                      : (row < sh.rows ? ww + (int64_t)(row - sh.r) * nd : nullptr);
+                    if (src) wv[ks][k] = *reinterpret_cast<const u32x4 *>(src + (int64_t)br * d + c);
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < kSmallKB; ++ks) {
+            const int c = c_wave + (kb + ks) * kChunk + 8 * g;
+            u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
+            if constexpr (F8) {
+                u32x2 o = rr[ks];
+                if (FUSED) {
+                    o = write8_fp8(sv, yy[ks], rr[ks]);
+                    if (valid && kin[ks]) *reinterpret_cast<u32x2 *>(srow + c) = o;
+                }
+                w = widen8_fp8_bf16(o);
+            } else {
+                w = rr[ks];
+                if (FUSED) {
+                    w = write8_bf16(sv, yy[ks], rr[ks]);
+                    if (valid && kin[ks]) *reinterpret_cast<u32x4 *>(srow + c) = w;
+                }
+            }
+            // masked lanes and chunks hold zeros: they add nothing below
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
+            // B = gamma . R' as bf16 hi + lo (exact fp32 product split once per
+            // k-step); A = the raw W rows
+            u32x4 bh, bl;
+            split_product(w, gm[ks], bh, bl);
+#pragma unroll
+            for (int k = 0; k < NRB; ++k) {
+                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bh), acc[k], 0, 0, 0);
+                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bl), acc[k], 0, 0, 0);
+            }
+        }
+    }
+    // this wave's share of ss per token: the four lane groups hold its channels
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+#pragma unroll
+    for (int k = 0; k < NRB; ++k)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) lds_p[wave][4 * k + m][lane] = acc[k][m];
+    lds_p[wave][ACC][lane] = ss;
+    __syncthreads();
+    // word j of lane l: P row 16(j/4) + 4(l/16) + j%4 of token l%16 (j < ACC), ss (j = ACC)
+    for (int v = tid; v < (ACC + 1) * 64; v += 64 * kSmallWaves) {
+        const int j = v >> 6, l = v & 63;
+        const int64_t tt = tg * 16 + (l & 15);
+        if (tt >= sh.N || (j == ACC && l >= 16)) continue;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][j][l];
+        float *rec = ws.partial + ((tt * n + br) * S + split) * (int64_t)sh.pstride;
+        rec[j < ACC ? 4 + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3) : 0] = sum;
+    }
+}
+
 // Kernel 1, wide form (r + n > 128; bf16 or e4m3 state, loaded and written as
 // in k_stream_proj).  Same walk, load layout,
 // eq:write and records as k_stream_proj, but the contraction is arranged so
@@ -623,7 +783,7 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
 #pragma unroll
             for (int e = 0; e < 4; ++e) ss[q] = dot2_bf16(w[e], w[e], ss[q]);
             u32x4 hi, lo;
-            split_wprime(w, gm, hi, lo);
+            split_product(w, gm, hi, lo);
             my_hi[(4 * q + g) * RP + m16] = hi;
             my_lo[(4 * q + g) * RP + m16] = lo;
         }
@@ -679,12 +839,13 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
     }
 }
 
-// Kernel 1b: combine the partial records written by k_stream_proj.  One wave
-// per token, four tokens per workgroup: lanes 0..NB-1 sum the squares over
-// the splits (rho_i, rms_i; shared by shuffles), then each lane owns outputs
+// Kernel 1b: combine the partial records written by kernel 1.  One wave per
+// token, four tokens per workgroup: lanes 0..NB-1 sum the squares over the
+// splits (rho_i, rms_i; shared by shuffles), and each lane owns outputs
 // j = lane, lane + 64, ...: the split sums of P_i[j] for every branch (lanes
-// read consecutive j: coalesced; four splits in flight per chain), rho
-// applied, summed over branches in order.
+// read consecutive j: coalesced), rho applied, summed over branches in order.
+// The loads of the sums of squares and of the first two outputs per lane go
+// out together, so a call of few tokens waits for memory once.
 //   j < r        z = (1/n) sum_i rho_i P_i[j]  ->  -log2(e) SiLU(z) as (hi, lo)
 //   r <= j < rk  zero padding of the up projection's k-steps
 //   rk + i       s_i = 2 sigmoid((1/n) sum_i' rho_i' P_i'[r + i])  (1 without W_write)
@@ -710,35 +871,53 @@ k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float ep
             for (int k = 0; k + w < S; k += 2 * w) v[k] += v[k + w];
         return v[0];
     };
+    // P row feeding output j (below), or -1 for a zero pad / no W_write
+    const int outs = sh.rk + NB;
+    auto prow = [&](int j) {
+        if (j < sh.rk) return j < sh.r ? j : -1;
+        return sh.nw ? sh.r + (j - sh.rk) : -1;
+    };
+    auto gather = [&](int j, float (&p)[NB]) {
+        const int row = j < outs ? prow(j) : -1;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) p[i] = row >= 0 ? split_sum(i, 4 + row) : 0.f;
+    };
+    // one round of loads: the sums of squares with the rows of the lane's
+    // first two outputs (none of them waits for rho)
+    const float ss_l = lane < NB ? split_sum(lane, 0) : 0.f;
+    float pa[NB], pb[NB];
+    gather(lane, pa);
+    gather(lane + 64, pb);
     float rho_l = 0.f;
     if (lane < NB) {
-        const float rms = sqrtf(split_sum(lane, 0) / (float)sh.d + eps);
+        const float rms = sqrtf(ss_l / (float)sh.d + eps);
         rho_l = 1.0f / rms;
         ws.rms[t * NB + lane] = rms;
     }
     float rho[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) rho[i] = __shfl(rho_l, i, 64);
-    auto proj = [&](int row) {  // sum_i rho_i (sum over splits of P_i[row]), i in order
-        float p[NB];
-#pragma unroll
-        for (int i = 0; i < NB; ++i) p[i] = split_sum(i, 4 + row);
+    // output j from p[i] = sum over splits of P_i[row(j)]: sum_i rho_i p_i, i in order
+    auto emit = [&](int j, const float (&p)[NB]) {
         float z = 0.f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) z = fmaf(rho[i], p[i], z);
-        return z;
-    };
-    const int outs = sh.rk + NB;
-    for (int j = lane; j < outs; j += 64) {
         if (j < sh.rk) {
-            const float v = j < sh.r ? -kLog2e * silu_f(proj(j) * inv_n) : 0.f;
+            const float v = j < sh.r ? -kLog2e * silu_f(z * inv_n) : 0.f;
             const bf16_t h = f32_to_bf16(v);
             ws.act[(t * 2) * sh.rk + j] = h;
             ws.act[(t * 2 + 1) * sh.rk + j] = f32_to_bf16(v - bf16_to_f32(h));
         } else {
             const int i = j - sh.rk;
-            s_out[t * NB + i] = sh.nw ? 2.0f * sigmoid_f(proj(sh.r + i) * inv_n) : 1.0f;
+            s_out[t * NB + i] = sh.nw ? 2.0f * sigmoid_f(z * inv_n) : 1.0f;
         }
+    };
+    if (lane < outs) emit(lane, pa);
+    if (lane + 64 < outs) emit(lane + 64, pb);
+    for (int j = lane + 128; j < outs; j += 64) {
+        float p[NB];
+        gather(j, p);
+        emit(j, p);
     }
 }
 
@@ -1440,6 +1619,21 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                                (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
                                (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
         break;
+    if (sh.small) {
+        const unsigned sgrid = (unsigned)(((sh.N + 15) / 16) * sh.n * sh.ksplit);
+#define GR_K1S(NRB)                                                                         \
+    case NRB:                                                                               \
+        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8>), dim3(sgrid), dim3(64 * kSmallWaves), 0, st, \
+                           (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,                \
+                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
+        break;
+        switch (sh.row_blocks) {
+            GR_K1S(1) GR_K1S(2) GR_K1S(3) GR_K1S(4) GR_K1S(5) GR_K1S(6) GR_K1S(7) GR_K1S(8)
+        default: return hipErrorInvalidValue;
+        }
+#undef GR_K1S
+        return hipGetLastError();
+    }
     if (sh.wide) {
 #define GR_K1W(NRB)                                                                         \
     case NRB:                                                                               \
@@ -1599,10 +1793,9 @@ bool fast_path_ok(const ReadArgs &a) {
     return nrb <= kMaxWideRowBlocks && (!a.fp8 || a.d % 128 == 0);
 }
 
-size_t fast_workspace_bytes(int64_t N, int n, int d, int r) {
-    ReadArgs a{};
-    a.N = N; a.n = n; a.d = d; a.r = r;
-    a.ww = (const void *)16;  // worst case: with write rows
+size_t fast_workspace_bytes(const ReadArgs &a) {
+    // the layout of exactly this call: with or without W_write the record
+    // stride, the gate form (narrow / wide) and so the W' planes differ
     return workspace_layout(shape_of(a), nullptr, nullptr);
 }
 

@@ -48,7 +48,7 @@ hipError_t launch_collapse(const void *state, const void *w, float eps, void *ou
 
 // MFMA fast path for the bf16 widened state (gr_fast.hip).
 bool fast_path_ok(const ReadArgs &a);
-size_t fast_workspace_bytes(int64_t N, int n, int d, int r);
+size_t fast_workspace_bytes(const ReadArgs &a);   // workspace bytes of this call's fast path
 hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st);
 
 }  // namespace grk
