@@ -133,6 +133,22 @@ def test_workspace_query_and_check(L):
         assert call_read(L, N=16384, lay=lay, ws=FAKE, ws_bytes=need.value - 16) == WORKSPACE
 
 
+def test_workspace_size_follows_the_write_projection(L):
+    """r = 128 with W_write is a wide gate (132 projection rows, no W' planes);
+    without W_write it is narrow (128 rows), and from 1024 tokens its W' hi / lo
+    planes (n x 2 x 128 x d bf16) are part of the workspace: the query sizes the
+    call as it will be made."""
+    d = 4096
+    sizes = {}
+    for ww in (FAKE, None):
+        nbytes = ctypes.c_size_t(0)
+        assert L.gr_workspace_size(1, 1, 1024, ctypes.byref(layer(d=d, r=128, ww=ww)),
+                                   ctypes.byref(nbytes)) == 0
+        sizes[ww] = nbytes.value
+    assert sizes[None] >= 4 * 2 * 128 * d * 2
+    assert sizes[FAKE] > 0
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_launch_failure_is_reported_without_a_gpu(L):
     """With valid arguments but no GPU, the launch itself fails and is mapped

@@ -344,8 +344,11 @@ hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count,
 }
 
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t st) {
+    // four workgroups per CU, each thread striding over the whole range: the
+    // grid sweeps memory as one narrow front (faster here than many short
+    // workgroups or several loads in flight per thread)
     const int64_t vecs = (int64_t)(bytes / 16);
-    const unsigned g = grid_for(vecs, 256 * 4, 256 * 64);
+    const unsigned g = grid_for(vecs, 256 * 4, 1024);
     hipLaunchKernelGGL(k_copy, dim3(g), dim3(256), 0, st, (const u32x4 *)src, (u32x4 *)dst, vecs);
     return hipGetLastError();
 }
