@@ -325,11 +325,22 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     const int nround = (chan + RC - 1) / RC;
     const int c_base = split * chan;                    // first channel of this split
     const int rows_p = NRB * 16;
+    // The rounds start at a rotation per tile (the n workgroups of a tile share
+    // it, and with it their y reads from L2): the tiles running at one time then
+    // stream four columns of their rows, a quarter of the row apart, instead of
+    // all the same one, which HBM serves better; four offsets, not one per tile,
+    // keep the W' chunks in use few enough to stay in L2.  Round s of the walk
+    // is round rnd(s) of the split; the W' chunks follow, chunk i of the walk
+    // being (c0 + i) mod nit.
+    const int rot = (int)(((tile >> 3) & 3) * ((nround + 3) / 4) % nround);
+    const int c0 = rot * (RC / kIter);
+    auto rnd = [&](int s_) { return (s_ + rot) % nround; };   // s_ < nround
 
     // W' staging.  PREP: vector v < NV of the hi plane, NV + v of the lo plane.
     // Else: row j < r from W_down, rows r..r+nw-1 from W_write, the rest zero;
     // times gamma of branch br; split into bf16 hi and lo planes here.
     u32x4 wreg[WV], greg[PREP ? 1 : WV];
+    auto chunk_of = [&](int it) { const int c_ = c0 + it; return c_ >= nit ? c_ - nit : c_; };  // it < nit
     auto load_w = [&](int it) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
@@ -340,7 +351,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                 wreg[q] = u32x4{0u, 0u, 0u, 0u};
                 if (v < 2 * NV && it < nit)
                     wreg[q] = *reinterpret_cast<const u32x4 *>(
-                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + it * kIter + cv * 8);
+                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + chunk_of(it) * kIter + cv * 8);
             } else {
                 const int row = v / (kIter / 8), cv = v % (kIter / 8);
                 const bf16_t *src = nullptr;
@@ -349,7 +360,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                     else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
                 }
                 if (src) {
-                    const int64_t col = (int64_t)br * d + c_base + it * kIter + cv * 8;
+                    const int64_t col = (int64_t)br * d + c_base + chunk_of(it) * kIter + cv * 8;
                     wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
                     greg[PREP ? 0 : q] = *reinterpret_cast<const u32x4 *>(gamma + col);
                 } else {
@@ -399,15 +410,18 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 
     SV rr[NSLOT][NQ];
     u32x4 yy[NSLOT][NQ];
-    auto load_round = [&](int rd, int slot, bool ds = true, bool dy = true) {
-        const bool in = rd < nround && rd * RC + 8 * m16 < chan;
+    // load round `ar` of the split (valid: the walk has such a step)
+    auto load_round = [&](int ar, bool valid, int slot, bool ds = true, bool dy = true) {
+        const bool in = valid && ar * RC + 8 * m16 < chan;
+        const T *const rs = sbase + ar * RC;                   // wave-uniform
+        const bf16_t *const ry = FUSED ? ybase + ar * RC : nullptr;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             if (ds) rr[slot][q] = SV{};
             if (dy) yy[slot][q] = u32x4{0u, 0u, 0u, 0u};
             if (vq[q] && in) {
-                if (ds) rr[slot][q] = *reinterpret_cast<const SV *>(sbase + q * qstride + rd * RC + soff);
-                if (FUSED && dy) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ybase + q * qystride + rd * RC + yoff);
+                if (ds) rr[slot][q] = *reinterpret_cast<const SV *>(rs + q * qstride + soff);
+                if (FUSED && dy) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ry + q * qystride + yoff);
             }
         }
     };
@@ -423,14 +437,18 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     store_w(0);
     load_w(1);
 #pragma unroll
-    for (int q = 0; q < DEPTH; ++q) load_round(q, q);
-    if (DEPTH == 0) load_round(0, 0, true, false);
+    for (int q = 0; q < DEPTH; ++q) load_round(q < nround ? rnd(q) : 0, q < nround, q);
+    if (DEPTH == 0) load_round(rot, true, 0, true, false);
     __syncthreads();
+    int it = 0;                                         // W' chunks of the walk used so far
+    int ar = rot;                                       // round of the split at walk step rd
     for (int rd = 0; rd < nround; ++rd) {
-        if (DEPTH > 0) load_round(rd + DEPTH, DEPTH);
-        else load_round(rd, 0, false, true);
+        const int an = ar + 1 == nround ? 0 : ar + 1;   // ... at step rd + 1
+        if (DEPTH > 0) load_round(rd + DEPTH < nround ? rnd(rd + DEPTH) : 0, rd + DEPTH < nround, DEPTH);
+        else load_round(ar, true, 0, false, true);
         // eq:write in the load layout: store, sum of squares, LDS tile
-        const bool in = rd * RC + 8 * m16 < chan;
+        const bool in = ar * RC + 8 * m16 < chan;
+        T *const ws_ = sbase + ar * RC;                          // wave-uniform
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
@@ -438,14 +456,14 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                 u32x2 o = rr[0][q];
                 if (FUSED) {
                     o = write8_fp8(sq[q], yy[0][q], rr[0][q]);
-                    if (vq[q] && in) *reinterpret_cast<u32x2 *>(sbase + q * qstride + rd * RC + soff) = o;
+                    if (vq[q] && in) *reinterpret_cast<u32x2 *>(ws_ + q * qstride + soff) = o;
                 }
                 w = widen8_fp8_bf16(o);
             } else {
                 w = rr[0][q];
                 if (FUSED) {
                     w = write8_bf16(sq[q], yy[0][q], rr[0][q]);
-                    if (vq[q] && in) *reinterpret_cast<u32x4 *>(sbase + q * qstride + rd * RC + soff) = w;
+                    if (vq[q] && in) *reinterpret_cast<u32x4 *>(ws_ + q * qstride + soff) = w;
                 }
             }
 #pragma unroll
@@ -456,11 +474,10 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
         // instructions of a wave execute in order); keep the phases apart so
         // the element work and the MFMA operands are not live together
         __builtin_amdgcn_sched_barrier(0);
-        if (DEPTH == 0) load_round(rd + 1, 0, true, false);
+        if (DEPTH == 0) load_round(an, rd + 1 < nround, 0, true, false);
 #pragma unroll
         for (int h = 0; h < RC / kIter; ++h) {
-            const int it = rd * (RC / kIter) + h;
-            if (it < nit) {
+            if (ar * (RC / kIter) + h < nit) {               // chunk h of this round exists
                 const int cur = it & 1;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -486,6 +503,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                 if (it + 1 < nit) store_w(cur ^ 1);
                 load_w(it + 2);
                 __syncthreads();
+                ++it;
             }
         }
 #pragma unroll
@@ -495,6 +513,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                 rr[q][e] = rr[q + 1][e];
                 yy[q][e] = yy[q + 1][e];
             }
+        ar = an;
     }
 
     // The record (ss, P) of this (token, branch, split); k_reduce_records,
