@@ -250,6 +250,51 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
     }
 }
 
+// Kernel 1's walk over the rounds (128 channels each) of token tile T starts at
+// this round of its nround: one of four offsets a quarter of a row apart, the
+// same for the tile's n workgroups (see k_stream_proj).  Kernel 2 uses it to
+// read first what kernel 1 wrote last.
+constexpr int kK1Round = 2 * kIter;       // channels per kernel-1 round
+__device__ __forceinline__ int k1_round_rotation(int64_t tile, int nround) {
+    return (int)(((tile >> 3) & 3) * ((nround + 3) / 4) % nround);
+}
+
+// The token tiles p, p + P, ... of a resident kernel-2 workgroup, in two
+// passes: first the tiles whose channels of this range kernel 1 wrote in the
+// second half of its walk over the tile (the likeliest to be still in the
+// 256 MB Infinity Cache when kernel 2 starts), then the others.  nround1 = 0
+// (kernel 1 did not rotate) gives the plain order.
+struct TileWalk {
+    int64_t p, P, tiles;
+    int nround1, kround;   // kernel 1's rounds per split, and this range's round
+    __device__ bool first_pass(int64_t X) const {
+        if (nround1 == 0) return true;
+        int s_ = kround - k1_round_rotation(X, nround1);
+        if (s_ < 0) s_ += nround1;
+        return s_ >= nround1 / 2;
+    }
+    // next tile at or after `from` in pass `pass` (0 or 1), moving on to pass 1
+    // when pass 0 is exhausted; -1 at the end of the walk
+    __device__ int64_t next(int64_t from, int &pass) const {
+        for (int64_t X = from; X < tiles; X += P)
+            if (first_pass(X) == (pass == 0)) return X;
+        if (pass == 0) {
+            pass = 1;
+            for (int64_t X = p; X < tiles; X += P)
+                if (!first_pass(X)) return X;
+        }
+        return -1;
+    }
+};
+__device__ __forceinline__ TileWalk tile_walk(const FastShape &sh, int64_t p, int64_t P, int64_t tiles, int c_begin) {
+    TileWalk w{p, P, tiles, 0, 0};
+    if (!sh.wide && !sh.small && sh.ksplit_chan > 0) {
+        w.nround1 = (sh.ksplit_chan + kK1Round - 1) / kK1Round;
+        w.kround = (c_begin % sh.ksplit_chan) / kK1Round;
+    }
+    return w;
+}
+
 // State element type of the fast path: bf16 words or e4m3 bytes.
 template <bool F8> struct StateT { using type = bf16_t; using vec8 = u32x4; };
 template <> struct StateT<true> { using type = fp8_t; using vec8 = u32x2; };
@@ -332,7 +377,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     // keep the W' chunks in use few enough to stay in L2.  Round s of the walk
     // is round rnd(s) of the split; the W' chunks follow, chunk i of the walk
     // being (c0 + i) mod nit.
-    const int rot = (int)(((tile >> 3) & 3) * ((nround + 3) / 4) % nround);
+    const int rot = k1_round_rotation(tile, nround);
     const int c0 = rot * (RC / kIter);
     auto rnd = [&](int s_) { return (s_ + rot) % nround; };   // s_ < nround
 
@@ -1118,10 +1163,11 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 // Kernel 2, resident form (many tokens).  One workgroup per (channel range of
 // CH channels, residue class p of the token tiles modulo P).  The W_up rows of
 // the range (every branch, MFMA row order as above) and gamma/n are staged in
-// LDS once; the workgroup then walks the tiles p, p + P, ... in steps of 64
-// channels.  A step reads, per token and branch, one whole 128-byte line of
-// the state (its two 64-byte halves back to back) and writes one whole line of
-// u, so no line is fetched or written in halves.  The next step's state is
+// LDS once; the workgroup then walks the tiles p, p + P, ... (those kernel 1
+// wrote last first, see TileWalk) in steps of 64 channels.  A step reads, per
+// token and branch, one whole 128-byte line of the state (its two 64-byte
+// halves back to back) and writes one whole line of u, so no line is fetched
+// or written in halves.  The next step's state is
 // loaded branch by branch, each as soon as the current step has finished with
 // that branch: the prefetch costs no registers beyond one step's state.  The
 // activations and rms of the next tile are loaded before the state of its
@@ -1199,7 +1245,9 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
     bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
     float rms[NB], nrms[NB];
     u32x4 sv[NB][SC];
-    int64_t T = p;
+    const TileWalk walk = tile_walk(sh, p, P, tiles, c_begin);
+    int pass = 0;
+    int64_t T = walk.next(p, pass);                    // >= 0: p < tiles
     int st = 0;
     load_act(T, bop, bopl, rms);
 #pragma unroll
@@ -1228,9 +1276,9 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
 
     for (;;) {
         int64_t Tn = T;
-        int sn = st + 1;
-        if (sn == nsteps) { sn = 0; Tn = T + P; }
-        const bool more = Tn < tiles;
+        int sn = st + 1, pn = pass;
+        if (sn == nsteps) { sn = 0; Tn = walk.next(T + P, pn); }
+        const bool more = Tn >= 0;
         if (sn == 0 && more) load_act(Tn, nbop, nbopl, nrms);
 
         float uacc[SC][8];
@@ -1294,6 +1342,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
         }
         T = Tn;
         st = sn;
+        pass = pn;
     }
 }
 
@@ -1528,7 +1577,9 @@ k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__res
     bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
     float rms[NB], nrms[NB];
     u32x4 sv[NB];
-    int64_t T = p;
+    const TileWalk walk = tile_walk(sh, p, P, tiles, c_begin);
+    int pass = 0;
+    int64_t T = walk.next(p, pass);                    // >= 0: p < tiles
     int st = 0;
     load_act(T, bop, bopl, rms);
 #pragma unroll
@@ -1553,9 +1604,9 @@ k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__res
 
     for (;;) {
         int64_t Tn = T;
-        int sn = st + 1;
-        if (sn == nsteps) { sn = 0; Tn = T + P; }
-        const bool more = Tn < tiles;
+        int sn = st + 1, pn = pass;
+        if (sn == nsteps) { sn = 0; Tn = walk.next(T + P, pn); }
+        const bool more = Tn >= 0;
         if (sn == 0 && more) load_act(Tn, nbop, nbopl, nrms);
 
         float uacc[16];
@@ -1610,6 +1661,7 @@ k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__res
         }
         T = Tn;
         st = sn;
+        pass = pn;
     }
 }
 
