@@ -148,6 +148,18 @@ def test_kernel2_forms(N, d, r, w_std, form, monkeypatch):
     run_read_write_fused(X, f"{form}-N{N}-d{d}-r{r}")
 
 
+@pytest.mark.parametrize("N,d,r,dtype", [(4133, 4096, 64, "bf16"), (8250, 2048, 32, "fp8")])
+def test_resident_walk_order(N, d, r, dtype):
+    """Many tokens, every token compared: kernel 1 rotates its walk per token
+    tile (with channel splits at N = 4133), and each resident kernel-2
+    workgroup visits its tiles in two passes (recently written ones first);
+    with several tiles per workgroup from both passes and a ragged last tile,
+    a tile visited twice or not at all would show here."""
+    X = inputs.make_gr_inputs(N, 4, d, r, dtype, seed=11 * N + d + r, w_std=0.2,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"walk-N{N}-d{d}-r{r}-{dtype}")
+
+
 @pytest.mark.parametrize("N,d,r,w_std", [(64, 512, 32, 0.5), (130, 1024, 48, 0.3),
                                          (48, 4096, 64, 0.2)])
 def test_saturating_gate(N, d, r, w_std):
