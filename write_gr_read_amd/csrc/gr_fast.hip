@@ -103,6 +103,7 @@ constexpr bool kSmallK1 = GR_K1_SMALL;     // few tokens: kernel 1's few-token f
 #define GR_SMALL_BELOW 32
 #endif
 constexpr int kSmallBelow = GR_SMALL_BELOW;  // ... used while (token tiles) x n is below this
+constexpr int kSmallBelowWide = 16;          // ... for a wide gate
 #ifndef GR_SMALL_TARGET
 #define GR_SMALL_TARGET 256
 #endif
@@ -151,12 +152,12 @@ FastShape shape_of(const ReadArgs &a) {
     s.k2_chan = c2;
     s.wide = s.row_blocks > kMaxRowBlocks;
     s.prep = !s.wide && s.tiles >= kPrepMinTiles;
-    // Few tokens, narrow gate: kernel 1's few-token form, whose workgroups are
+    // Few tokens: kernel 1's few-token form (narrow or wide gate), whose workgroups are
     // (16 tokens, branch, split); splits (a power of two, at most kMaxSplit)
     // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
     s.small = false;
     s.small_kpw = 0;
-    if (kSmallK1 && !s.wide && s.tiles * s.n < kSmallBelow) {
+    if (kSmallK1 && s.tiles * s.n < (s.wide ? kSmallBelowWide : kSmallBelow)) {
         const int64_t groups = (s.N + 15) / 16;
         int sp = 1;
         while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
@@ -595,7 +596,10 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // bf16 hi + lo once per k-step as the B operand.  The waves' partial
 // projections and sums of squares are added in LDS in wave order and written as
 // the (token, branch, split) record that k_reduce_records expects.
-constexpr int kSmallKB = 4;               // k-steps loaded together (one batch)
+// k-steps loaded together (one batch): four, or one for a wide gate (its
+// NRB W fragments per k-step take 4 NRB VGPRs)
+template <int NRB> constexpr int small_kb() { return NRB <= kMaxRowBlocks ? 4 : 1; }
+constexpr int kSmallPass = kMaxRowBlocks;  // row blocks per pass of the LDS reduction
 template <bool FUSED, int NRB, bool F8>
 __global__ void __launch_bounds__(64 * kSmallWaves, 2)
 k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
@@ -604,8 +608,10 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
                     FastShape sh) {
     using T = typename StateT<F8>::type;
     using SV = typename StateT<F8>::vec8;
-    constexpr int ACC = NRB * 4;                          // accumulator words per lane
-    __shared__ float lds_p[kSmallWaves][ACC + 1][64];     // per wave: accumulators, then ss
+    constexpr int kSmallKB = small_kb<NRB>();
+    constexpr int PB = NRB < kSmallPass ? NRB : kSmallPass;   // row blocks per reduction pass
+    constexpr int NPASS = (NRB + PB - 1) / PB;
+    __shared__ float lds_p[kSmallWaves][4 * PB + 1][64];  // per wave: a pass's accumulators, then ss
     const int n = sh.n, d = sh.d, S = sh.ksplit, kpw = sh.small_kpw;
     // blockIdx -> (token group, branch, split) with (branch, split) fastest, so
     // the workgroups reading one slice of W sit on one XCD when n S % 8 == 0
@@ -691,22 +697,32 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
     // this wave's share of ss per token: the four lane groups hold its channels
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
+    // add the waves' accumulators in LDS, PB row blocks per pass (ss with the first)
 #pragma unroll
-    for (int k = 0; k < NRB; ++k)
+    for (int ps = 0; ps < NPASS; ++ps) {
+        constexpr int ACC = 4 * PB;                       // words per lane and pass
+        if (ps > 0) __syncthreads();                      // the previous pass is read
 #pragma unroll
-        for (int m = 0; m < 4; ++m) lds_p[wave][4 * k + m][lane] = acc[k][m];
-    lds_p[wave][ACC][lane] = ss;
-    __syncthreads();
-    // word j of lane l: P row 16(j/4) + 4(l/16) + j%4 of token l%16 (j < ACC), ss (j = ACC)
-    for (int v = tid; v < (ACC + 1) * 64; v += 64 * kSmallWaves) {
-        const int j = v >> 6, l = v & 63;
-        const int64_t tt = tg * 16 + (l & 15);
-        if (tt >= sh.N || (j == ACC && l >= 16)) continue;
-        float sum = 0.f;
+        for (int k = 0; k < PB; ++k)
 #pragma unroll
-        for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][j][l];
-        float *rec = ws.partial + ((tt * n + br) * S + split) * (int64_t)sh.pstride;
-        rec[j < ACC ? 4 + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3) : 0] = sum;
+            for (int m = 0; m < 4; ++m)
+                if (ps * PB + k < NRB) lds_p[wave][4 * k + m][lane] = acc[ps * PB + k][m];
+        if (ps == 0) lds_p[wave][ACC][lane] = ss;
+        __syncthreads();
+        // word j of lane l: P row 16(ps PB + j/4) + 4(l/16) + j%4 of token l%16
+        // (j < ACC), ss (j = ACC, first pass)
+        const int words = 4 * (ps * PB + PB <= NRB ? PB : NRB - ps * PB);   // P words of this pass
+        for (int v = tid; v < (ACC + 1) * 64; v += 64 * kSmallWaves) {
+            const int j = v >> 6, l = v & 63;
+            const int64_t tt = tg * 16 + (l & 15);
+            const bool is_ss = j == ACC;
+            if (tt >= sh.N || (is_ss ? (ps != 0 || l >= 16) : j >= words)) continue;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][j][l];
+            float *rec = ws.partial + ((tt * n + br) * S + split) * (int64_t)sh.pstride;
+            rec[is_ss ? 0 : 4 + 16 * (ps * PB + (j >> 2)) + 4 * (l >> 4) + (j & 3)] = sum;
+        }
     }
 }
 
@@ -1379,8 +1395,24 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
     using SV = typename StateT<F8>::vec8;              // 8 channels of the state
     const int grp = j / GS, side = j % GS, groups = wgs_per_xcd / GS;
     const int64_t tiles = (sh.N + kResTile - 1) / kResTile;
-    const int64_t ntx = tiles > xcd ? (tiles - xcd + 7) / 8 : 0;   // tiles xcd + 8k of this XCD
-    const int64_t units = (int64_t)(ranges / GS) * ntx;            // (range group, tile) units
+    const int rgs = ranges / GS;                       // range groups (GS ranges each)
+    // XCD x takes the tiles x, x + 8, ... and every range group; with fewer
+    // than 8 tiles, XCD x takes tile x % tiles and every reps-th range group
+    // from x / tiles, so that all XCDs work (reps = 8 / tiles)
+    int64_t ntx, tile0;
+    int rg0 = 0, rgstep = 1, nrg = rgs;
+    if (tiles >= 8) {
+        ntx = tiles > xcd ? (tiles - xcd + 7) / 8 : 0;
+        tile0 = xcd;
+    } else {
+        const int reps = 8 / (int)tiles;
+        ntx = xcd < tiles * reps ? 1 : 0;
+        tile0 = xcd % tiles;
+        rg0 = xcd / (int)tiles;
+        rgstep = reps;
+        nrg = rg0 < rgs ? (rgs - rg0 + reps - 1) / reps : 0;
+    }
+    const int64_t units = (int64_t)nrg * ntx;         // (range group, tile) units
     if (grp >= groups) return;                         // whole workgroup (the count's remainder idles)
     const int64_t u0 = units * grp / groups, u1 = units * (grp + 1) / groups;
     if (u0 >= u1) return;                              // whole workgroup
@@ -1388,8 +1420,8 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
     const int g = lane >> 4, m16 = lane & 15;
     const float inv_n = 1.0f / (float)NB;
 
-    auto unit_tile = [&](int64_t q) { return (int64_t)xcd + 8 * (q % ntx); };
-    auto unit_range = [&](int64_t q) { return GS * (int)(q / ntx) + side; };
+    auto unit_tile = [&](int64_t q) { return tile0 + 8 * (q % ntx); };
+    auto unit_range = [&](int64_t q) { return GS * (rg0 + rgstep * (int)(q / ntx)) + side; };
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
     auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
         const int64_t t = token(T);
@@ -1700,6 +1732,8 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
         break;
         switch (sh.row_blocks) {
             GR_K1S(1) GR_K1S(2) GR_K1S(3) GR_K1S(4) GR_K1S(5) GR_K1S(6) GR_K1S(7) GR_K1S(8)
+            GR_K1S(9) GR_K1S(10) GR_K1S(11) GR_K1S(12) GR_K1S(13) GR_K1S(14) GR_K1S(15)
+            GR_K1S(16) GR_K1S(17) GR_K1S(18) GR_K1S(19) GR_K1S(20) GR_K1S(21)
         default: return hipErrorInvalidValue;
         }
 #undef GR_K1S
