@@ -160,6 +160,19 @@ def test_resident_walk_order(N, d, r, dtype):
     run_read_write_fused(X, f"walk-N{N}-d{d}-r{r}-{dtype}")
 
 
+@pytest.mark.parametrize("N,d,r,w_std", [(37, 256, 16, 0.05), (300, 192, 32, 0.05), (257, 320, 128, 0.2),
+                                         (2500, 4096, 64, 0.05)])
+@pytest.mark.parametrize("form", ["staged", "resident"])
+def test_kernel2_forms_fp8(N, d, r, w_std, form, monkeypatch):
+    """Both kernel-2 forms on an e4m3 state (staged: 8 bytes per lane widened
+    to bf16 words; resident: 64-channel units), a ragged last range (d = 192,
+    320) and several tiles per workgroup (N = 2500)."""
+    monkeypatch.setenv("GR_KERNEL_VARIANT", form)
+    X = inputs.make_gr_inputs(N, 4, d, r, "fp8", seed=5 * N + d + r, w_std=w_std,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0))
+    run_read_write_fused(X, f"fp8-{form}-N{N}-d{d}-r{r}")
+
+
 @pytest.mark.parametrize("N,d,r,w_std", [(64, 512, 32, 0.5), (130, 1024, 48, 0.3),
                                          (48, 4096, 64, 0.2)])
 def test_saturating_gate(N, d, r, w_std):

@@ -300,6 +300,13 @@ __device__ __forceinline__ TileWalk tile_walk(const FastShape &sh, int64_t p, in
 template <bool F8> struct StateT { using type = bf16_t; using vec8 = u32x4; };
 template <> struct StateT<true> { using type = fp8_t; using vec8 = u32x2; };
 
+// Eight state values at p as four packed bf16 words (exact for e4m3).
+template <bool F8>
+__device__ __forceinline__ u32x4 load8_as_bf16(const typename StateT<F8>::type *p) {
+    if constexpr (F8) return widen8_fp8_bf16(*reinterpret_cast<const u32x2 *>(p));
+    else return *reinterpret_cast<const u32x4 *>(p);
+}
+
 // ---------------------------------------------------------------------------
 #ifndef GR_K1_WAVES_PER_SIMD
 #define GR_K1_WAVES_PER_SIMD 4
@@ -1013,9 +1020,9 @@ k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float ep
 // straight from the packed state.  Pipeline: the state of the chunk two ahead
 // and the W_up rows of the chunk after it are in flight while a chunk is
 // combined.
-template <int NB, int RKS>
+template <int NB, int RKS, bool F8>
 __global__ void __launch_bounds__(kK2Threads, kK2WavesPerSimd)
-k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
+k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
     constexpr int SUB = kK2Sub;                        // 32-channel chunks per iteration
@@ -1101,7 +1108,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
 #pragma unroll
     for (int i = 0; i < NB; ++i) rms[i] = valid ? ws.rms[t * NB + i] : 1.0f;
 
-    const bf16_t *srow = state + t * (int64_t)NB * d + 8 * g;
+    const typename StateT<F8>::type *srow = state + t * (int64_t)NB * d + 8 * g;
     bf16_t *urow = u + t * (int64_t)d + 8 * g;
     const int m16 = lane & 15;  // A row this lane feeds
 
@@ -1114,7 +1121,7 @@ k_gate_combine(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamm
                 const int c0 = c_begin + it * KC + sc * kChunk;
                 sv[sc][i] = u32x4{0u, 0u, 0u, 0u};
                 if (valid && it < nit && c0 < c_end)
-                    sv[sc][i] = *reinterpret_cast<const u32x4 *>(srow + (int64_t)i * d + c0);
+                    sv[sc][i] = load8_as_bf16<F8>(srow + (int64_t)i * d + c0);
             }
     };
 
@@ -1762,14 +1769,14 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     return hipGetLastError();
 }
 
-template <int NB>
+template <int NB, bool F8>
 hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     const int ranges = (sh.d + sh.k2_chan - 1) / sh.k2_chan;
     const unsigned grid = (unsigned)(((sh.N + kK2Tile - 1) / kK2Tile) * ranges);
 #define GR_K2(RKS)                                                                          \
     case RKS:                                                                               \
-        hipLaunchKernelGGL((k_gate_combine<NB, RKS>), dim3(grid), dim3(kK2Threads), 0, st,  \
-                           (const bf16_t *)a.state, (const bf16_t *)a.gamma,                \
+        hipLaunchKernelGGL((k_gate_combine<NB, RKS, F8>), dim3(grid), dim3(kK2Threads), 0, st, \
+                           (const typename StateT<F8>::type *)a.state, (const bf16_t *)a.gamma, \
                            (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);             \
         break;
     switch (sh.rk / 32) {
@@ -1881,6 +1888,7 @@ hipError_t launch_k2_resident(const ReadArgs &a, const FastShape &sh, const Work
 // The resident kernel 2 pays a one-off W_up staging per workgroup; it wins
 // once every workgroup walks a few token tiles.
 constexpr int64_t kResidentMinTokens = 4096;
+constexpr int64_t kResidentMinTokensFp8 = 1024;  // (e4m3: the staged form loses from ~1-2k tokens)
 // The XCD-aware walk of a wide gate's kernel 2 wants several tiles per XCD.
 constexpr int64_t kWideXcdMinTokens = 8 * 4 * kResTile;
 
@@ -1921,13 +1929,18 @@ hipError_t launch_read_fast(const ReadArgs &a, hipStream_t st) {
     default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // an e4m3 state: the resident form (narrow gate) or the XCD walk (wide gate)
-    if (a.fp8) return sh.rk > 128 ? launch_k2_wide<4, true>(a, sh, w, st) : launch_k2_resident_fp8<4>(a, sh, w, st);
+    // an e4m3 state: the staged form (few tokens) or the resident form (narrow
+    // gate), or the XCD walk (wide gate)
+    if (a.fp8) {
+        if (sh.rk > 128) return launch_k2_wide<4, true>(a, sh, w, st);
+        const bool res8 = a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokensFp8);
+        return res8 ? launch_k2_resident_fp8<4>(a, sh, w, st) : launch_k2<4, true>(a, sh, w, st);
+    }
     // a wide gate (more than four k-steps) has the resident form only, walked
     // XCD by XCD once every XCD has several token tiles
     if (sh.rk > 128 && sh.N >= kWideXcdMinTokens && a.k2_variant != 2) return launch_k2_wide<4, false>(a, sh, w, st);
     const bool resident = sh.rk > 128 || a.k2_variant == 2 || (a.k2_variant == 0 && sh.N >= kResidentMinTokens);
-    return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4>(a, sh, w, st);
+    return resident ? launch_k2_resident<4>(a, sh, w, st) : launch_k2<4, false>(a, sh, w, st);
 }
 
 }  // namespace grk
