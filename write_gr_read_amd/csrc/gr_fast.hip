@@ -56,14 +56,10 @@ constexpr int kTile = 16 * kWaves;        // tokens per workgroup
 constexpr int kChunk = 32;                // channels per MFMA k-step
 
 #ifndef GR_K1_DEPTH
-#define GR_K1_DEPTH 0             // many tokens (with the W' prep)
-#endif
-#ifndef GR_K1_DEPTH_SPLIT
-#define GR_K1_DEPTH_SPLIT 2       // few tokens: short channel splits need a deeper pipeline
+#define GR_K1_DEPTH 0
 #endif
 constexpr int kIter = 64;                 // channels per W' chunk of kernel 1 (a round is two)
-constexpr int kDepth = GR_K1_DEPTH;       // iterations of state / y loads in flight (with prep)
-constexpr int kDepthSplit = GR_K1_DEPTH_SPLIT;  // ... without (few tokens)
+constexpr int kDepth = GR_K1_DEPTH;       // kernel 1: rounds of state / y loads in flight ahead
 #ifndef GR_K1_TG
 #define GR_K1_TG 1
 #endif
@@ -91,14 +87,6 @@ constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgro
 #endif
 constexpr int kSplitTarget = GR_SPLIT_TARGET;  // kernel-1 workgroups wanted before splitting channels
 constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power of two)
-#ifndef GR_PREP_MIN_TILES
-#define GR_PREP_MIN_TILES 8
-#endif
-constexpr int kPrepMinTiles = GR_PREP_MIN_TILES;  // token tiles from which W' is split once per call
-#ifndef GR_K1_SMALL
-#define GR_K1_SMALL 1
-#endif
-constexpr bool kSmallK1 = GR_K1_SMALL;     // few tokens: kernel 1's few-token form
 #ifndef GR_SMALL_BELOW
 #define GR_SMALL_BELOW 32
 #endif
@@ -137,9 +125,9 @@ FastShape shape_of(const ReadArgs &a) {
     s.rk = (s.r + 31) / 32 * 32;
     s.N = a.N;
     s.tiles = (a.N + kTile - 1) / kTile;
-    // Enough workgroups to fill the GPU when N is small (decode): split the
-    // channels of kernel 1 (partial records are summed in the tile reduction)
-    // and narrow the channel range of kernel 2.
+    // Enough workgroups to fill the GPU below ~16k tokens: split the channels
+    // of kernel 1's tile walk (partial records are summed in the tile
+    // reduction) and narrow the channel range of the staged kernel 2.
     int ks = 1;
     while (s.tiles * s.n * ks < kSplitTarget && ks < kMaxSplit && (s.d / (ks * 2)) % kIter == 0 &&
            s.d / (ks * 2) >= 2 * kIter)
@@ -151,13 +139,12 @@ FastShape shape_of(const ReadArgs &a) {
     while (tiles2 * ((s.d + c2 - 1) / c2) < 1024 && c2 > kChunk && (c2 / 2) % kChunk == 0) c2 /= 2;
     s.k2_chan = c2;
     s.wide = s.row_blocks > kMaxRowBlocks;
-    s.prep = !s.wide && s.tiles >= kPrepMinTiles;
     // Few tokens: kernel 1's few-token form (narrow or wide gate), whose workgroups are
     // (16 tokens, branch, split); splits (a power of two, at most kMaxSplit)
     // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
     s.small = false;
     s.small_kpw = 0;
-    if (kSmallK1 && s.tiles * s.n < (s.wide ? kSmallBelowWide : kSmallBelow)) {
+    if (s.tiles * s.n < (s.wide ? kSmallBelowWide : kSmallBelow)) {
         const int64_t groups = (s.N + 15) / 16;
         int sp = 1;
         while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
@@ -166,8 +153,9 @@ FastShape shape_of(const ReadArgs &a) {
         s.ksplit = sp;
         s.ksplit_chan = 0;
         s.small_kpw = (s.d + per - 1) / per;
-        s.prep = false;
     }
+    // the tile walk of a narrow gate (at least 8 tiles) reads W' split once per call
+    s.prep = !s.wide && !s.small;
     return s;
 }
 
@@ -326,9 +314,8 @@ __device__ __forceinline__ u32x4 load8_as_bf16(const typename StateT<F8>::type *
 // lane / 16) is read.
 //
 // W' (W_down / W_write rows of the branch times gamma, as bf16 hi and lo
-// planes) is either formed here per 64-channel chunk (PREP = false) or read
-// ready-made from the workspace, where k_prep_wprime wrote it once for the
-// call (PREP = true: every token tile would otherwise redo the same split).
+// planes) is read ready-made from the workspace, where k_prep_wprime wrote it
+// once for the call (every token tile would otherwise redo the same split).
 // It is staged in a double-buffered LDS slot per chunk: the chunk after next
 // is loaded into registers while a chunk is used, with one barrier per chunk.
 // DEPTH > 0: DEPTH rounds of state / y loads are in flight ahead of the round
@@ -336,8 +323,8 @@ __device__ __forceinline__ u32x4 load8_as_bf16(const typename StateT<F8>::type *
 // element phase has freed their registers, so they fly during the MFMA phase
 // at no register cost; y (mostly an L2 hit: the n workgroups of a tile share
 // it) is loaded at the start of its round.
-template <bool FUSED, int NRB, int DEPTH, bool PREP, int TG, bool F8>
-__global__ void __launch_bounds__(64 * (kWaves / TG), (NRB <= 5 && TG == 1 && PREP) ? GR_K1_WAVES_PER_SIMD : 2)
+template <bool FUSED, int NRB, int DEPTH, int TG, bool F8>
+__global__ void __launch_bounds__(64 * (kWaves / TG), (NRB <= 5 && TG == 1) ? GR_K1_WAVES_PER_SIMD : 2)
 k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
@@ -350,8 +337,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     constexpr int KS = kIter / kChunk;                 // MFMA k-steps per W' chunk
     constexpr int kPitch = kIter + 8;                  // bf16 per staged W' row
     constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per chunk (per plane)
-    constexpr int WV = PREP ? (2 * NV + THREADS - 1) / THREADS  // hi and lo planes, ready-made
-                            : (NV + THREADS - 1) / THREADS;     // W and gamma, split here
+    constexpr int WV = (2 * NV + THREADS - 1) / THREADS;  // hi and lo planes
     constexpr int NSLOT = DEPTH + 1;
     using T = typename StateT<F8>::type;
     using SV = typename StateT<F8>::vec8;              // 8 channels of the state
@@ -389,56 +375,29 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     const int c0 = rot * (RC / kIter);
     auto rnd = [&](int s_) { return (s_ + rot) % nround; };   // s_ < nround
 
-    // W' staging.  PREP: vector v < NV of the hi plane, NV + v of the lo plane.
-    // Else: row j < r from W_down, rows r..r+nw-1 from W_write, the rest zero;
-    // times gamma of branch br; split into bf16 hi and lo planes here.
-    u32x4 wreg[WV], greg[PREP ? 1 : WV];
+    // W' staging: vector v < NV of the hi plane, NV + v of the lo plane
+    u32x4 wreg[WV];
     auto chunk_of = [&](int it) { const int c_ = c0 + it; return c_ >= nit ? c_ - nit : c_; };  // it < nit
     auto load_w = [&](int it) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * THREADS;
-            if (PREP) {
-                const int plane = v / NV, rem = v % NV;
-                const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
-                wreg[q] = u32x4{0u, 0u, 0u, 0u};
-                if (v < 2 * NV && it < nit)
-                    wreg[q] = *reinterpret_cast<const u32x4 *>(
-                        ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + chunk_of(it) * kIter + cv * 8);
-            } else {
-                const int row = v / (kIter / 8), cv = v % (kIter / 8);
-                const bf16_t *src = nullptr;
-                if (v < NV && it < nit) {
-                    if (row < sh.r) src = wd + (int64_t)row * nd;
-                    else if (row < sh.rows) src = ww + (int64_t)(row - sh.r) * nd;
-                }
-                if (src) {
-                    const int64_t col = (int64_t)br * d + c_base + chunk_of(it) * kIter + cv * 8;
-                    wreg[q] = *reinterpret_cast<const u32x4 *>(src + col);
-                    greg[PREP ? 0 : q] = *reinterpret_cast<const u32x4 *>(gamma + col);
-                } else {
-                    wreg[q] = u32x4{0u, 0u, 0u, 0u};
-                    greg[PREP ? 0 : q] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
+            const int plane = v / NV, rem = v % NV;
+            const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
+            wreg[q] = u32x4{0u, 0u, 0u, 0u};
+            if (v < 2 * NV && it < nit)
+                wreg[q] = *reinterpret_cast<const u32x4 *>(
+                    ws.wprime + ((int64_t)(br * 2 + plane) * rows_p + row) * d + c_base + chunk_of(it) * kIter + cv * 8);
         }
     };
     auto store_w = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * THREADS;
-            if (PREP) {
-                if (v < 2 * NV) {
-                    const int plane = v / NV, rem = v % NV;
-                    const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
-                    *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + cv * 8]) = wreg[q];
-                }
-            } else if (v < NV) {
-                const int row = v / (kIter / 8), cv = v % (kIter / 8);
-                u32x4 hi, lo;
-                split_product(wreg[q], greg[PREP ? 0 : q], hi, lo);
-                *reinterpret_cast<u32x4 *>(&lds_w[buf][0][row * kPitch + cv * 8]) = hi;
-                *reinterpret_cast<u32x4 *>(&lds_w[buf][1][row * kPitch + cv * 8]) = lo;
+            if (v < 2 * NV) {
+                const int plane = v / NV, rem = v % NV;
+                const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
+                *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + cv * 8]) = wreg[q];
             }
         }
     };
@@ -1720,14 +1679,9 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     }
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
-        if (sh.prep)                                                                        \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, true, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
-                               (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
-                               (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
-        else                                                                                \
-            hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepthSplit, false, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
-                               (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,       \
-                               (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh); \
+        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
+                           (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,                \
+                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
         break;
     if (sh.small) {
         const unsigned sgrid = (unsigned)(((sh.N + 15) / 16) * sh.n * sh.ksplit);
