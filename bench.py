@@ -91,6 +91,7 @@ def cpu_baseline(Xin, threads, n_tokens):
     import numpy as np
     import oracle
     p0, p1 = Xin.params
+    n_tokens = min(n_tokens, Xin.N)
     R = Xin.X[:n_tokens].double().numpy()
     y = Xin.y[:n_tokens].double().numpy()
     _, s0 = oracle.read(Xin.X[:1], p0.gamma, p0.w_down, p0.w_up, p0.w_write)
@@ -103,7 +104,7 @@ def cpu_baseline(Xin, threads, n_tokens):
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fused write+read of the first {n_tokens} of {Xin.N} prefill tokens "
                       f"(fp64 C oracle, {threads} threads over disjoint token ranges, "
-                      f"{dt:.2f} s wall)"}
+                      f"{dt:.2f} s wall, ~{dt * threads:.0f} thread-seconds)"}
 
 
 def timed(fn, steps, warmup, stream):
@@ -342,7 +343,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens of the workload the CPU baseline runs (about 20 thread-seconds at 16384)")
     ap.add_argument("--copy-probe", action="store_true", help="also time the copy probe")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm",
