@@ -462,6 +462,20 @@ def test_add_rmsnorm_workload():
         check(f"addnorm out {N}x{d}", out, o, dt)
 
 
+@pytest.mark.parametrize("N,d,dt,alias", [(1500, 4096, "bf16", False), (2049, 2048, "f32", False),
+                                         (3001, 8192, "bf16", True), (1100, 16384, "bf16", False)])
+def test_add_rmsnorm_walk(N, d, dt, alias):
+    """The persistent add + RMSNorm (above 1024 tokens): every token compared,
+    token counts that are not multiples of the grid, every rows-per-thread
+    count, and out written over y (the one aliasing the call allows)."""
+    B = inputs.make_addnorm_inputs(N, d, dt, seed=3 * N + d)
+    x, y = B.x.to(DEV), B.y.to(DEV)
+    out = gr.residual_add_rmsnorm(x, y, B.w.to(DEV), out=y if alias else None)
+    h, o = oracle.add_rmsnorm(B.x, B.y, B.w, B.eps, dt)
+    check(f"addnorm-walk h {N}x{d}", x, h, dt)
+    check(f"addnorm-walk out {N}x{d}", out, o, dt)
+
+
 def gpu_chain(Xin):
     X = Xin.X.to(DEV)
     ps = [dev_params(p) for p in Xin.params]

@@ -239,6 +239,90 @@ k_add_rmsnorm(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ 
     }
 }
 
+// Persistent form for rows of at most 2048 vectors (d <= 16384 bf16): four
+// workgroups per CU walk the tokens t = blockIdx, blockIdx + grid, ..., so the
+// grid sweeps memory as one narrow front; w stays in registers, and the next
+// token's x and y are loaded while the current token's sum of squares is
+// reduced.  x and y are read and h written with non-temporal hints (streamed
+// once; h is used again only after the sublayer), out with ordinary stores (the
+// sublayer reads it next): 51 -> 43.5 us at N = 8192, d = 4096 bf16, where all
+// non-temporal gives 45.7 us and none 51 us.  Same arithmetic, in the same
+// order, as k_add_rmsnorm.
+template <typename T, int KPT>
+__global__ void __launch_bounds__(256)
+k_add_rmsnorm_walk(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ w, float eps,
+                   T *out, int d, int64_t N) {
+    constexpr int VEC = 16 / sizeof(T);
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int dv = d / VEC;
+    u32x4 wv[KPT], xv[KPT], yv[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+        const int cv = tid + k * 256;
+        wv[k] = cv < dv ? *reinterpret_cast<const u32x4 *>(w + cv * VEC) : u32x4{0u, 0u, 0u, 0u};
+    }
+    auto load = [&](int64_t t) {
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int cv = tid + k * 256;
+            if (t < N && cv < dv) {
+                xv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(x + t * d + cv * VEC));
+                yv[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + t * d + cv * VEC));
+            }
+        }
+    };
+    int64_t t = blockIdx.x;
+    load(t);
+    for (; t < N; t += gridDim.x) {
+        u32x4 h[KPT];
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int cv = tid + k * 256;
+            if (cv >= dv) continue;
+            u32x4 hv;
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hv[e] = pack_bf16x2(bf16_lo(xv[k][e]) + bf16_lo(yv[k][e]), bf16_hi(xv[k][e]) + bf16_hi(yv[k][e]));
+                    const float a = bf16_lo(hv[e]), b = bf16_hi(hv[e]);
+                    ss = fmaf(a, a, ss);
+                    ss = fmaf(b, b, ss);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float hf = __uint_as_float(xv[k][e]) + __uint_as_float(yv[k][e]);
+                    hv[e] = __float_as_uint(hf);
+                    ss = fmaf(hf, hf, ss);
+                }
+            }
+            __builtin_nontemporal_store(hv, reinterpret_cast<u32x4 *>(x + t * d + cv * VEC));
+            h[k] = hv;
+        }
+        load(t + gridDim.x);   // the next token's rows fly during the reduction
+        const float inv = 1.0f / sqrtf(block_sum(ss, red) / (float)d + eps);
+#pragma unroll
+        for (int k = 0; k < KPT; ++k) {
+            const int cv = tid + k * 256;
+            if (cv >= dv) continue;
+            u32x4 ov;
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ov[e] = pack_bf16x2(bf16_lo(wv[k][e]) * bf16_lo(h[k][e]) * inv,
+                                        bf16_hi(wv[k][e]) * bf16_hi(h[k][e]) * inv);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ov[e] = __float_as_uint(__uint_as_float(wv[k][e]) * __uint_as_float(h[k][e]) * inv);
+            }
+            *reinterpret_cast<u32x4 *>(out + t * d + cv * VEC) = ov;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Measurement support: y = 0.1 tanh(u) elementwise; plain 16-byte copy.
 template <typename T>
@@ -307,9 +391,19 @@ hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, b
     return hipGetLastError();
 }
 
+#ifndef GR_ADDNORM_WALK
+#define GR_ADDNORM_WALK 1
+#endif
 template <typename T, int KPT>
 static void add_rmsnorm_k(void *x, const void *y, const void *w, float eps, void *out,
                           int64_t N, int d, hipStream_t st) {
+    if constexpr (KPT > 0) {
+        if (GR_ADDNORM_WALK && N > 1024) {
+            hipLaunchKernelGGL((k_add_rmsnorm_walk<T, KPT>), dim3(1024), dim3(256), 0, st, (T *)x,
+                               (const T *)y, (const T *)w, eps, (T *)out, d, N);
+            return;
+        }
+    }
     hipLaunchKernelGGL((k_add_rmsnorm<T, KPT>), dim3((unsigned)N), dim3(256), 0, st, (T *)x,
                        (const T *)y, (const T *)w, eps, (T *)out, d);
 }
