@@ -62,7 +62,8 @@ typedef enum gr_dtype {
     GR_FP8_E4M3 = 2   /* fp8 branch state (OCP e4m3, values saturate at +-448;
                          "Paper reading: Qwen3.8 Flash Next", part 2 Residual,
                          sec. 7 names an FP8 state), bf16 y, u, gains and
-                         weights, fp32 accumulation.  Read, write and fused only. */
+                         weights, fp32 accumulation.  Not for
+                         residual_add_rmsnorm or the tanh stand-in. */
 } gr_dtype;
 
 typedef enum gr_status {
@@ -186,7 +187,9 @@ gr_status gr_write_per_channel(void *state, const void *y, const float *s, gr_dt
 gr_status gr_collapse(const void *state, const void *w, float eps, void *out, gr_dtype dt, int64_t N,
                       int32_t n, int32_t d, void *stream);
 
-/* Bytes of workspace `op` needs for N tokens of layer L (may be 0).
+/* Bytes of workspace `op` needs for N tokens of layer L (may be 0), for that
+ * layer as given: with or without W_write the layout differs, so query with
+ * the layer the call will use.
  * The workspace needs no initialisation: a call writes every byte it reads.
  * Calls that share a workspace must not run concurrently (same stream, or
  * synchronised). */
