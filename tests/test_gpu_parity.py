@@ -101,7 +101,7 @@ def test_fp8_state_shapes(N, n, d, r, path, monkeypatch):
     u at the bf16 tolerance).  "default" takes the MFMA kernels wherever the
     shape allows (n = 4, r a multiple of 16, d a multiple of 64), including a
     last channel range of one 64-channel unit (d = 192, 320), every k-step
-    count of the up projection and the channel-split kernel 1 of few tokens;
+    count of the up projection and the few-token kernel 1;
     "generic" forces the shape-generic kernels on the same shapes."""
     if path == "generic":
         monkeypatch.setenv("GR_KERNEL_VARIANT", "generic")

@@ -4,14 +4,16 @@
 // eq:write first when fused; sec. 7: read fused into one traversal with Group
 // RMSNorm, and the FP8 state).
 //
-// Four kernels in stream order, no inter-workgroup waiting (so no
-// co-residency assumption).  Below, the narrow-gate (r + n <= 128) forms;
-// an e4m3 state uses the same kernel 1 template and its own kernel 2
-// (k_gate_combine_resident_fp8), and a wide gate (r up to 320, the pages'
-// r = d/8 at d = 2560) has its own kernel 1 and 2 (k_stream_proj_wide,
-// k_gate_combine_wide), each described where it is defined.
+// Up to four kernels in stream order, no inter-workgroup waiting (so no
+// co-residency assumption).  Below, the narrow-gate (r + n <= 128) forms at
+// many tokens; an e4m3 state uses the same kernel 1 template and its own
+// resident kernel 2 (k_gate_combine_resident_fp8), a wide gate (r up to 320,
+// the pages' r = d/8 at d = 2560) has its own kernel 1 and 2
+// (k_stream_proj_wide, k_gate_combine_wide), and below 1024 tokens (512 for a
+// wide gate) kernel 1 is k_stream_proj_small; each is described where it is
+// defined.
 //
-// k_prep_wprime   (many tokens) W' = (W_down ; W_write) . gamma per branch,
+// k_prep_wprime   (tile walk) W' = (W_down ; W_write) . gamma per branch,
 //                 split once into bf16 hi / lo planes for the whole call.
 // k_stream_proj   one workgroup per (token tile of 16*WAVES tokens, branch i).
 //                 Streams branch i of the tile once: (fused) R' = R + s_i y in
