@@ -438,6 +438,34 @@ def test_real_shape_fp8_full_sampled():
     sampled_read_parity(Xin, sample_tokens(Xin.N, 64, seed=8), "fp8-d2560-r320-16384")
 
 
+def test_state_beyond_2_31_elements():
+    """N x n x d above 2^31 elements (131372 x 4 x 4096 bf16, a 4.3 GB state):
+    kernel 1's tile walk, kernel 2's resident walk and the record reduction
+    address past 32-bit element offsets.  Tokens sampled on both sides of the
+    boundary (token 131072 starts at element 2^31) are compared with the
+    oracle, which gets those rows of the same device tensors."""
+    N, n, d, r = 131372, 4, 4096, 64
+    P = inputs.make_gr_inputs(1, n, d, r, "bf16", seed=91, n_param_sets=2).params
+    X, y = inputs.make_device_state(N, n, d, "bf16", seed=92, device=DEV)
+    idx = np.unique(np.concatenate([[0, 1, 65535, 131070, 131071, 131072, 131073, N - 2, N - 1],
+                                    sample_tokens(N, 24, seed=93)]))
+    ti = torch.from_numpy(idx).to(DEV)
+    Xs, ys = X[ti].cpu(), y[ti].cpu()
+    u0, s0 = gr.read(X, dev_params(P[0]))
+    ou0, os0, A0 = orc_read(Xs, P[0], "bf16")
+    check("2^31 read u (sampled)", u0[ti].cpu(), ou0, "bf16", scale=A0)
+    check("2^31 read s (sampled)", s0[ti].cpu(), os0, "bf16")
+    s_in = s0.clone()
+    s_in[ti] = torch.from_numpy(os0).float().to(DEV)
+    u1, s1 = gr.fused_write_read(X, y, s_in, dev_params(P[1]))
+    oR, ou1, os1, A1 = orc_fused(Xs, ys, os0, P[1], "bf16")
+    check_exact("2^31 fused state (sampled)", X[ti].cpu(), oR)
+    check("2^31 fused u (sampled)", u1[ti].cpu(), ou1, "bf16", scale=A1)
+    check("2^31 fused s (sampled)", s1[ti].cpu(), os1, "bf16")
+    del X, y, u0, u1
+    torch.cuda.empty_cache()
+
+
 def test_decode_workload():
     """Workload 4 (N=256), every token."""
     run_read_write_fused(inputs.workload(4), "decode-256")

@@ -207,6 +207,25 @@ def make_variant_inputs(N: int, n: int, d: int, dtype: str = "bf16", seed: int =
     return VariantInputs(N, n, d, dtype, X, e, y, h, s, w)
 
 
+def make_device_state(N: int, n: int, d: int, dtype: str = "bf16", seed: int = 0, device="cuda:0",
+                      x_std: float = 1.0, y_std: float = 0.05,
+                      branch_scale: Optional[Sequence[float]] = (1.0, 0.5, 2.0, 1.0)):
+    """State [N, n, d] and y [N, d] drawn on ``device`` with torch's seeded
+    generator of that device: for sizes whose host-side draw would be slow
+    (billions of values).  Same distributions as make_gr_inputs; a test hands
+    the oracle the rows it samples from these very tensors."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    X = torch.randn((N, n, d), generator=g, device=device, dtype=torch.float32).mul_(x_std)
+    if branch_scale is not None:
+        X.mul_(torch.tensor(branch_scale[:n], device=device, dtype=torch.float32).view(1, n, 1))
+    if _dtype(dtype) == torch.float8_e4m3fn:
+        X.clamp_(-448.0, 448.0)
+    X = X.to(_dtype(dtype))
+    y = torch.randn((N, d), generator=g, device=device, dtype=torch.float32).mul_(y_std)
+    return X, y.to(_dtype(param_dtype(dtype)))
+
+
 # The synthetic workloads, by number. Seed of workload k is 1000*k.
 WORKLOADS = {
     1: dict(name="gr_tiny_f32", kind="gr", N=64, n=4, d=256, r=16, dtype="f32",
