@@ -57,7 +57,7 @@ def gate_flops(N, n, d, r, has_write=True):
 
 # The files holding the kernels of gr_fused_write_read (the MFMA path and its
 # device helpers); stored counters apply while these are unchanged.
-FUSED_KERNEL_SOURCES = ("gr_device.h", "gr_fast.hip")
+FUSED_KERNEL_SOURCES = ("gr_device.h", "gr_fast_common.h", "gr_fast.hip", "gr_fast_k1.hip", "gr_fast_k2.hip")
 
 
 def kernel_source_digest():
