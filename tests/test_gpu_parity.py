@@ -558,6 +558,37 @@ def test_chain_workload_full_sampled():
     check_chain("chain-full final state (sampled)", R[idx], oR, chain_scale(Xin.X[idx], ss, ys))
 
 
+def test_concurrent_streams_keep_separate_workspaces():
+    """Two fused calls in flight at once on two streams (default priority),
+    each with its own inputs and, through the binding, its own workspace:
+    every result equals the same call made alone, bit for bit.  A shared
+    workspace would mix the two calls' records."""
+    A = inputs.make_gr_inputs(4500, 4, 2048, 64, "bf16", seed=31, branch_scale=(1.0, 0.5, 2.0, 1.0))
+    B = inputs.make_gr_inputs(700, 4, 2048, 64, "bf16", seed=32, branch_scale=(1.0, 0.5, 2.0, 1.0))
+    runs = []
+    for Xin in (A, B):
+        p = dev_params(Xin.params[1])
+        R = Xin.X.to(DEV)
+        s_in = torch.full((Xin.N, 4), 0.9, device=DEV)
+        u, s = gr.fused_write_read(R, Xin.y.to(DEV), s_in, p)        # alone, current stream
+        torch.cuda.synchronize()
+        runs.append((Xin, p, s_in, R, u, s))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (Xin, p, s_in, _, _, _), st in zip(runs, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            R = Xin.X.to(DEV, non_blocking=False)
+            y = Xin.y.to(DEV)
+            for _ in range(3):                                        # several calls queued per stream
+                Rc = R.clone()
+                u, s = gr.fused_write_read(Rc, y, s_in, p)
+            outs.append((Rc, u, s))
+    torch.cuda.synchronize()
+    for (_, _, _, R1, u1, s1), (R2, u2, s2) in zip(runs, outs):
+        assert torch.equal(R1, R2) and torch.equal(u1, u2) and torch.equal(s1, s2)
+
+
 def test_graph_replay_matches_eager():
     """The fused call captured in a HIP graph (torch.cuda.CUDAGraph) and
     replayed three times, with eager work and synchronisations in between:
