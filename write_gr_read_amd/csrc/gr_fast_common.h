@@ -12,7 +12,6 @@
 namespace grk {
 namespace fast {
 
-
 constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16 * kWaves;        // tokens per workgroup
@@ -53,14 +52,13 @@ constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power
 #ifndef GR_SMALL_BELOW
 #define GR_SMALL_BELOW 32
 #endif
-constexpr int kSmallBelow = GR_SMALL_BELOW;  // ... used while (token tiles) x n is below this
+constexpr int kSmallBelow = GR_SMALL_BELOW;  // few-token kernel 1 while (token tiles) x n is below this
 constexpr int kSmallBelowWide = 16;          // ... for a wide gate
 #ifndef GR_SMALL_TARGET
 #define GR_SMALL_TARGET 256
 #endif
 constexpr int kSmallTarget = GR_SMALL_TARGET;  // few-token kernel 1: workgroups wanted before splitting
 constexpr int kSmallWaves = 8;            // waves per few-token kernel-1 workgroup
-
 
 struct FastShape {
     int n, d, r, nw;     // nw = n if W_write given, else 0
