@@ -265,6 +265,26 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     }
 }
 
+// The up projection's B operand for token t (-log2(e) a as bf16 hi and lo
+// words, lane group g's eight of each k-step) and 1/rho of its branches.  A
+// token past the end of a ragged last tile reads the last token's values
+// instead: its u is never stored, and loads without a condition let the
+// compiler keep them in flight (a conditional load with a default value was
+// merged at once, a wait for every load in flight at each tile change).
+template <int NB, int RKS>
+__device__ __forceinline__ void load_act_rms(const Workspace &ws, const FastShape &sh, int64_t t, int g,
+                                             bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
+    constexpr int RK = RKS * 32;
+    if (t >= sh.N) t = sh.N - 1;
+#pragma unroll
+    for (int ks = 0; ks < RKS; ++ks) {
+        hi[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g));
+        lo[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g));
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rm[i] = ws.rms[t * NB + i];
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 2, resident form (many tokens).  One workgroup per (channel range of
 // CH channels, residue class p of the token tiles modulo P).  The W_up rows of
@@ -323,20 +343,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
 
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
     auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
-        const int64_t t = token(T);
-        const bool ok = t < sh.N;
-#pragma unroll
-        for (int ks = 0; ks < RKS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-            if (ok) {
-                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
-                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
-            }
-            hi[ks] = as_bf16x8(v);
-            lo[ks] = as_bf16x8(vl);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+        load_act_rms<NB, RKS>(ws, sh, token(T), g, hi, lo, rm);
     };
     // state of branch i, step st of tile T: SC 16-byte words per lane
     auto load_state = [&](int64_t T, int st, int i, u32x4 (&sv)[SC]) {
@@ -514,20 +521,7 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
     auto unit_range = [&](int64_t q) { return GS * (rg0 + rgstep * (int)(q / ntx)) + side; };
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
     auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
-        const int64_t t = token(T);
-        const bool ok = t < sh.N;
-#pragma unroll
-        for (int ks = 0; ks < RKS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-            if (ok) {
-                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
-                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
-            }
-            hi[ks] = as_bf16x8(v);
-            lo[ks] = as_bf16x8(vl);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+        load_act_rms<NB, RKS>(ws, sh, token(T), g, hi, lo, rm);
     };
     // state of branch i, range rg of tile T: 8 channels per lane
     auto load_state = [&](int64_t T, int rg, int i) {
@@ -673,20 +667,7 @@ k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__res
 
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
     auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
-        const int64_t t = token(T);
-        const bool ok = t < sh.N;
-#pragma unroll
-        for (int ks = 0; ks < RKS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-            if (ok) {
-                v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
-                vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
-            }
-            hi[ks] = as_bf16x8(v);
-            lo[ks] = as_bf16x8(vl);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) rm[i] = ok ? ws.rms[t * NB + i] : 1.0f;
+        load_act_rms<NB, RKS>(ws, sh, token(T), g, hi, lo, rm);
     };
     // e4m3 word of branch i, step st of tile T
     auto load_state = [&](int64_t T, int st, int i) {
