@@ -135,9 +135,9 @@ def test_workspace_query_and_check(L):
 
 def test_workspace_size_follows_the_write_projection(L):
     """r = 128 with W_write is a wide gate (132 projection rows, no W' planes);
-    without W_write it is narrow (128 rows), and from 1024 tokens its W' hi / lo
-    planes (n x 2 x 128 x d bf16) are part of the workspace: the query sizes the
-    call as it will be made."""
+    without W_write it is narrow (128 rows), and with 8 token tiles or more
+    (1024 tokens here) its W' hi / lo planes (n x 2 x 128 x d bf16) are part of
+    the workspace: the query sizes the call as it will be made."""
     d = 4096
     sizes = {}
     for ww in (FAKE, None):

@@ -186,12 +186,13 @@ def test_saturating_gate(N, d, r, w_std):
     run_read_write_fused(X, f"saturating-N{N}-d{d}-r{r}")
 
 
-@pytest.mark.parametrize("N,d,r", [(511, 1024, 48), (512, 4096, 64), (1000, 1024, 32), (1024, 2048, 64),
-                                   (2065, 1024, 16), (3000, 4096, 64)])
+@pytest.mark.parametrize("N,d,r", [(511, 1024, 48), (512, 4096, 64), (896, 1024, 32), (897, 1024, 32),
+                                   (1000, 1024, 32), (1024, 2048, 64), (2065, 1024, 16), (3000, 4096, 64)])
 def test_kernel1_forms_by_token_count(N, d, r):
-    """Kernel 1 takes its few-token form below 1024 tokens (n = 4) and the tile
-    walk with channel splits above, until the grid is full; both sides of each
-    switch, ragged tails, every token compared."""
+    """Kernel 1 takes its few-token form with fewer than 8 tiles of 128 tokens
+    (N <= 896, n = 4) and the tile walk with channel splits from there, until
+    the grid is full; both sides of each switch, ragged tails, every token
+    compared."""
     X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=7 * N + d + r, w_std=0.2,
                               branch_scale=(1.0, 0.5, 2.0, 1.0))
     run_read_write_fused(X, f"k1-forms-N{N}-d{d}-r{r}")

@@ -12,9 +12,9 @@
 // many tokens; an e4m3 state uses the same kernel 1 template and its own
 // resident kernel 2 (k_gate_combine_resident_fp8), a wide gate (r up to 320,
 // the pages' r = d/8 at d = 2560) has its own kernel 1 and 2
-// (k_stream_proj_wide, k_gate_combine_wide), and below 1024 tokens (512 for a
-// wide gate) kernel 1 is k_stream_proj_small; each is described where it is
-// defined.
+// (k_stream_proj_wide, k_gate_combine_wide), and with fewer than 8 token tiles
+// of 128 (N <= 896; fewer than 4, N <= 384, for a wide gate) kernel 1 is
+// k_stream_proj_small; each is described where it is defined.
 //
 // k_prep_wprime   (tile walk) W' = (W_down ; W_write) . gamma per branch,
 //                 split once into bf16 hi / lo planes for the whole call.
