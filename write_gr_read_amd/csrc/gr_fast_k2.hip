@@ -14,13 +14,14 @@ namespace {
 // splits (rho_i, rms_i; shared by shuffles), and each lane owns outputs
 // j = lane, lane + 64, ...: the split sums of P_i[j] for every branch (lanes
 // read consecutive j: coalesced), rho applied, summed over branches in order.
-// The loads of the sums of squares and of the first two outputs per lane go
-// out together, so a call of few tokens waits for memory once.
+// The loads of the sums of squares and of the first JO outputs per lane go
+// out together (JO = 2, or 6 for a wide gate's up to 384 outputs with at most
+// two splits), so a wave waits for memory once.
 //   j < r        z = (1/n) sum_i rho_i P_i[j]  ->  -log2(e) SiLU(z) as (hi, lo)
 //   r <= j < rk  zero padding of the up projection's k-steps
 //   rk + i       s_i = 2 sigmoid((1/n) sum_i' rho_i' P_i'[r + i])  (1 without W_write)
 constexpr int kRedWaves = 4;
-template <int NB, int S>
+template <int NB, int S, int JO>
 __global__ void __launch_bounds__(64 * kRedWaves)
 k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float eps) {
     const int lane = threadIdx.x & 63;
@@ -47,17 +48,21 @@ k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float ep
         if (j < sh.rk) return j < sh.r ? j : -1;
         return sh.nw ? sh.r + (j - sh.rk) : -1;
     };
+    // (no row: output j is past the end, a zero pad, or s = 1 without W_write,
+    // none of which uses the sums, so row 0, present in every record, is read;
+    // loads without a condition all go out before the first wait)
     auto gather = [&](int j, float (&p)[NB]) {
         const int row = j < outs ? prow(j) : -1;
+        const int rr = row >= 0 ? row : 0;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) p[i] = row >= 0 ? split_sum(i, 4 + row) : 0.f;
+        for (int i = 0; i < NB; ++i) p[i] = split_sum(i, 4 + rr);
     };
     // one round of loads: the sums of squares with the rows of the lane's
-    // first two outputs (none of them waits for rho)
-    const float ss_l = lane < NB ? split_sum(lane, 0) : 0.f;
-    float pa[NB], pb[NB];
-    gather(lane, pa);
-    gather(lane + 64, pb);
+    // first JO outputs (none of them waits for rho)
+    const float ss_l = split_sum(lane < NB ? lane : 0, 0);   // used by lanes < NB
+    float pj[JO][NB];
+#pragma unroll
+    for (int q = 0; q < JO; ++q) gather(lane + 64 * q, pj[q]);
     float rho_l = 0.f;
     if (lane < NB) {
         const float rms = sqrtf(ss_l / (float)sh.d + eps);
@@ -82,9 +87,10 @@ k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float ep
             s_out[t * NB + i] = sh.nw ? 2.0f * sigmoid_f(z * inv_n) : 1.0f;
         }
     };
-    if (lane < outs) emit(lane, pa);
-    if (lane + 64 < outs) emit(lane + 64, pb);
-    for (int j = lane + 128; j < outs; j += 64) {
+#pragma unroll
+    for (int q = 0; q < JO; ++q)
+        if (lane + 64 * q < outs) emit(lane + 64 * q, pj[q]);
+    for (int j = lane + 64 * JO; j < outs; j += 64) {
         float p[NB];
         gather(j, p);
         emit(j, p);
@@ -895,12 +901,21 @@ constexpr int64_t kWideXcdMinTokens = 8 * 4 * kResTile;
 
 hipError_t launch_reduce(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     const dim3 rgrid((unsigned)((sh.N + kRedWaves - 1) / kRedWaves)), rblock(64 * kRedWaves);
+    // a wide gate's records (more than 128 outputs) with one or two splits: all
+    // of a lane's outputs in one round of loads
+    const bool wide = sh.rk + 4 > 128;
     switch (sh.ksplit) {
-    case 1: hipLaunchKernelGGL((k_reduce_records<4, 1>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 2: hipLaunchKernelGGL((k_reduce_records<4, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 4: hipLaunchKernelGGL((k_reduce_records<4, 4>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 8: hipLaunchKernelGGL((k_reduce_records<4, 8>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 16: hipLaunchKernelGGL((k_reduce_records<4, 16>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 1:
+        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 1, 6>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        else hipLaunchKernelGGL((k_reduce_records<4, 1, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        break;
+    case 2:
+        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 2, 6>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        else hipLaunchKernelGGL((k_reduce_records<4, 2, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        break;
+    case 4: hipLaunchKernelGGL((k_reduce_records<4, 4, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 8: hipLaunchKernelGGL((k_reduce_records<4, 8, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 16: hipLaunchKernelGGL((k_reduce_records<4, 16, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
