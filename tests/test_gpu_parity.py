@@ -222,14 +222,15 @@ def test_workspace_needs_no_initialisation():
 
 @pytest.mark.parametrize("N,d,r,w_std", [
     (1, 2560, 320, 0.05), (64, 2560, 320, 0.05), (37, 512, 144, 0.05), (130, 1024, 256, 0.2),
-    (300, 640, 320, 0.05), (129, 2560, 160, 0.3), (200, 448, 224, 0.5),
+    (300, 640, 320, 0.05), (129, 2560, 160, 0.3), (200, 448, 224, 0.5), (2500, 256, 320, 0.2),
 ])
 def test_wide_gate_shapes(N, d, r, w_std):
     """Gate ranks beyond 124 (r + n > 128 projection rows): kernel 1's wide
     form (raw weights in LDS, gamma . R' split into hi / lo on the state side)
     and kernel 2's 32-channel resident form.  Ragged token tiles, channel
-    splits at few tokens (N = 1, 64), r from 144 to 320, and large weights
-    (w_std = 0.5) so the gate spans (0, 1)."""
+    splits at few tokens (N = 1, 64) and in the tile walk (N = 2500: four
+    splits, whose record reduction gathers a lane's outputs in rounds), r from
+    144 to 320, and large weights (w_std = 0.5) so the gate spans (0, 1)."""
     X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=13 * N + d + r, w_std=w_std,
                               branch_scale=(1.0, 0.5, 2.0, 1.0))
     run_read_write_fused(X, f"wide-N{N}-d{d}-r{r}")
