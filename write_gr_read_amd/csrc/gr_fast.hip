@@ -80,14 +80,14 @@ FastShape shape_of(const ReadArgs &a) {
     // Few tokens: kernel 1's few-token form (narrow or wide gate), whose workgroups are
     // (16 tokens, branch, split); splits (a power of two, at most kMaxSplit)
     // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
-    s.small = false;
+    s.small = 0;
     s.small_kpw = 0;
     if (s.tiles * s.n < (s.wide ? kSmallBelowWide : kSmallBelow)) {
         const int64_t groups = (s.N + 15) / 16;
         int sp = 1;
         while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
         const int per = kSmallWaves * kChunk * sp;   // channels covered per k-step of every wave
-        s.small = true;
+        s.small = 1;
         s.ksplit = sp;
         s.ksplit_chan = 0;
         s.small_kpw = (s.d + per - 1) / per;

@@ -69,9 +69,12 @@ struct FastShape {
     int ksplit_chan;     // channels per split (multiple of kIter)
     int k2_chan;         // channels per kernel-2 workgroup (multiple of kChunk)
     int rk;              // r padded to a multiple of 32 (k-steps of the up projection)
-    bool prep;           // W' split once per call by k_prep_wprime (enough token tiles)
-    bool wide;           // r + n beyond 128: kernel 1's wide form (gamma on the state side, no W')
-    bool small;          // few tokens: kernel 1's few-token form (k_stream_proj_small)
+    // flags as 32-bit ints: every field of the struct, a kernel argument, is
+    // then dword-aligned and read through the scalar cache (a bool pair at an
+    // odd offset took a vector load and a wait at kernel start)
+    int prep;            // W' split once per call by k_prep_wprime (enough token tiles)
+    int wide;            // r + n beyond 128: kernel 1's wide form (gamma on the state side, no W')
+    int small;           // few tokens: kernel 1's few-token form (k_stream_proj_small)
     int small_kpw;       // ... its k-steps (32 channels) per wave
     int64_t N, tiles;
 };
