@@ -2,8 +2,10 @@
 // call): the W' preparation and the three forms of kernel 1 -- the tile walk
 // (k_stream_proj), the few-token form (k_stream_proj_small) and the wide-gate
 // form (k_stream_proj_wide).  Each streams the state once: eq:write when fused,
-// the sums of squares, and the down / write projections on MFMA, ending in
-// per-(token, branch, split) records.
+// the sums of squares of eq:rms, and the down and write projections of eq:gate
+// and eq:s on MFMA, ending in per-(token, branch, split) records ("Paper
+// reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4; one traversal per
+// direction as in its sec. 7).
 #include "gr_fast_common.h"
 
 namespace grk {

@@ -1,8 +1,10 @@
 // gr_fast_k2.hip -- the rest of the fast path's call (see gr_fast.hip): the
-// reduction of kernel 1's records (rho, the SiLU activations, the write
-// strengths) and the forms of kernel 2 (up projection on MFMA, sigmoid gate,
-// gated combine): staged (few tokens), resident (many tokens), resident for an
-// e4m3 state, and the XCD walk of a wide gate; and which form a call takes.
+// reduction of kernel 1's records (rho of eq:rms, the SiLU activations of
+// eq:gate, the write strengths of eq:s) and the forms of kernel 2 (up
+// projection on MFMA, sigmoid gate of eq:gate, gated combine of eq:use_gate;
+// "Paper reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4): staged (few
+// tokens), resident (many tokens), resident for an e4m3 state, and the XCD
+// walk of a wide gate; and which form a call takes.
 #include "gr_fast_common.h"
 
 namespace grk {
