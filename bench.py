@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU baseline (default: the host's, at most 16)")
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens of the workload the CPU baseline runs (about 20 thread-seconds at 16384)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -452,7 +454,7 @@ def main():
         del a, b
 
     if not args.no_cpu:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        threads = args.cpu_threads or max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"CPU baseline: oracle on {args.cpu_tokens} tokens, {threads} threads ...")
         out["cpu_baseline"] = cpu_baseline(Xin, threads, args.cpu_tokens)
         log(f"CPU baseline: {out['cpu_baseline']['value']:.0f} tokens/s")
