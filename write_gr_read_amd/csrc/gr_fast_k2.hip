@@ -7,6 +7,8 @@
 // walk of a wide gate; and which form a call takes.
 #include "gr_fast_common.h"
 
+#include <atomic>
+
 namespace grk {
 namespace fast {
 namespace {
@@ -836,17 +838,18 @@ hipError_t launch_k2_resident_fp8(const ReadArgs &a, const FastShape &sh, const 
     }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; calls may come from
+// several threads, so the cache entries are atomics: a race only repeats the query).
 int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 template <int NB, int RKS, bool F8>
