@@ -80,7 +80,14 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     constexpr int RC = 2 * kIter;                      // channels per round
     constexpr int PCS = RC / 8;                        // 16-byte pieces per token row and round
     constexpr int KS = kIter / kChunk;                 // MFMA k-steps per W' chunk
-    constexpr int kPitch = kIter + 8;                  // bf16 per staged W' row
+    // A staged W' row is kIter bf16 = eight 16-byte pieces, with piece p of row
+    // `row` stored at p ^ ((row >> 1) & 7): the MFMA A reads (16 rows, one
+    // piece each per lane group) then hit distinct banks, where a padded pitch
+    // of 144 bytes still conflicted (~2e7 conflict cycles per call).  Rows
+    // m16 and m16 + 16 k share the swizzle.
+    constexpr int kPitch = kIter;                      // bf16 per staged W' row
+    auto swz = [](int row) { return (row >> 1) & 7; };
+    static_assert(kIter / 8 == 8, "the W' swizzle permutes eight 16-byte pieces per row");
     constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per chunk (per plane)
     constexpr int WV = (2 * NV + THREADS - 1) / THREADS;  // hi and lo planes
     constexpr int NSLOT = DEPTH + 1;
@@ -142,7 +149,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
             if (v < 2 * NV) {
                 const int plane = v / NV, rem = v % NV;
                 const int row = rem / (kIter / 8), cv = rem % (kIter / 8);
-                *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + cv * 8]) = wreg[q];
+                *reinterpret_cast<u32x4 *>(&lds_w[buf][plane][row * kPitch + (cv ^ swz(row)) * 8]) = wreg[q];
             }
         }
     };
@@ -243,8 +250,9 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 #pragma unroll
                     for (int tg = 0; tg < TG; ++tg)
                         bop[tg] = as_bf16x8(my_r[(16 * tg + m16) * RP + pc]);
-                    const bf16_t *wh = &lds_w[cur][0][m16 * kPitch + ks * kChunk + 8 * g];
-                    const bf16_t *wl = &lds_w[cur][1][m16 * kPitch + ks * kChunk + 8 * g];
+                    const int pw = ((ks * kChunk / 8 + g) ^ swz(m16)) * 8;   // swizzled piece
+                    const bf16_t *wh = &lds_w[cur][0][m16 * kPitch + pw];
+                    const bf16_t *wl = &lds_w[cur][1][m16 * kPitch + pw];
 #pragma unroll
                     for (int k = 0; k < NRB; ++k) {
                         const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kPitch);
