@@ -14,14 +14,17 @@
  * sec. 2 and 3).  The pages fuse the read into one kernel and the write into
  * another (same paper reading, sec. 7).  This library computes s inside the
  * read (it depends only on R-hat, which the read holds) and hands it to the
- * write, and adds a fused write(l)+read(l+1) call so the widened state makes
- * one HBM round trip per sublayer.  The n = 1 degenerate case is the fused
+ * write, and adds a fused write(l)+read(l+1) call, so the write's output is
+ * read back without a separate call.  The n = 1 degenerate case is the fused
  * residual add + RMSNorm of "Residual" (LLM inference), sec. 3.3.
  *
  * Conventions shared by every call
  *   Memory     All tensor pointers are DEVICE pointers owned by the caller;
  *              the library keeps no reference after a call returns.  Scratch
- *              memory comes only from the caller's workspace argument.
+ *              memory comes from the caller's workspace argument, except on
+ *              the single-pass path (GR_KERNEL_VARIANT=single, below), which
+ *              exchanges partial sums through a library-owned device array
+ *              of ~11 MB per GPU and allocates nothing.
  *   Layout     Contiguous, row-major: state [N][n][d] (token, branch,
  *              channel); y, u [N][d]; s [N][n] (always fp32); gamma [n][d];
  *              W_down [r][n*d]; W_up [n*d][r]; W_write [n][n*d].  The vec()
@@ -113,8 +116,16 @@ gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int6
 
 /*
  * gr_fused_write_read -- gr_write of sublayer l, then gr_read of sublayer
- * l+1 with `next`, on the STORED (rounded) state, in one pass over it.
- * Results equal gr_write followed by gr_read (state bit for bit).
+ * l+1 with `next`, on the STORED (rounded) state.  Results equal gr_write
+ * followed by gr_read (state bit for bit).  The default kernels pass over
+ * the state twice: the first forms and stores R' together with its
+ * projections, the second reads R' back for the gated combine (28 d bytes
+ * per token with a bf16 state, where one pass would move 20 d).  With
+ * GR_KERNEL_VARIANT=single (n = 4, bf16 state, d = 4096 or 2048,
+ * 16 <= r <= 64, r % 16 == 0, a GPU of 8 XCDs x 32 CUs) one persistent
+ * kernel keeps R' on chip between the two and reads the state once; it is
+ * currently slower than the default, see gr_device_error_word for its
+ * diagnostic, and calls of it on one GPU run one after the other.
  *   state  in/out [N][n][d];  y in [N][d];  s_in in [N][n] fp32
  *   u_next out [N][d];  s_next out [N][n] fp32
  *   workspace >= gr_workspace_size(GR_OP_FUSED_WRITE_READ, ...) bytes
@@ -194,6 +205,13 @@ gr_status gr_collapse(const void *state, const void *w, float eps, void *out, gr
  * Calls that share a workspace must not run concurrently (same stream, or
  * synchronised). */
 gr_status gr_workspace_size(int op, gr_dtype dt, int64_t N, const gr_layer *L, size_t *bytes);
+
+/* Diagnostic of the single-pass path (GR_KERNEL_VARIANT=single): *word
+ * receives the current GPU's device error word of that path -- bit 0 is set
+ * when one of its bounded waits on another workgroup timed out, after which
+ * the call's outputs are not to be trusted -- and is cleared when reset != 0.
+ * Synchronous (copies one word from the device).  0 when the path is unused. */
+gr_status gr_device_error_word(uint32_t *word, int reset);
 
 /* Static description of a status code. */
 const char *gr_status_string(gr_status status);

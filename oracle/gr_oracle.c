@@ -183,11 +183,14 @@ int gro_read(int64_t N, int n, int d, int r, double eps, int dtype,
  * GR write for N tokens  [QFN eq:write; NOTES sec. 3]:
  *   R'_i = R_i + s_i * y, the same y into every branch, stored in place.
  *   R [N][n][d] in/out, y [N][d], s [N][n].
- * The pages fix no precision for forming R + s y before it is stored, so the
- * rounding is taken in the kernels' precision: the sum (exact in fp64 here
- * whenever it can matter) is rounded to fp32 -- what one fp32 fused
- * multiply-add delivers -- and that fp32 value is stored, i.e. rounded again
- * to the storage dtype.
+ * The pages fix no precision for forming R + s y before it is stored; the
+ * workloads state their arithmetic as a bf16 (or e4m3) state with fp32
+ * accumulation, and adding s y into the state is that accumulation.  So the
+ * sum (exact in fp64 here whenever it can matter) is rounded to fp32 -- what
+ * one fp32 fused multiply-add delivers -- and that fp32 value is stored, i.e.
+ * rounded again to the storage dtype.  Where this differs from one rounding
+ * of the exact sum (the fp32 value sits exactly on a rounding midpoint of the
+ * storage dtype) the two differ by one unit in the last place.
  */
 int gro_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
               const double *s)

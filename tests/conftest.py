@@ -23,3 +23,27 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Margins of the GPU parity checks run in this session (tests/parity.py):
+    the worst max|g-o|/RMS(o) and relative L2 error per dtype, and the checks
+    with elements past the A13 bound when the combine scale A is left out."""
+    try:
+        from parity import RECORDS
+    except ImportError:
+        return
+    if not RECORDS:
+        return
+    tr = terminalreporter
+    tr.section("parity margins")
+    for dt in sorted({r[1] for r in RECORDS}):
+        rs = [r for r in RECORDS if r[1] == dt]
+        worst_rms = max(rs, key=lambda r: r[2])
+        worst_l2 = max(rs, key=lambda r: r[3])
+        tr.write_line(f"{dt}: {len(rs)} checks; worst max|g-o|/RMS {worst_rms[2]:.3e} ({worst_rms[0]}); "
+                      f"worst relative L2 {worst_l2[3]:.3e} ({worst_l2[0]})")
+    strict = [r for r in RECORDS if r[4] > 0]
+    tr.write_line(f"checks with elements past 2e-2*max(|o|, RMS/16) (no combine scale): {len(strict)}")
+    for r in strict[:40]:
+        tr.write_line(f"  {r[0]}: {r[4]} of {r[5]}")

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["read", "write", "fused_write_read", "residual_add_rmsnorm", "tanh_standin",
-           "copy", "workspace_size", "library_path", "GRError"]
+           "copy", "workspace_size", "library_path", "device_error_word", "GRError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgr.so")
@@ -77,13 +77,15 @@ def lib():
         L.gr_collapse.argtypes = [P, P, F, P, ctypes.c_int, I64, I32, I32, P]
         L.gr_bench_tanh_standin.argtypes = [P, P, ctypes.c_int, I64, P]
         L.gr_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
+        L.gr_device_error_word.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
         L.gr_status_string.argtypes = [ctypes.c_int]
         L.gr_status_string.restype = ctypes.c_char_p
         L.gr_last_error.argtypes = []
         L.gr_last_error.restype = ctypes.c_char_p
         for f in ("gr_read", "gr_write", "gr_fused_write_read", "residual_add_rmsnorm",
                   "gr_workspace_size", "gr_bench_tanh_standin", "gr_bench_copy", "gr_expand",
-                  "gr_static_read", "gr_round_robin_write", "gr_write_per_channel", "gr_collapse"):
+                  "gr_static_read", "gr_round_robin_write", "gr_write_per_channel", "gr_collapse",
+                  "gr_device_error_word"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -178,6 +180,14 @@ def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
 
 
 # ------------------------------------------------------------------ public API
+
+def device_error_word(reset: bool = False) -> int:
+    """The single-pass path's device error word on the current GPU (bit 0: a
+    bounded wait on another workgroup timed out).  Synchronous."""
+    w = ctypes.c_uint32(0)
+    _call("gr_device_error_word", ctypes.byref(w), 1 if reset else 0)
+    return w.value
+
 
 def read(state: torch.Tensor, layer, eps: float = 1e-6, u: Optional[torch.Tensor] = None,
          s: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:

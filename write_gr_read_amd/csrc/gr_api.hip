@@ -92,7 +92,9 @@ gr_status check_layer(const gr_layer *L, gr_dtype dt, const char *fn) {
 
 // GR_KERNEL_VARIANT selects kernels for A/B checks: "generic" forces the
 // shape-generic kernels; "staged" / "resident" force that form of the fast
-// path's second kernel whatever the token count.
+// path's second kernel whatever the token count; "single" takes the
+// single-pass cluster kernel where the shape allows it (n = 4, d = 4096 or
+// 2048, 16 <= r <= 64 with r % 16 == 0, bf16 state).
 bool force_generic() {
     const char *v = getenv("GR_KERNEL_VARIANT");
     return v && strcmp(v, "generic") == 0;
@@ -111,6 +113,7 @@ size_t read_workspace(gr_dtype dt, int64_t N, const gr_layer *L) {
     a.fp8 = dt == GR_FP8_E4M3;
     a.N = N; a.n = L->n; a.d = L->d; a.r = L->r;
     a.ww = L->w_write;
+    if (grk::cluster_path_ok(a)) return 0;   // single pass: exchange in the library's own device array
     return grk::fast_path_ok(a) && !force_generic() ? grk::fast_workspace_bytes(a) : 0;
 }
 
@@ -131,6 +134,7 @@ gr_status run_read(grk::ReadArgs &a, const gr_layer *L, size_t ws_bytes, hipStre
     }
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     a.k2_variant = k2_variant();
+    if (grk::cluster_path_ok(a)) return launched(grk::launch_cluster(a, st), fn);
     if (grk::fast_path_ok(a) && !force_generic()) return launched(grk::launch_read_fast(a, st), fn);
     return launched(grk::launch_read_generic(a, st), fn);
 }
@@ -196,6 +200,14 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
     fill_layer(a, next);
     a.u = u_next; a.s_out = s_next; a.ws = workspace; a.ws_bytes = ws_bytes;
     return run_read(a, next, ws_bytes, (hipStream_t)stream, fn);
+}
+
+gr_status gr_device_error_word(uint32_t *word, int reset) {
+    const char *fn = "gr_device_error_word";
+    if (!word) return fail(GR_ERROR_INVALID_VALUE, "%s: word is NULL", fn);
+    hipError_t e = grk::cluster_error_word(word, reset != 0);
+    if (e != hipSuccess) return fail(GR_ERROR_LAUNCH, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
 }
 
 gr_status gr_write(void *state, const void *y, const float *s, gr_dtype dt, int64_t N, int32_t n,

@@ -166,7 +166,7 @@ k_write_fp8(fp8_t *__restrict__ state, const bf16_t *__restrict__ y, const float
 // KPT == 0: any width, h is re-read (each thread only its own chunks).
 template <typename T, int KPT>
 __global__ void __launch_bounds__(256)
-k_add_rmsnorm(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ w, float eps,
+k_add_rmsnorm(T *__restrict__ x, const T *y, const T *__restrict__ w, float eps,
               T *out, int d) {
     constexpr int VEC = 16 / sizeof(T);
     __shared__ float red[4];
@@ -247,10 +247,11 @@ k_add_rmsnorm(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ 
 // once; h is used again only after the sublayer), out with ordinary stores (the
 // sublayer reads it next): 51 -> 43.5 us at N = 8192, d = 4096 bf16, where all
 // non-temporal gives 45.7 us and none 51 us.  Same arithmetic, in the same
-// order, as k_add_rmsnorm.
+// order, as k_add_rmsnorm.  y is not restrict-qualified in either form:
+// the call allows out == y.
 template <typename T, int KPT>
 __global__ void __launch_bounds__(256)
-k_add_rmsnorm_walk(T *__restrict__ x, const T *__restrict__ y, const T *__restrict__ w, float eps,
+k_add_rmsnorm_walk(T *__restrict__ x, const T *y, const T *__restrict__ w, float eps,
                    T *out, int d, int64_t N) {
     constexpr int VEC = 16 / sizeof(T);
     __shared__ float red[4];

@@ -46,6 +46,12 @@ hipError_t launch_write_per_channel(void *state, const void *y, const float *s, 
 hipError_t launch_collapse(const void *state, const void *w, float eps, void *out, int dt, int64_t N, int n,
                            int d, hipStream_t st);
 
+// Single-pass cluster path (gr_cluster.hip): n = 4, bf16 or e4m3 state,
+// d = 4096 (r <= 64) or d = 2048 (r <= 32), on an 8-XCD gfx950 GPU.
+bool cluster_path_ok(const ReadArgs &a);
+hipError_t launch_cluster(const ReadArgs &a, hipStream_t st);
+hipError_t cluster_error_word(uint32_t *word, bool reset);
+
 // MFMA fast path for the bf16 widened state (gr_fast.hip).
 bool fast_path_ok(const ReadArgs &a);
 size_t fast_workspace_bytes(const ReadArgs &a);   // workspace bytes of this call's fast path
