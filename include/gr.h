@@ -135,6 +135,23 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
                               void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * gr_fused_write_read_noalloc -- gr_fused_write_read for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): same arguments without the workspace.
+ * The scratch memory its kernels need comes from a library-owned device array
+ * of 48 MiB per GPU (enough for 16384 tokens at d = 4096, n = 4, r = 64), set
+ * up on the first call on each GPU and held until the process ends; the call
+ * itself allocates nothing.  A call whose scratch would exceed 48 MiB returns
+ * GR_ERROR_WORKSPACE before any launch.  Every call on one GPU shares that
+ * array (the kernels write every byte they read, so nothing needs clearing),
+ * so calls that overlap in time on one GPU -- on different streams without
+ * ordering -- race and must not be made.
+ */
+gr_status gr_fused_write_read_noalloc(void *state, const void *y, const float *s_in, gr_dtype dt,
+                                      int64_t N, const gr_layer *next, void *u_next, float *s_next,
+                                      void *stream);
+
+/*
  * residual_add_rmsnorm -- n = 1 fused residual add + RMSNorm ("Residual",
  * LLM inference, sec. 3.3): h = x + y stored in place of x, then
  * out = w (.) h / sqrt(mean(h^2) + eps), the mean taken over the stored h.

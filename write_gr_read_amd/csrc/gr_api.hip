@@ -10,6 +10,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gr.h"
 #include "gr_internal.h"
 
@@ -154,6 +156,36 @@ gr_status check_variant(gr_dtype dt, int64_t N, int32_t n, int32_t d, const char
     return GR_SUCCESS;
 }
 
+// Scratch of gr_fused_write_read_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = 48ull << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchPtr {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+constexpr int kMaxScratchDevices = 64;
+ScratchPtr g_scratch[kMaxScratchDevices];
+
+// Device address of the current GPU's `scratch` (set up on its first use).
+hipError_t scratch_ptr(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    ScratchPtr &sp = g_scratch[dev];
+    std::call_once(sp.once, [&] {
+        sp.err = hipGetSymbolAddress(&sp.ptr, HIP_SYMBOL(scratch));
+        if (sp.err == hipSuccess && !sp.ptr) sp.err = hipErrorInvalidSymbol;
+    });
+    *ptr = sp.ptr;
+    return sp.err;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +232,41 @@ gr_status gr_fused_write_read(void *state, const void *y, const float *s_in, gr_
     fill_layer(a, next);
     a.u = u_next; a.s_out = s_next; a.ws = workspace; a.ws_bytes = ws_bytes;
     return run_read(a, next, ws_bytes, (hipStream_t)stream, fn);
+}
+
+gr_status gr_fused_write_read_noalloc(void *state, const void *y, const float *s_in, gr_dtype dt,
+                                      int64_t N, const gr_layer *next, void *u_next, float *s_next,
+                                      void *stream) {
+    const char *fn = "gr_fused_write_read_noalloc";
+    gr_status st;
+    if ((st = check_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_layer(next, dt, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) ||
+        (st = check_ptr(s_in, "s_in", fn)) || (st = check_ptr(u_next, "u_next", fn)) ||
+        (st = check_ptr(s_next, "s_next", fn)))
+        return st;
+    const size_t need = read_workspace(dt, N, next);
+    if (need > kNoAllocScratchBytes)
+        return fail(GR_ERROR_WORKSPACE,
+                    "%s: this call needs %zu bytes of scratch, more than the %zu bytes of the "
+                    "library's static array (use gr_fused_write_read with a workspace, or fewer tokens)",
+                    fn, need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        (void)hipGetLastError();
+        hipError_t e = scratch_ptr(&ws);
+        if (e != hipSuccess) return fail(GR_ERROR_LAUNCH, "%s: scratch set-up failed: %s", fn, hipGetErrorString(e));
+    }
+    grk::ReadArgs a{};
+    a.bf16 = dt != GR_F32;
+    a.fp8 = dt == GR_FP8_E4M3;
+    a.fused = true;
+    a.state = state; a.y = y; a.s_in = s_in;
+    a.N = N;
+    fill_layer(a, next);
+    a.u = u_next; a.s_out = s_next; a.ws = ws; a.ws_bytes = kNoAllocScratchBytes;
+    return run_read(a, next, kNoAllocScratchBytes, (hipStream_t)stream, fn);
 }
 
 gr_status gr_device_error_word(uint32_t *word, int reset) {
