@@ -86,8 +86,21 @@ def stored_traffic(kernel_name):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(Xin, threads, n_tokens):
-    """The oracle (plain fp64 C) on a bounded sample of the same workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(Xin, threads, n_tokens, single_tokens=1024):
+    """The oracle (plain fp64 C) on a bounded sample of the same workload:
+    `threads` threads over disjoint token ranges, and one thread on the first
+    `single_tokens` tokens."""
     import numpy as np
     import oracle
     p0, p1 = Xin.params
@@ -101,10 +114,16 @@ def cpu_baseline(Xin, threads, n_tokens):
     t0 = time.perf_counter()
     oracle.parallel_tokens(fn, [R, y, s_in], threads)
     dt = time.perf_counter() - t0
+    m = min(single_tokens, n_tokens)
+    t1 = time.perf_counter()
+    fn(R[:m], y[:m], s_in[:m])
+    dt1 = time.perf_counter() - t1
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fused write+read of the first {n_tokens} of {Xin.N} prefill tokens "
                       f"(fp64 C oracle, {threads} threads over disjoint token ranges, "
-                      f"{dt:.2f} s wall, ~{dt * threads:.0f} thread-seconds)"}
+                      f"{dt:.2f} s wall, ~{dt * threads:.0f} thread-seconds)",
+            "cpu_model": cpu_model(), "cores_in_affinity_mask": len(os.sched_getaffinity(0)),
+            "single_thread": {"value": m / dt1, "unit": "tokens/s", "tokens": m, "seconds": dt1}}
 
 
 def timed(fn, steps, warmup, stream):
@@ -257,18 +276,27 @@ def bench_other(which, args, dev):
         # the variants on the widened state at the prefill shape, bf16: one line each
         N, n, d = 16384, 4, 4096
         V = inputs.make_variant_inputs(N, n, d, "bf16", seed=8000, branch_scale=(1.0, 0.5, 2.0, 1.0))
-        X, e, y = V.X.to(dev), V.e.to(dev), V.y.to(dev)
         h, sc, w = V.h.to(dev), V.s.to(dev), V.w.to(dev)
-        u = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
-        st = torch.empty_like(X)
+        # three buffer sets rotate between calls, so a call's footprint (up to
+        # 640 MiB) is not left in the 256 MB Infinity Cache by the previous call
+        sets = [dict(X=V.X.to(dev), e=V.e.to(dev), y=V.y.to(dev),
+                     u=torch.empty((N, d), dtype=torch.bfloat16, device=dev),
+                     st=torch.empty((N, n, d), dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+        rot = {"i": 0}
+        def rotating(f):
+            def call():
+                b = sets[rot["i"] % 3]
+                rot["i"] += 1
+                f(b)
+            return call
         steps = args.steps if args.steps_given else 50
         ops = {
-            "expand": (lambda: gr.expand(e, n, state=st), N * d * 2 + N * n * d * 2),
-            "static_read": (lambda: gr.static_read(X, h, u=u), N * n * d * 2 + N * d * 2),
-            "round_robin_write": (lambda: gr.round_robin_write(X, y, 1), 3 * N * d * 2),
-            "write_per_channel": (lambda: gr.write_per_channel(X, y, sc),
+            "expand": (rotating(lambda b: gr.expand(b["e"], n, state=b["st"])), N * d * 2 + N * n * d * 2),
+            "static_read": (rotating(lambda b: gr.static_read(b["X"], h, u=b["u"])), N * n * d * 2 + N * d * 2),
+            "round_robin_write": (rotating(lambda b: gr.round_robin_write(b["X"], b["y"], 1)), 3 * N * d * 2),
+            "write_per_channel": (rotating(lambda b: gr.write_per_channel(b["X"], b["y"], sc)),
                                   2 * N * n * d * 2 + N * d * 2 + n * d * 4),
-            "collapse": (lambda: gr.collapse(X, w, out=u), N * n * d * 2 + N * d * 2 + d * 2),
+            "collapse": (rotating(lambda b: gr.collapse(b["X"], w, out=b["u"])), N * n * d * 2 + N * d * 2 + d * 2),
         }
         lines = []
         for name, (fn, alg) in ops.items():
@@ -277,7 +305,7 @@ def bench_other(which, args, dev):
             lines.append(line(f"GR variant {name} tokens/s (N={N}, d={d}, n={n}, bf16 state)",
                               N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
                               {"workload": f"variant_{name}", "N": N, "d": d, "n": n,
-                               "state_dtype": "bf16"},
+                               "state_dtype": "bf16", "buffer_sets": 3},
                               roofline=roofline(alg, ms, f"gr_{name}")))
         return lines
     if which == "addnorm":
@@ -350,6 +378,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="time the copy probe beside the headline (the default; kept for older command lines)")
     ap.add_argument("--no-copy-probe", action="store_true", help="skip the copy probe")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the decode / add+RMSNorm / chain / single-pass keys of the default line")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm",
                              "chain", "tiny", "variants", "all"])
@@ -453,7 +483,29 @@ def main():
         log(f"copy probe: {out['copy_probe_GBps']:.0f} GB/s (read + write of 1 GiB)")
         del a, b
 
+    if not args.no_others:
+        # the other configurations of the workload set, one key each with its
+        # own roofline: decode (us/call), the n = 1 fused add + RMSNorm, the
+        # 32-sublayer chain, and the single-pass kernel on this same prefill call
+        others = {}
+        for w in ("decode", "addnorm", "chain"):
+            log(f"workload {w} ...")
+            res = bench_other(w, args, dev)
+            keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
+                    "warm", "cold", "graph_replay_us_per_call", "gr_ms_per_pass", "f_standin_ms_per_pass")
+            others[w] = {k: res[k] for k in keep if k in res}
+        os.environ["GR_KERNEL_VARIANT"] = "single"
+        try:
+            ms1 = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next), args.steps, args.warmup, stream)
+        finally:
+            del os.environ["GR_KERNEL_VARIANT"]
+        others["prefill_single_pass"] = {"value": N / (ms1 * 1e-3), "unit": "tokens/s", "ms_per_step": ms1,
+                                         "roofline": roofline(alg, ms1, "gr_fused_write_read (GR_KERNEL_VARIANT=single)")}
+        log(f"single-pass kernel on the prefill call: {ms1 * 1e3:.1f} us/call")
+        out["other_workloads"] = others
+
     if not args.no_cpu:
+        # 16 threads: the host CPU share of one GPU on the measurement machines
         threads = args.cpu_threads or max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"CPU baseline: oracle on {args.cpu_tokens} tokens, {threads} threads ...")
         out["cpu_baseline"] = cpu_baseline(Xin, threads, args.cpu_tokens)

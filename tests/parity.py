@@ -2,16 +2,13 @@
 
 Tolerances (written here, used by every GPU parity test):
   * fp32 state:  max |g - o| <= 1e-5 * RMS(o), per output tensor.
-  * bf16 state:  |g - o| <= 2e-2 * max(|o|, A, RMS(o)/16) element by element,
-    fp32 accumulation on the GPU.  A is the condition scale of the element:
-    for u, the sum of the absolute values of the terms of the n-branch
-    combine, (1/n) sum_i |G_i R-hat_i| (eq:use_gate); for a chained state,
-    |R^(0)| + sum_u |s^(u) y^(u)| (eq:rcv).  A comes from the oracle's own
-    intermediates.  Reason: u is an n-term sum that may cancel; the GPU forms
-    it in fp32 from fp32 gate values (hi/lo bf16 operands on MFMA) and rounds
-    once, so its error is a small multiple of fp32 rounding of the TERMS, not
-    of the result, plus one bf16 ulp of the result.  Where no A is given the
-    RMS(o)/16 floor applies.  Also reported: max|g-o|/RMS(o) and the relative L2 error.
+  * bf16 state (and u / y with an e4m3 state):
+    |g - o| <= 2e-2 * max(|o|, RMS(o)/16) element by element (the per-element
+    relative bound with a floor near zero), and relative L2 error
+    ||g - o|| / ||o|| <= 4e-3, with fp32 accumulation on the GPU.  Also
+    reported: max|g-o|/RMS(o).  (An earlier form also allowed the combine's
+    term scale (1/n) sum_i |G_i R-hat_i| in the per-element bound; measured on
+    every GPU check, no element needed it, so it is gone.)
   * written state (eq:write): bit for bit (check_exact).  Both sides form
     R + s y in fp32 (the exact value rounded once, as one fp32 FMA does) and
     store that rounded to the state dtype.
@@ -20,7 +17,9 @@ Tolerances (written here, used by every GPU parity test):
     sides (a pre-rounding difference of 1e-7 lands on a bf16 rounding
     boundary) moves that element by one ulp for good; such flips cascade
     through y = F(u).  So: every element within 6e-2 * max(|o|, A), at least
-    99.9 % of elements within 2e-2 * max(|o|, A), relative L2 error <= 2e-3.
+    99.9 % of elements within 2e-2 * max(|o|, A), relative L2 error <= 2e-3,
+    where A = |R^(0)| + sum_u |s^(u) y^(u)| (eq:rcv); the per-element A13
+    figures (against max(|o|, RMS/16)) are reported beside them.
 """
 import numpy as np
 import torch
@@ -37,12 +36,11 @@ def to64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def check(name: str, got, ref, dtype: str, rms=None, scale=None):
+def check(name: str, got, ref, dtype: str, rms=None):
     """Assert ``got`` (GPU) matches ``ref`` (oracle) at the stated tolerance.
 
     ``rms`` overrides the RMS used for the floor (e.g. the RMS of the whole
-    output when only sampled tokens are compared); ``scale`` is the per-element
-    condition scale A (same shape as ``ref``)."""
+    output when only sampled tokens are compared)."""
     g, o = to64(got), to64(ref)
     assert g.shape == o.shape, f"{name}: shape {g.shape} vs {o.shape}"
     assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
@@ -60,10 +58,7 @@ def check(name: str, got, ref, dtype: str, rms=None, scale=None):
     else:
         # A13: relative L2 error of a bf16-stored result within ~3 half-ulps
         assert stats["rel_l2"] <= 4e-3, f"{name}: relative L2 error {stats['rel_l2']:.3e} > 4e-3"
-        mag = np.maximum(np.abs(o), rms / 16)
-        if scale is not None:
-            mag = np.maximum(mag, to64(scale))
-        bound = 2e-2 * mag
+        bound = 2e-2 * np.maximum(np.abs(o), rms / 16)
         bad = err > bound
         if bad.any():
             k = int(np.argmax(err / bound))
@@ -107,10 +102,16 @@ def check_chain(name: str, got, ref, scale):
     g, o, A = to64(got), to64(ref), to64(scale)
     assert g.shape == o.shape == A.shape
     assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
-    q = np.abs(g - o) / np.maximum(np.abs(o), A)
+    err = np.abs(g - o)
+    q = err / np.maximum(np.abs(o), A)
+    rms = float(np.sqrt(np.mean(o * o)))
+    strict = err / np.maximum(np.abs(o), rms / 16)
     rel_l2 = float(np.linalg.norm(g - o) / np.linalg.norm(o))
     frac = float((q > 2e-2).mean())
-    stats = {"max_err_over_scale": float(q.max()), "frac_over_2e-2": frac, "rel_l2": rel_l2}
+    stats = {"max_err_over_scale": float(q.max()), "frac_over_2e-2": frac, "rel_l2": rel_l2,
+             "a13_max_ratio": float(strict.max()), "a13_frac_over_2e-2": float((strict > 2e-2).mean())}
+    RECORDS.append((name, "bf16-chain", float(err.max() / max(rms, 1e-300)), rel_l2,
+                    int((strict > 2e-2).sum()), int(g.size)))
     assert q.max() <= 6e-2, f"{name}: element off by {q.max():.3e} of its scale; {stats}"
     assert frac <= 1e-3, f"{name}: {frac:.2e} of elements beyond 2e-2; {stats}"
     assert rel_l2 <= 2e-3, f"{name}: relative L2 error {rel_l2:.2e}; {stats}"

@@ -51,7 +51,7 @@ def run_read_write_fused(Xin: inputs.GRInputs, label: str):
     # read
     u0, s0 = gr.read(X, dev_params(p0))
     ou0, os0, A0 = orc_read(Xin.X, p0, dt)
-    check(f"{label} read u", u0, ou0, dt, scale=A0)
+    check(f"{label} read u", u0, ou0, dt)
     check(f"{label} read s", s0, os0, dt)
     # write with the oracle's strengths (same input on both sides)
     s_in = torch.from_numpy(os0).float()
@@ -64,7 +64,7 @@ def run_read_write_fused(Xin: inputs.GRInputs, label: str):
     u1, s1 = gr.fused_write_read(Xf, y, s_in.to(DEV), dev_params(p1))
     oR, ou1, os1, A1 = orc_fused(Xin.X, Xin.y, s_in.double().numpy(), p1, dt)
     check_exact(f"{label} fused state", Xf, oR)
-    check(f"{label} fused u", u1, ou1, dt, scale=A1)
+    check(f"{label} fused u", u1, ou1, dt)
     check(f"{label} fused s", s1, os1, dt)
     # the fused state is exactly the standalone write's
     assert torch.equal(Xf, Xw), f"{label}: fused state differs from gr_write's"
@@ -271,7 +271,7 @@ def test_wide_gate_without_write_projection():
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))
     assert torch.all(s == 1.0)
     ou, _, A = orc_read(X.X, X.params[0], "bf16")
-    check("wide no-write u", u, ou, "bf16", scale=A)
+    check("wide no-write u", u, ou, "bf16")
 
 
 def test_no_write_projection_gives_unit_strength():
@@ -279,7 +279,7 @@ def test_no_write_projection_gives_unit_strength():
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))
     assert torch.all(s == 1.0)
     ou, _, A = orc_read(X.X, X.params[0], "bf16")
-    check("no-write u", u, ou, "bf16", scale=A)
+    check("no-write u", u, ou, "bf16")
 
 
 def test_zero_write_projection_gives_exactly_one():
@@ -387,7 +387,7 @@ def sampled_read_parity(Xin, idx, label, fused=True):
     Xc = X.cpu()
     u1c = u1.cpu()
     check_exact(f"{label} fused state (sampled)", Xc[idx], oR)
-    check(f"{label} fused u (sampled)", u1c[idx], ou1, dt, scale=A1)
+    check(f"{label} fused u (sampled)", u1c[idx], ou1, dt)
     check(f"{label} fused s (sampled)", s1.cpu()[idx], os1, dt)
     assert torch.isfinite(u1c.float()).all() and torch.isfinite(Xc.float()).all()
 
@@ -455,14 +455,14 @@ def test_state_beyond_2_31_elements():
     Xs, ys = X[ti].cpu(), y[ti].cpu()
     u0, s0 = gr.read(X, dev_params(P[0]))
     ou0, os0, A0 = orc_read(Xs, P[0], "bf16")
-    check("2^31 read u (sampled)", u0[ti].cpu(), ou0, "bf16", scale=A0)
+    check("2^31 read u (sampled)", u0[ti].cpu(), ou0, "bf16")
     check("2^31 read s (sampled)", s0[ti].cpu(), os0, "bf16")
     s_in = s0.clone()
     s_in[ti] = torch.from_numpy(os0).float().to(DEV)
     u1, s1 = gr.fused_write_read(X, y, s_in, dev_params(P[1]))
     oR, ou1, os1, A1 = orc_fused(Xs, ys, os0, P[1], "bf16")
     check_exact("2^31 fused state (sampled)", X[ti].cpu(), oR)
-    check("2^31 fused u (sampled)", u1[ti].cpu(), ou1, "bf16", scale=A1)
+    check("2^31 fused u (sampled)", u1[ti].cpu(), ou1, "bf16")
     check("2^31 fused s (sampled)", s1[ti].cpu(), os1, "bf16")
     del X, y, u0, u1
     torch.cuda.empty_cache()

@@ -51,7 +51,7 @@ def test_variants_shapes(N, n, d, dt):
     u = gr.static_read(X, V.h.to(DEV))
     ou = oracle.static_read(V.X, V.h, dt)
     A = np.abs(to64(V.h)[None, :, None] * to64(V.X)).sum(axis=1)
-    check(f"{label} static read", u, ou, tol_dtype(dt), scale=A)
+    check(f"{label} static read", u, ou, tol_dtype(dt))
     # round-robin write, two depths
     for layer in (0, 2 * n + 1):
         Xr = X.clone()
@@ -99,7 +99,7 @@ def test_variants_prefill_size_sampled(dt):
     check_exact("expand (sampled)", R0.cpu()[idx], oracle.expand(V.e[idx], 4, dt))
     u = gr.static_read(X, V.h.to(DEV)).cpu()
     A = np.abs(to64(V.h)[None, :, None] * to64(V.X[idx])).sum(axis=1)
-    check("static read (sampled)", u[idx], oracle.static_read(V.X[idx], V.h, dt), "bf16", scale=A)
+    check("static read (sampled)", u[idx], oracle.static_read(V.X[idx], V.h, dt), "bf16")
     Xr = gr.round_robin_write(X.clone(), V.y.to(DEV), 7).cpu()
     check_exact("round-robin write (sampled)", Xr[idx], oracle.round_robin_write(V.X[idx], V.y[idx], 7, dt))
     Xp = gr.write_per_channel(X.clone(), V.y.to(DEV), V.s.to(DEV)).cpu()
