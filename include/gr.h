@@ -215,6 +215,69 @@ gr_status gr_write_per_channel(void *state, const void *y, const float *s, gr_dt
 gr_status gr_collapse(const void *state, const void *w, float eps, void *out, gr_dtype dt, int64_t N,
                       int32_t n, int32_t d, void *stream);
 
+/*
+ * ---- Hyper-Connections (HC) and manifold-constrained HC (mHC) -------------
+ * The branch-mixing family the GR design was cut down from ("Paper reading:
+ * Qwen3.8 Flash Next", part 2 Residual, sec. 2 Hyper-Connections): a block
+ * reads x = H_mix^T R, runs y = F(Norm(x)) (eq:block) and writes
+ *   R'_i = sum_j H_res[i][j] R_j + H_comb[i] y,
+ * each operator a static term plus a data-dependent one predicted from the
+ * per-branch-normalised state Rbar_i = g_i (.) R_i / rms(R_i) (eq:mix,
+ * eq:combine), with a_ik = Rbar_i . P_k:
+ *   GR_HC_TANH (HC):  H_mix_i = hm_i + lm tanh(a_i0), H_comb_i = hc_i + lc tanh(a_i1),
+ *                     H_res[i][j] = hr_ij + lr tanh(a_i,2+j)
+ *   GR_HC_MHC  (mHC): H_mix_i = sigmoid(hm_i + lm a_i0), H_comb_i = 2 sigmoid(hc_i + lc a_i1),
+ *                     H_res = `sinkhorn_iters` Sinkhorn-Knopp steps (rows scaled
+ *                     to sum 1, then columns) on exp(hr_ij + lr a_i,2+j)
+ * ("DepthBench", sec. 2.5: sigmoid read weights, twice-sigmoid write weights,
+ * 20 Sinkhorn-Knopp iterations).  The block's Norm is an RMSNorm with gain
+ * w_norm: u = w_norm (.) x / sqrt(mean(x^2) + eps).  The read predicts all
+ * three operators from the same state and hands the write's coefficient
+ * record coeff[t] = [H_comb (n) | H_res row-major (n*n)] (fp32).
+ * dtype GR_F32 or GR_BF16 (state, y, u, gains and P share it); 1 <= n <= 8.
+ * bf16 with n in {1, 2, 4} and d <= 4096 runs one workgroup per token that
+ * keeps the token's state in registers: the fused call reads and writes the
+ * state once.  No workspace; coeff_in and coeff_out must not overlap.
+ */
+typedef enum gr_hc_mode { GR_HC_TANH = 0, GR_HC_MHC = 1 } gr_hc_mode;
+
+typedef struct gr_hc_layer {
+    int32_t n, d;              /* branches (1..8) and width */
+    int32_t mode;              /* gr_hc_mode */
+    int32_t sinkhorn_iters;    /* GR_HC_MHC: Sinkhorn-Knopp steps (0..1000); the pages use 20 */
+    float eps;                 /* both RMSNorms, inside the root (>= 0, finite) */
+    float lambda_mix, lambda_comb, lambda_res;   /* scales of the dynamic terms */
+    const void *gamma;         /* [n][d]   per-branch gains of Rbar */
+    const void *w_norm;        /* [d]      gain of the block's RMSNorm on x */
+    const void *w_proj;        /* [n+2][d] rows W_mix, W_comb, then column j of W_res as row 2+j */
+    const float *h_static;     /* [2n + n*n] fp32: hm | hc | hr (row-major) */
+} gr_hc_layer;
+
+/*
+ * gr_hc_read -- x, its RMSNorm u, and the write's coefficients.
+ *   state in [N][n][d];  u out [N][d];  coeff out [N][n + n*n] fp32
+ */
+gr_status gr_hc_read(const void *state, gr_dtype dt, int64_t N, const gr_hc_layer *L, void *u,
+                     float *coeff, void *stream);
+
+/*
+ * gr_hc_write -- in place: R'_i = sum_j H_res[i][j] R_j + H_comb[i] y, summed
+ * in fp32 and stored in the state dtype (round to nearest even).
+ *   state in/out [N][n][d];  y in [N][d];  coeff in [N][n + n*n] fp32
+ */
+gr_status gr_hc_write(void *state, const void *y, const float *coeff, gr_dtype dt, int64_t N,
+                      int32_t n, int32_t d, void *stream);
+
+/*
+ * gr_hc_fused_write_read -- gr_hc_write of block l, then gr_hc_read of block
+ * l+1 with `next` on the stored state (the state equals gr_hc_write's).
+ *   state in/out [N][n][d];  y in [N][d];  coeff_in in [N][n + n*n]
+ *   u_next out [N][d];  coeff_next out [N][n + n*n]
+ */
+gr_status gr_hc_fused_write_read(void *state, const void *y, const float *coeff_in, gr_dtype dt,
+                                 int64_t N, const gr_hc_layer *next, void *u_next, float *coeff_next,
+                                 void *stream);
+
 /* Bytes of workspace `op` needs for N tokens of layer L (may be 0), for that
  * layer as given: with or without W_write the layout differs, so query with
  * the layer the call will use.

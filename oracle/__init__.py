@@ -27,6 +27,10 @@ Every function follows a passage of the pages:
                            was tried); strengths a learned [n, d] parameter.
   collapse              -- read-out after the last block: sum of the branches,
                            then RMSNorm (a reading; the GR pages give none).
+  sinkhorn, hc_read,    -- Hyper-Connections and mHC: the paper reading, sec. 2
+  hc_write, hc_fused       (eq:block, eq:mix, eq:combine; phi = tanh), and
+                           "DepthBench" sec. 2.5 (mHC: sigmoid reads, twice-
+                           sigmoid writes, 20 Sinkhorn-Knopp iterations).
 """
 from __future__ import annotations
 
@@ -74,6 +78,12 @@ def _load():
         lib.gro_round_robin_write.argtypes = [I64, I, I, I, I, P, P]
         lib.gro_write_per_channel.argtypes = [I64, I, I, I, P, P, P]
         lib.gro_collapse.argtypes = [I64, I, I, D, I, P, P, P]
+        lib.gro_sinkhorn.argtypes = [I, I, P, P]
+        lib.gro_hc_read.argtypes = [I64, I, I, I, I, D, I, P, P, P, P, P, P, P, P, P]
+        lib.gro_hc_write.argtypes = [I64, I, I, I, P, P, P]
+        lib.gro_hc_fused.argtypes = [I64, I, I, I, I, D, I, P, P, P, P, P, P, P, P, P, P]
+        for f in (lib.gro_sinkhorn, lib.gro_hc_read, lib.gro_hc_write, lib.gro_hc_fused):
+            f.restype = ctypes.c_int
         lib.orc_round_bf16.argtypes = [D]
         lib.orc_round_bf16.restype = D
         lib.orc_round_e4m3.argtypes = [D]
@@ -232,6 +242,64 @@ def collapse(R, w, eps: float = 1e-6, dtype: str = "bf16") -> np.ndarray:
     out = np.empty((N, d))
     _check(_load().gro_collapse(N, n, d, eps, _DT[dtype], _p(R), _p(w), _p(out)), "collapse")
     return out
+
+
+_HC_MODE = {"hc": 0, "mhc": 1}
+
+
+def sinkhorn(L, iters: int = 20) -> np.ndarray:
+    """Sinkhorn-Knopp on exp(L) (n x n): rows then columns scaled to sum 1, per iteration."""
+    L = _f64(L)
+    n = L.shape[0]
+    M = np.empty((n, n))
+    _check(_load().gro_sinkhorn(n, int(iters), _p(L), _p(M)), "sinkhorn")
+    return M
+
+
+def _hc_params(n, d, gamma, w_norm, w_proj, h_static, lam):
+    return (_f64(gamma, (n, d)), _f64(w_norm, (d,)), _f64(w_proj, (n + 2, d)),
+            _f64(h_static, (2 * n + n * n,)), _f64(lam, (3,)))
+
+
+def hc_read(R, gamma, w_norm, w_proj, h_static, lam, mode: str = "mhc", iters: int = 20,
+            eps: float = 1e-6, dtype: str = "bf16", detail: bool = False):
+    """HC / mHC read: returns (u [N,d], coeff [N, n+n*n]) and, with ``detail``,
+    H_mix [N, n].  coeff holds H_combine then H_res (row-major)."""
+    R = _f64(R)
+    N, n, d = R.shape
+    g, w, P, hs, lm = _hc_params(n, d, gamma, w_norm, w_proj, h_static, lam)
+    u = np.empty((N, d))
+    coeff = np.empty((N, n + n * n))
+    hm = np.empty((N, n)) if detail else None
+    _check(_load().gro_hc_read(N, n, d, _HC_MODE[mode], int(iters), eps, _DT[dtype], _p(R), _p(g),
+                               _p(w), _p(P), _p(hs), _p(lm), _p(u), _p(coeff), _p(hm)), "hc_read")
+    return (u, coeff, hm) if detail else (u, coeff)
+
+
+def hc_write(R, y, coeff, dtype: str = "bf16") -> np.ndarray:
+    """HC / mHC write: R'_i = sum_j H_res[i,j] R_j + H_comb[i] y (a new array)."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    coeff = _f64(coeff, (N, n + n * n))
+    _check(_load().gro_hc_write(N, n, d, _DT[dtype], _p(R), _p(y), _p(coeff)), "hc_write")
+    return R
+
+
+def hc_fused(R, y, coeff_in, gamma, w_norm, w_proj, h_static, lam, mode: str = "mhc",
+             iters: int = 20, eps: float = 1e-6, dtype: str = "bf16"):
+    """Write of block l, then the read of block l+1: returns (R', u, coeff_out)."""
+    R = _f64(R).copy()
+    N, n, d = R.shape
+    y = _f64(y, (N, d))
+    cin = _f64(coeff_in, (N, n + n * n))
+    g, w, P, hs, lm = _hc_params(n, d, gamma, w_norm, w_proj, h_static, lam)
+    u = np.empty((N, d))
+    cout = np.empty((N, n + n * n))
+    _check(_load().gro_hc_fused(N, n, d, _HC_MODE[mode], int(iters), eps, _DT[dtype], _p(R), _p(y),
+                                _p(cin), _p(g), _p(w), _p(P), _p(hs), _p(lm), _p(u), _p(cout)),
+           "hc_fused")
+    return R, u, cout
 
 
 def chain(X0, params: Sequence, eps: float = 1e-6, dtype: str = "bf16",

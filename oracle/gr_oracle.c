@@ -353,3 +353,173 @@ int gro_tanh_standin(int64_t count, int dtype, const double *u, double *y)
     for (int64_t k = 0; k < count; ++k) y[k] = store_round(0.1 * tanh(u[k]), dtype);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Hyper-Connections (HC) and manifold-constrained HC (mHC)
+ *
+ * [QFN sec. 2] "Hyper-Connections": a block reads x = H_mix^T R, runs
+ * y = F(Norm(x)) (eq:block), and writes R' = H_res R + H_combine y^T, with
+ * H_mix, H_combine in R^n and H_res in R^{n x n}.  Each operator is a static
+ * term plus a data-dependent term predicted from the normalised branches
+ * Rbar = Norm(R): H = H^s + lambda * phi(Rbar W) (eq:mix, eq:combine and the
+ * line after them); HC takes phi = tanh.
+ * [DB sec. 2.5] "DepthBench" (cc.laoqi.cc), "Block AttnRes and mHC": mHC reads
+ * with sigmoid weights, writes with twice-sigmoid weights, and maps the
+ * propagation matrix through 20 Sinkhorn-Knopp iterations to an approximately
+ * doubly stochastic one.
+ *
+ * Readings where the pages leave a point open:
+ *   - Norm is the per-branch RMSNorm of eq:rms: Rbar_i = g_i * R_i * rho_i,
+ *     rho_i = 1/sqrt(mean_c R_ic^2 + eps), with a gain g_i per branch.
+ *   - Rbar W_m, Rbar W_c are n-vectors and Rbar W_r an n x n matrix, so
+ *     W_m, W_c are d-vectors and W_r is d x n, shared by the branches:
+ *     (Rbar W_r)_ij = sum_c Rbar_ic W_r[c][j].  They are passed as the rows
+ *     of P [n+2][d]: P[0] = W_m, P[1] = W_c, P[2+j] = column j of W_r.
+ *   - lambda_m, lambda_c, lambda_r are scalars.
+ *   - HC:  H_mix = Hs_mix + lm tanh(Rbar W_m), H_comb = Hs_comb + lc tanh(Rbar W_c),
+ *          H_res = Hs_res + lr tanh(Rbar W_r).
+ *   - mHC: H_mix = sigmoid(Hs_mix + lm Rbar W_m), H_comb = 2 sigmoid(Hs_comb + lc Rbar W_c),
+ *          H_res = SK(exp(Hs_res + lr Rbar W_r)): exp makes the matrix positive,
+ *          as Sinkhorn-Knopp requires; one iteration divides every row by its
+ *          sum, then every column by its sum.
+ *   - The block's Norm is an RMSNorm with gain w: u = w x / sqrt(mean x^2 + eps),
+ *     stored in the state dtype; x is formed from the raw R (eq:block).
+ *   - The read predicts all three operators from the same pre-write state; it
+ *     hands H_combine and H_res (the coefficient record [H_comb | H_res row-major],
+ *     n + n*n values, fp32) to the write of the same block, as the GR read
+ *     hands s to its write.
+ *   - The write is evaluated exactly (fp64) and rounded once to the state dtype.
+ * ------------------------------------------------------------------------ */
+
+enum { ORC_HC_TANH = 0, ORC_HC_MHC = 1 };
+
+/* Sinkhorn-Knopp [DB sec. 2.5]: M = exp(L) (n x n, row-major), then `iters`
+ * times: scale each row to sum 1, then each column to sum 1. */
+int gro_sinkhorn(int n, int iters, const double *L, double *M)
+{
+    if (n < 1 || iters < 0) return -1;
+    for (int k = 0; k < n * n; ++k) M[k] = exp(L[k]);
+    for (int it = 0; it < iters; ++it) {
+        for (int i = 0; i < n; ++i) {
+            double s = 0.0;
+            for (int j = 0; j < n; ++j) s += M[i * n + j];
+            for (int j = 0; j < n; ++j) M[i * n + j] /= s;
+        }
+        for (int j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int i = 0; i < n; ++i) s += M[i * n + j];
+            for (int i = 0; i < n; ++i) M[i * n + j] /= s;
+        }
+    }
+    return 0;
+}
+
+/*
+ * HC / mHC read of one block.
+ *   R [N][n][d]; g [n][d]; w [d]; P [n+2][d]; hs [2n + n*n] = Hs_mix | Hs_comb | Hs_res;
+ *   lam[3] = lambda_m, lambda_c, lambda_r.
+ * Outputs u [N][d] (state dtype), coeff [N][n + n*n] (fp32), and, if given,
+ * hmix [N][n] (fp64, for tests).
+ */
+int gro_hc_read(int64_t N, int n, int d, int mode, int iters, double eps, int dtype,
+                const double *R, const double *g, const double *w, const double *P,
+                const double *hs, const double *lam, double *u, double *coeff, double *hmix)
+{
+    if (N < 0 || n < 1 || d < 1 || (mode != ORC_HC_TANH && mode != ORC_HC_MHC)) return -1;
+    const int nc = n + n * n;
+    double *rbar = malloc(sizeof(double) * n * d);
+    double *proj = malloc(sizeof(double) * n * (n + 2));   /* proj[i][k] = Rbar_i . P[k] */
+    double *hm = malloc(sizeof(double) * n);
+    double *L = malloc(sizeof(double) * n * n);
+    double *Hres = malloc(sizeof(double) * n * n);
+    double *x = malloc(sizeof(double) * d);
+    if (!rbar || !proj || !hm || !L || !Hres || !x) {
+        free(rbar); free(proj); free(hm); free(L); free(Hres); free(x);
+        return -1;
+    }
+    for (int64_t t = 0; t < N; ++t) {
+        const double *Rt = R + t * n * (int64_t)d;
+        /* Rbar = per-branch RMSNorm (eq:rms) */
+        for (int i = 0; i < n; ++i) {
+            double ss = 0.0;
+            for (int c = 0; c < d; ++c) ss += Rt[i * d + c] * Rt[i * d + c];
+            const double rho = 1.0 / sqrt(ss / d + eps);
+            for (int c = 0; c < d; ++c) rbar[i * d + c] = g[i * d + c] * Rt[i * d + c] * rho;
+        }
+        for (int i = 0; i < n; ++i)
+            for (int k = 0; k < n + 2; ++k) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c) acc += rbar[i * d + c] * P[k * (int64_t)d + c];
+                proj[i * (n + 2) + k] = acc;
+            }
+        double *ct = coeff + t * nc;
+        for (int i = 0; i < n; ++i) {
+            const double am = proj[i * (n + 2) + 0], ac = proj[i * (n + 2) + 1];
+            if (mode == ORC_HC_TANH) {
+                hm[i] = hs[i] + lam[0] * tanh(am);
+                ct[i] = hs[n + i] + lam[1] * tanh(ac);
+            } else {
+                hm[i] = sigmoid(hs[i] + lam[0] * am);
+                ct[i] = 2.0 * sigmoid(hs[n + i] + lam[1] * ac);
+            }
+            for (int j = 0; j < n; ++j) {
+                const double ar = proj[i * (n + 2) + 2 + j];
+                if (mode == ORC_HC_TANH) Hres[i * n + j] = hs[2 * n + i * n + j] + lam[2] * tanh(ar);
+                else L[i * n + j] = hs[2 * n + i * n + j] + lam[2] * ar;
+            }
+        }
+        if (mode == ORC_HC_MHC) gro_sinkhorn(n, iters, L, Hres);
+        for (int i = 0; i < n; ++i) ct[i] = orc_round_f32(ct[i]);
+        for (int k = 0; k < n * n; ++k) ct[n + k] = orc_round_f32(Hres[k]);
+        if (hmix) for (int i = 0; i < n; ++i) hmix[t * n + i] = hm[i];
+        /* x = H_mix^T R, then the block's RMSNorm (eq:block) */
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i) acc += hm[i] * Rt[i * d + c];
+            x[c] = acc;
+            ss += acc * acc;
+        }
+        const double inv = 1.0 / sqrt(ss / d + eps);
+        for (int c = 0; c < d; ++c) u[t * d + c] = store_round(w[c] * x[c] * inv, dtype);
+    }
+    free(rbar); free(proj); free(hm); free(L); free(Hres); free(x);
+    return 0;
+}
+
+/* HC / mHC write [QFN sec. 2]: R'_i = sum_j H_res[i][j] R_j + H_comb[i] y, with
+ * coeff [N][n + n*n] = H_comb | H_res row-major; exact, then one rounding. */
+int gro_hc_write(int64_t N, int n, int d, int dtype, double *R, const double *y,
+                 const double *coeff)
+{
+    if (N < 0 || n < 1 || d < 1) return -1;
+    const int nc = n + n * n;
+    double *old = malloc(sizeof(double) * n);
+    if (!old) return -1;
+    for (int64_t t = 0; t < N; ++t) {
+        double *Rt = R + t * n * (int64_t)d;
+        const double *ct = coeff + t * nc;
+        for (int c = 0; c < d; ++c) {
+            for (int j = 0; j < n; ++j) old[j] = Rt[j * d + c];
+            for (int i = 0; i < n; ++i) {
+                double acc = ct[i] * y[t * d + c];
+                for (int j = 0; j < n; ++j) acc += ct[n + i * n + j] * old[j];
+                Rt[i * d + c] = store_state(acc, dtype);
+            }
+        }
+    }
+    free(old);
+    return 0;
+}
+
+/* Write of block l (coefficients coeff_in), then the read of block l+1 on the
+ * stored state. */
+int gro_hc_fused(int64_t N, int n, int d, int mode, int iters, double eps, int dtype,
+                 double *R, const double *y, const double *coeff_in, const double *g,
+                 const double *w, const double *P, const double *hs, const double *lam,
+                 double *u, double *coeff_out)
+{
+    int rc = gro_hc_write(N, n, d, dtype, R, y, coeff_in);
+    if (rc) return rc;
+    return gro_hc_read(N, n, d, mode, iters, eps, dtype, R, g, w, P, hs, lam, u, coeff_out, NULL);
+}

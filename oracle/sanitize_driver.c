@@ -25,6 +25,13 @@ int gro_round_robin_write(int64_t, int, int, int, int, double *, const double *)
 int gro_write_per_channel(int64_t, int, int, int, double *, const double *, const double *);
 int gro_collapse(int64_t, int, int, double, int, const double *, const double *, double *);
 int gro_tanh_standin(int64_t, int, const double *, double *);
+int gro_sinkhorn(int, int, const double *, double *);
+int gro_hc_read(int64_t, int, int, int, int, double, int, const double *, const double *, const double *,
+                const double *, const double *, const double *, double *, double *, double *);
+int gro_hc_write(int64_t, int, int, int, double *, const double *, const double *);
+int gro_hc_fused(int64_t, int, int, int, int, double, int, double *, const double *, const double *,
+                 const double *, const double *, const double *, const double *, const double *,
+                 double *, double *);
 double orc_round_bf16(double);
 double orc_round_e4m3(double);
 
@@ -92,6 +99,26 @@ int main(void)
         double *x = arr(N * d);
         expect(gro_add_rmsnorm(N, d, 1e-6, dt, x, y, w1, o) == (dt == 3 ? -1 : 0), "add_rmsnorm", N, n, d, r, dt);
         expect(gro_tanh_standin(N * d, dt, u, o) == 0, "tanh_standin", N, n, d, r, dt);
+        /* HC / mHC: coefficient records of n + n*n, projections of n + 2 rows */
+        {
+            const int64_t nc = n + (int64_t)n * n;
+            double *P = arr((n + 2) * (int64_t)d), *hs = arr(2 * n + (int64_t)n * n), *lam = arr(3);
+            double *cin = arr(N * nc), *cout = arr(N * nc), *hm = arr(N * n), *uu = arr(N * d);
+            double *L = arr((int64_t)n * n), *M = arr((int64_t)n * n);
+            expect(gro_sinkhorn(n, 20, L, M) == 0 && finite_all(M, (int64_t)n * n), "sinkhorn", N, n, d, r, dt);
+            for (int mode = 0; mode < 2; ++mode) {
+                expect(gro_hc_read(N, n, d, mode, 20, 1e-6, dt, R, gamma, w1, P, hs, lam, uu, cout, hm) == 0,
+                       "hc_read", N, n, d, r, dt);
+                expect(finite_all(uu, N * d) && finite_all(cout, N * nc) && finite_all(hm, N * n),
+                       "hc_read finite", N, n, d, r, dt);
+                expect(gro_hc_fused(N, n, d, mode, 20, 1e-6, dt, R, y, cin, gamma, w1, P, hs, lam, uu, cout) == 0,
+                       "hc_fused", N, n, d, r, dt);
+            }
+            expect(gro_hc_write(N, n, d, dt, R, y, cin) == 0, "hc_write", N, n, d, r, dt);
+            expect(gro_hc_read(N, n, d, 2, 20, 1e-6, dt, R, gamma, w1, P, hs, lam, uu, cout, NULL) == -1,
+                   "hc_read bad mode", N, n, d, r, dt);
+            free(P); free(hs); free(lam); free(cin); free(cout); free(hm); free(uu); free(L); free(M);
+        }
         free(R); free(y); free(s_in); free(gamma); free(wd); free(wu); free(ww); free(u); free(s);
         free(rho); free(G); free(e0); free(h); free(sc); free(w1); free(o); free(x);
     }

@@ -12,6 +12,11 @@ Tolerances (written here, used by every GPU parity test):
   * written state (eq:write): bit for bit (check_exact).  Both sides form
     R + s y in fp32 (the exact value rounded once, as one fp32 FMA does) and
     store that rounded to the state dtype.
+  * state written by the HC / mHC write (check_sum_store): R'_i is a sum of
+    n + 1 products, formed in fp32 on the GPU and exactly in the oracle, then
+    rounded once to the state dtype, so the two may differ by the fp32 sum's
+    error and one rounding: |g - o| <= ulp(max(|g|, |o|)) + (n + 2) 2^-24 T,
+    T = sum_j |H_res_ij R_j| + |H_comb_i y| (ulp of the state dtype).
   * chained bf16 state after L sublayers (check_chain): each stored value is
     rounded L times, and a rounding decision that differs between the two
     sides (a pre-rounding difference of 1e-7 lands on a bf16 rounding
@@ -78,6 +83,31 @@ def check_exact(name: str, got, ref):
         idx = tuple(int(v) for v in np.argwhere(diff)[0])
         raise AssertionError(f"{name}: {int(diff.sum())} of {diff.size} elements differ "
                              f"(first at {idx}: gpu {g[idx]!r} oracle {o[idx]!r})")
+
+
+def _ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    bits = 8 if dtype == "bf16" else 24
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - (bits - 1))
+
+
+def check_sum_store(name: str, got, ref, terms, n: int, dtype: str):
+    """The HC write's criterion stated in the module docstring; ``terms`` is T."""
+    g, o, T = to64(got), to64(ref), to64(terms)
+    assert g.shape == o.shape == T.shape, f"{name}: shapes {g.shape} {o.shape} {T.shape}"
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
+    err = np.abs(g - o)
+    bound = _ulp(np.maximum(np.abs(g), np.abs(o)), dtype) + (n + 2) * 2.0 ** -24 * T
+    rms = float(np.sqrt(np.mean(o * o))) if o.size else 1.0
+    exact = float((err == 0).mean()) if o.size else 1.0
+    RECORDS.append((name, dtype + "-hc-state", float(err.max() / max(rms, 1e-300)) if o.size else 0.0,
+                    float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-300)), 0, int(g.size)))
+    bad = err > bound
+    if bad.any():
+        idx = tuple(int(v) for v in np.argwhere(bad)[0])
+        raise AssertionError(f"{name}: {int(bad.sum())} of {bad.size} elements beyond one rounding "
+                             f"(first at {idx}: gpu {g[idx]!r} oracle {o[idx]!r} bound {bound[idx]:.3e})")
+    return {"exact_fraction": exact}
 
 
 def sample_tokens(N: int, k: int, seed: int = 0) -> np.ndarray:

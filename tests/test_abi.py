@@ -185,3 +185,37 @@ def test_variant_calls_reject_bad_arguments(L):
     assert L.gr_collapse(FAKE, FAKE, float("nan"), FAKE, 1, 4, 4, 64, None) == INVALID
     assert L.gr_collapse(FAKE, None, 1e-6, FAKE, 1, 4, 4, 64, None) == INVALID
     assert L.gr_last_error() != b""
+
+
+def hc_layer(n=4, d=64, mode=1, iters=20, eps=1e-6, lam=(1.0, 1.0, 1.0), gamma=FAKE, wn=FAKE, wp=FAKE,
+             hs=FAKE):
+    return gr._HcLayer(n, d, mode, iters, eps, *lam, gamma, wn, wp, hs)
+
+
+def test_hc_calls_reject_bad_arguments(L):
+    """Hyper-Connections / mHC calls: host-side checks only (no launch)."""
+    rd = lambda lay, dt=1, N=4, state=FAKE, u=FAKE, c=FAKE: L.gr_hc_read(state, dt, N, ctypes.byref(lay), u, c, None)
+    assert L.gr_hc_read(None, 1, 0, None, None, None, None) == 0                     # N = 0
+    assert L.gr_hc_write(None, None, None, 1, 0, 4, 64, None) == 0
+    assert L.gr_hc_fused_write_read(None, None, None, 1, 0, None, None, None, None) == 0
+    assert rd(hc_layer(n=0)) == INVALID
+    assert rd(hc_layer(n=9)) == INVALID
+    assert rd(hc_layer(mode=2)) == INVALID
+    assert rd(hc_layer(iters=-1)) == INVALID
+    assert rd(hc_layer(iters=1001)) == INVALID
+    assert rd(hc_layer(eps=-1.0)) == INVALID
+    assert rd(hc_layer(lam=(1.0, float("inf"), 1.0))) == INVALID
+    assert rd(hc_layer(d=60)) == NOT_SUPPORTED                                         # bf16: d % 8
+    assert rd(hc_layer(), dt=2) == NOT_SUPPORTED                                       # no fp8 state
+    assert rd(hc_layer(), dt=7) == INVALID
+    assert rd(hc_layer(wp=None)) == INVALID
+    assert rd(hc_layer(hs=MISALIGNED)) == INVALID
+    assert rd(hc_layer(), c=None) == INVALID
+    assert rd(hc_layer(), N=-1) == INVALID
+    assert L.gr_hc_write(FAKE, FAKE, FAKE, 1, 4, 0, 64, None) == INVALID               # n < 1
+    assert L.gr_hc_write(FAKE, None, FAKE, 1, 4, 4, 64, None) == INVALID
+    assert L.gr_hc_write(FAKE, FAKE, FAKE, 0, 4, 4, 62, None) == NOT_SUPPORTED         # fp32: d % 4
+    lay = hc_layer()
+    assert L.gr_hc_fused_write_read(FAKE, FAKE, None, 1, 4, ctypes.byref(lay), FAKE, FAKE, None) == INVALID
+    assert L.gr_hc_fused_write_read(FAKE, FAKE, FAKE, 1, 4, None, FAKE, FAKE, None) == INVALID
+    assert b"gr_hc_fused_write_read" in L.gr_last_error()

@@ -12,6 +12,8 @@ GR ("Paper reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4):
   write  R_i += s_i y
   fused  write of sublayer l, then read of sublayer l+1, one pass over R.
 n = 1 fused residual add + RMSNorm: "Residual" (LLM inference), sec. 3.3.
+Hyper-Connections / mHC (same paper reading, sec. 2; "DepthBench", sec. 2.5):
+  hc_read, hc_write, hc_fused_write_read with an ``HCLayer``.
 """
 from __future__ import annotations
 
@@ -22,13 +24,16 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["read", "write", "fused_write_read", "residual_add_rmsnorm", "tanh_standin",
-           "copy", "workspace_size", "library_path", "device_error_word", "GRError"]
+           "copy", "workspace_size", "library_path", "device_error_word", "GRError",
+           "hc_read", "hc_write", "hc_fused_write_read", "HC_TANH", "HC_MHC"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgr.so")
 
 GR_F32, GR_BF16, GR_FP8_E4M3 = 0, 1, 2
 GR_OP_READ, GR_OP_FUSED_WRITE_READ = 0, 1
+HC_TANH, HC_MHC = 0, 1
+_HC_MODES = {"hc": HC_TANH, "mhc": HC_MHC, HC_TANH: HC_TANH, HC_MHC: HC_MHC}
 
 
 class GRError(RuntimeError):
@@ -44,6 +49,15 @@ class _Layer(ctypes.Structure):
                 ("eps", ctypes.c_float), ("gamma", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_write", ctypes.c_void_p)]
+
+
+class _HcLayer(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("d", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("sinkhorn_iters", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("lambda_mix", ctypes.c_float), ("lambda_comb", ctypes.c_float),
+                ("lambda_res", ctypes.c_float), ("gamma", ctypes.c_void_p),
+                ("w_norm", ctypes.c_void_p), ("w_proj", ctypes.c_void_p),
+                ("h_static", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,6 +92,10 @@ def lib():
         L.gr_bench_tanh_standin.argtypes = [P, P, ctypes.c_int, I64, P]
         L.gr_bench_copy.argtypes = [P, P, ctypes.c_size_t, P]
         L.gr_device_error_word.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+        HP = ctypes.POINTER(_HcLayer)
+        L.gr_hc_read.argtypes = [P, ctypes.c_int, I64, HP, P, P, P]
+        L.gr_hc_write.argtypes = [P, P, P, ctypes.c_int, I64, I32, I32, P]
+        L.gr_hc_fused_write_read.argtypes = [P, P, P, ctypes.c_int, I64, HP, P, P, P]
         L.gr_status_string.argtypes = [ctypes.c_int]
         L.gr_status_string.restype = ctypes.c_char_p
         L.gr_last_error.argtypes = []
@@ -85,7 +103,7 @@ def lib():
         for f in ("gr_read", "gr_write", "gr_fused_write_read", "residual_add_rmsnorm",
                   "gr_workspace_size", "gr_bench_tanh_standin", "gr_bench_copy", "gr_expand",
                   "gr_static_read", "gr_round_robin_write", "gr_write_per_channel", "gr_collapse",
-                  "gr_device_error_word"):
+                  "gr_device_error_word", "gr_hc_read", "gr_hc_write", "gr_hc_fused_write_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -343,3 +361,71 @@ def copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
     dp = _dev(dst, "dst", tuple(src.shape), src.dtype, src.device)
     _call("gr_bench_copy", sp, dp, nbytes, _stream(src.device))
     return dst
+
+
+# ------------------------------------------------------------------ Hyper-Connections / mHC
+def _hc_layer(layer, n: int, d: int, dtype, device) -> _HcLayer:
+    """``layer`` has mode ("hc" / "mhc"), iters, eps, lam (3 floats), gamma [n, d],
+    w_norm [d], w_proj [n+2, d] (state dtype) and h_static [2n + n*n] fp32."""
+    g = _dev(layer.gamma, "gamma", (n, d), dtype, device)
+    wn = _dev(layer.w_norm, "w_norm", (d,), dtype, device)
+    wp = _dev(layer.w_proj, "w_proj", (n + 2, d), dtype, device)
+    hs = _dev(layer.h_static, "h_static", (2 * n + n * n,), torch.float32, device)
+    lm, lc, lr = (float(v) for v in layer.lam)
+    return _HcLayer(n, d, _HC_MODES[layer.mode], int(layer.iters), float(layer.eps), lm, lc, lr,
+                    g, wn, wp, hs)
+
+
+def _hc_dt(state: torch.Tensor) -> int:
+    if state.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"the HC calls take a float32 or bfloat16 state, not {state.dtype}")
+    return _dt(state)
+
+
+def hc_read(state: torch.Tensor, layer, u: Optional[torch.Tensor] = None,
+            coeff: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """HC / mHC read of ``state`` [N, n, d]: returns (u [N, d], coeff [N, n + n*n] fp32),
+    coeff = [H_comb | H_res row-major] for the write."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    code = _hc_dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    L = _hc_layer(layer, n, d, dt, dev)
+    u = torch.empty((N, d), dtype=dt, device=dev) if u is None else u
+    coeff = torch.empty((N, n + n * n), dtype=torch.float32, device=dev) if coeff is None else coeff
+    up = _dev(u, "u", (N, d), dt, dev)
+    cp = _dev(coeff, "coeff", (N, n + n * n), torch.float32, dev)
+    _call("gr_hc_read", sp, code, N, ctypes.byref(L), up, cp, _stream(dev))
+    return u, coeff
+
+
+def hc_write(state: torch.Tensor, y: torch.Tensor, coeff: torch.Tensor) -> torch.Tensor:
+    """HC / mHC write, in place: R'_i = sum_j H_res[i, j] R_j + H_comb[i] y.  Returns state."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    code = _hc_dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    yp = _dev(y, "y", (N, d), dt, dev)
+    cp = _dev(coeff, "coeff", (N, n + n * n), torch.float32, dev)
+    _call("gr_hc_write", sp, yp, cp, code, N, n, d, _stream(dev))
+    return state
+
+
+def hc_fused_write_read(state: torch.Tensor, y: torch.Tensor, coeff_in: torch.Tensor, layer,
+                        u: Optional[torch.Tensor] = None,
+                        coeff: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """HC / mHC write of block l (y, coeff_in) in place, then the read of block
+    l+1 with ``layer``: returns (u_next [N, d], coeff_next [N, n + n*n])."""
+    N, n, d = state.shape
+    dev, dt = state.device, state.dtype
+    code = _hc_dt(state)
+    sp = _dev(state, "state", (N, n, d), dt, None)
+    yp = _dev(y, "y", (N, d), dt, dev)
+    cip = _dev(coeff_in, "coeff_in", (N, n + n * n), torch.float32, dev)
+    L = _hc_layer(layer, n, d, dt, dev)
+    u = torch.empty((N, d), dtype=dt, device=dev) if u is None else u
+    coeff = torch.empty((N, n + n * n), dtype=torch.float32, device=dev) if coeff is None else coeff
+    up = _dev(u, "u_next", (N, d), dt, dev)
+    cp = _dev(coeff, "coeff_next", (N, n + n * n), torch.float32, dev)
+    _call("gr_hc_fused_write_read", sp, yp, cip, code, N, ctypes.byref(L), up, cp, _stream(dev))
+    return u, coeff

@@ -269,6 +269,111 @@ gr_status gr_fused_write_read_noalloc(void *state, const void *y, const float *s
     return run_read(a, next, kNoAllocScratchBytes, (hipStream_t)stream, fn);
 }
 
+}  // extern "C"
+
+namespace {
+
+gr_status check_hc_layer(const gr_hc_layer *L, gr_dtype dt, const char *fn) {
+    if (!L) return fail(GR_ERROR_INVALID_VALUE, "%s: layer is NULL", fn);
+    if (L->n < 1 || L->n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, L->n);
+    gr_status st = check_width(dt, L->d, fn);
+    if (st) return st;
+    if ((int64_t)L->n * L->d > (1 << 24)) return fail(GR_ERROR_NOT_SUPPORTED, "%s: n*d too large", fn);
+    if (L->mode != GR_HC_TANH && L->mode != GR_HC_MHC)
+        return fail(GR_ERROR_INVALID_VALUE, "%s: unknown mode %d", fn, L->mode);
+    if (L->sinkhorn_iters < 0 || L->sinkhorn_iters > 1000)
+        return fail(GR_ERROR_INVALID_VALUE, "%s: sinkhorn_iters = %d outside 0..1000", fn, L->sinkhorn_iters);
+    if (!(L->eps >= 0.f) || !isfinite(L->eps) || !isfinite(L->lambda_mix) || !isfinite(L->lambda_comb) ||
+        !isfinite(L->lambda_res))
+        return fail(GR_ERROR_INVALID_VALUE, "%s: eps must be finite and >= 0, the lambdas finite", fn);
+    if ((st = check_ptr(L->gamma, "gamma", fn)) || (st = check_ptr(L->w_norm, "w_norm", fn)) ||
+        (st = check_ptr(L->w_proj, "w_proj", fn)) || (st = check_ptr(L->h_static, "h_static", fn)))
+        return st;
+    return GR_SUCCESS;
+}
+
+gr_status check_hc_dtype(gr_dtype dt, const char *fn) {
+    gr_status st = check_dtype(dt, fn);
+    if (st) return st;
+    if (dt == GR_FP8_E4M3) return fail(GR_ERROR_NOT_SUPPORTED, "%s: the HC calls take fp32 or bf16", fn);
+    return GR_SUCCESS;
+}
+
+void fill_hc(grk::HcArgs &a, const gr_hc_layer *L) {
+    a.n = L->n; a.d = L->d; a.mode = L->mode; a.iters = L->sinkhorn_iters;
+    a.eps = L->eps; a.lam_m = L->lambda_mix; a.lam_c = L->lambda_comb; a.lam_r = L->lambda_res;
+    a.gamma = L->gamma; a.w_norm = L->w_norm; a.w_proj = L->w_proj; a.h_static = L->h_static;
+}
+
+}  // namespace
+
+extern "C" {
+
+gr_status gr_hc_read(const void *state, gr_dtype dt, int64_t N, const gr_hc_layer *L, void *u,
+                     float *coeff, void *stream) {
+    const char *fn = "gr_hc_read";
+    gr_status st;
+    if ((st = check_hc_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_hc_layer(L, dt, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(u, "u", fn)) ||
+        (st = check_ptr(coeff, "coeff", fn)))
+        return st;
+    grk::HcArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.do_read = true;
+    a.state = const_cast<void *>(state);
+    a.N = N;
+    fill_hc(a, L);
+    a.u = u; a.coeff_out = coeff;
+    (void)hipGetLastError();
+    return launched(grk::launch_hc(a, (hipStream_t)stream, force_generic()), fn);
+}
+
+gr_status gr_hc_write(void *state, const void *y, const float *coeff, gr_dtype dt, int64_t N,
+                      int32_t n, int32_t d, void *stream) {
+    const char *fn = "gr_hc_write";
+    gr_status st;
+    if ((st = check_hc_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if (n < 1 || n > 8) return fail(GR_ERROR_INVALID_VALUE, "%s: n = %d outside 1..8", fn, n);
+    if ((st = check_width(dt, d, fn))) return st;
+    if ((int64_t)n * d > (1 << 24)) return fail(GR_ERROR_NOT_SUPPORTED, "%s: n*d too large", fn);
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) ||
+        (st = check_ptr(coeff, "coeff", fn)))
+        return st;
+    grk::HcArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.do_write = true;
+    a.state = state; a.y = y; a.coeff_in = coeff;
+    a.N = N; a.n = n; a.d = d;
+    (void)hipGetLastError();
+    return launched(grk::launch_hc(a, (hipStream_t)stream, force_generic()), fn);
+}
+
+gr_status gr_hc_fused_write_read(void *state, const void *y, const float *coeff_in, gr_dtype dt,
+                                 int64_t N, const gr_hc_layer *next, void *u_next, float *coeff_next,
+                                 void *stream) {
+    const char *fn = "gr_hc_fused_write_read";
+    gr_status st;
+    if ((st = check_hc_dtype(dt, fn)) || (st = check_tokens(N, fn))) return st;
+    if (N == 0) return ok();
+    if ((st = check_hc_layer(next, dt, fn))) return st;
+    if ((st = check_ptr(state, "state", fn)) || (st = check_ptr(y, "y", fn)) ||
+        (st = check_ptr(coeff_in, "coeff_in", fn)) || (st = check_ptr(u_next, "u_next", fn)) ||
+        (st = check_ptr(coeff_next, "coeff_next", fn)))
+        return st;
+    grk::HcArgs a{};
+    a.bf16 = dt == GR_BF16;
+    a.do_write = true; a.do_read = true;
+    a.state = state; a.y = y; a.coeff_in = coeff_in;
+    a.N = N;
+    fill_hc(a, next);
+    a.u = u_next; a.coeff_out = coeff_next;
+    (void)hipGetLastError();
+    return launched(grk::launch_hc(a, (hipStream_t)stream, force_generic()), fn);
+}
+
 gr_status gr_device_error_word(uint32_t *word, int reset) {
     const char *fn = "gr_device_error_word";
     if (!word) return fail(GR_ERROR_INVALID_VALUE, "%s: word is NULL", fn);

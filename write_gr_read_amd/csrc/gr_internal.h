@@ -52,6 +52,26 @@ bool cluster_path_ok(const ReadArgs &a);
 hipError_t launch_cluster(const ReadArgs &a, hipStream_t st);
 hipError_t cluster_error_word(uint32_t *word, bool reset);
 
+// Hyper-Connections / mHC (gr_hc.hip); validated by the API.
+struct HcArgs {
+    bool bf16;                 // state, y, u, gains and P in bf16 (else fp32)
+    bool do_write, do_read;
+    void *state;               // [N][n][d]
+    const void *y;             // [N][d]          (write)
+    const float *coeff_in;     // [N][n + n*n]    (write)
+    const void *gamma;         // [n][d]          (read)
+    const void *w_norm;        // [d]
+    const void *w_proj;        // [n+2][d]
+    const float *h_static;     // [2n + n*n]
+    void *u;                   // [N][d]
+    float *coeff_out;          // [N][n + n*n]
+    int64_t N;
+    int n, d, mode, iters;
+    float eps, lam_m, lam_c, lam_r;
+};
+bool hc_fast_ok(const HcArgs &a);
+hipError_t launch_hc(const HcArgs &a, hipStream_t st, bool force_generic);
+
 // MFMA fast path for the bf16 widened state (gr_fast.hip).
 bool fast_path_ok(const ReadArgs &a);
 size_t fast_workspace_bytes(const ReadArgs &a);   // workspace bytes of this call's fast path

@@ -18,6 +18,9 @@ Recipe (the same for every workload):
     channel), ``gamma [n, d]``, ``W_down [r, n*d]``, ``W_up [n*d, r]``,
     ``W_write [n, n*d]`` (the vec index of branch i, channel c is ``i*d + c``).
 
+Hyper-Connections / mHC inputs (make_hc_inputs) follow the same recipe with
+their own parameter streams (gamma, w_norm, w_proj, h_static).
+
 Workload sizes are the synthetic configurations the GR measurements use
 (tiny fp32 read/write, n=1 fused add+RMSNorm, prefill, decode, a 32-sublayer
 chain, the prefill shape with an e4m3 state, and the pages' own model shape
@@ -205,6 +208,69 @@ def make_variant_inputs(N: int, n: int, d: int, dtype: str = "bf16", seed: int =
     s = normal(rngs[4], (n, d), 0.25, mean=1.0, dtype="f32")
     w = normal(rngs[5], (d,), 0.01, mean=1.0, dtype=pdt)
     return VariantInputs(N, n, d, dtype, X, e, y, h, s, w)
+
+
+@dataclass
+class HCLayer:
+    """One Hyper-Connections / mHC module's parameters (CPU tensors).  The
+    fields match the library's ``gr_hc_layer``."""
+    mode: str                  # "hc" (tanh) or "mhc" (sigmoid, twice sigmoid, Sinkhorn)
+    gamma: torch.Tensor        # [n, d]   per-branch gains (state dtype)
+    w_norm: torch.Tensor       # [d]      gain of the block's RMSNorm (state dtype)
+    w_proj: torch.Tensor       # [n+2, d] W_mix, W_comb, columns of W_res (state dtype)
+    h_static: torch.Tensor     # [2n + n*n] fp32: H^s_mix | H^s_comb | H^s_res
+    lam: tuple                 # (lambda_mix, lambda_comb, lambda_res)
+    iters: int = 20
+    eps: float = 1e-6
+
+    def to(self, device) -> "HCLayer":
+        return HCLayer(self.mode, self.gamma.to(device), self.w_norm.to(device), self.w_proj.to(device),
+                       self.h_static.to(device), self.lam, self.iters, self.eps)
+
+
+@dataclass
+class HCInputs:
+    N: int
+    n: int
+    d: int
+    dtype: str
+    X: torch.Tensor            # [N, n, d]
+    y: torch.Tensor            # [N, d]
+    params: List[HCLayer] = field(default_factory=list)
+
+
+def hc_static_terms(mode: str, n: int, layer: int = 0) -> torch.Tensor:
+    """Static terms that start the widened network as the Pre-Norm one: HC takes
+    e_(layer mod n), 1 and I for H_mix, H_comb and H_res; mHC takes logits 0
+    (sigmoid 1/2), 0 (twice sigmoid 1) and a gap of 8 on the diagonal of H_res."""
+    eye = torch.eye(n, dtype=torch.float32)
+    if mode == "hc":
+        return torch.cat([eye[layer % n], torch.ones(n), eye.reshape(-1)])
+    return torch.cat([torch.zeros(n), torch.zeros(n), (8.0 * eye).reshape(-1)])
+
+
+def make_hc_inputs(N: int, n: int, d: int, mode: str = "mhc", dtype: str = "bf16", seed: int = 0,
+                   n_param_sets: int = 2, x_std: float = 1.0, y_std: float = 0.05,
+                   w_std: float = 0.02, gamma_std: float = 0.01, lam=(1.0, 1.0, 1.0),
+                   static: str = "init", branch_scale: Optional[Sequence[float]] = None,
+                   iters: int = 20) -> HCInputs:
+    """Seeded inputs of the HC / mHC calls.  Child streams: X, y, then per
+    parameter set (gamma, w_norm, w_proj, h_static).  ``static`` = "init" uses
+    hc_static_terms (layer = the set's index), "random" draws N(0, 1) fp32."""
+    children = np.random.SeedSequence(seed).spawn(2 + 4 * n_param_sets)
+    rngs = [np.random.Generator(np.random.PCG64(c)) for c in children]
+    X = normal(rngs[0], (N, n, d), x_std, dtype=dtype, scale_rows=branch_scale)
+    y = normal(rngs[1], (N, d), y_std, dtype=dtype)
+    params = []
+    for p in range(n_param_sets):
+        g_rng, w_rng, p_rng, h_rng = rngs[2 + 4 * p: 6 + 4 * p]
+        gamma = normal(g_rng, (n, d), gamma_std, mean=1.0, dtype=dtype)
+        w_norm = normal(w_rng, (d,), gamma_std, mean=1.0, dtype=dtype)
+        w_proj = normal(p_rng, (n + 2, d), w_std, dtype=dtype)
+        hs = (hc_static_terms(mode, n, p) if static == "init"
+              else normal(h_rng, (2 * n + n * n,), 1.0, dtype="f32"))
+        params.append(HCLayer(mode, gamma, w_norm, w_proj, hs, tuple(float(v) for v in lam), iters))
+    return HCInputs(N, n, d, dtype, X, y, params)
 
 
 def make_device_state(N: int, n: int, d: int, dtype: str = "bf16", seed: int = 0, device="cuda:0",
