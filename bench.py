@@ -60,12 +60,12 @@ def gate_flops(N, n, d, r, has_write=True):
 FUSED_KERNEL_SOURCES = ("gr_device.h", "gr_fast_common.h", "gr_fast.hip", "gr_fast_k1.hip", "gr_fast_k2.hip")
 
 
-def kernel_source_digest():
-    """Digest of the fused call's kernel sources, to tell whether stored
-    counters still apply."""
+def kernel_source_digest(files=FUSED_KERNEL_SOURCES):
+    """Digest of a call's kernel sources, to tell whether stored counters
+    still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "write_gr_read_amd", "csrc")
-    for f in FUSED_KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -81,7 +81,7 @@ def stored_traffic(kernel_name):
     except (OSError, ValueError):
         return None
     rec = data.get(kernel_name)
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    if not rec or rec.get("source_digest") != kernel_source_digest(tuple(rec.get("sources", FUSED_KERNEL_SOURCES))):
         return None
     return rec.get("bytes_per_launch")
 
@@ -124,6 +124,24 @@ def cpu_baseline(Xin, threads, n_tokens, single_tokens=1024):
                       f"{dt:.2f} s wall, ~{dt * threads:.0f} thread-seconds)",
             "cpu_model": cpu_model(), "cores_in_affinity_mask": len(os.sched_getaffinity(0)),
             "single_thread": {"value": m / dt1, "unit": "tokens/s", "tokens": m, "seconds": dt1}}
+
+
+def copy_probe(gr, torch, dev, stream):
+    """What a plain 16-byte copy kernel moves on this GPU (read + write of
+    1 GiB): context for the HBM fractions, and the known-size reference that
+    scales the FETCH_SIZE / WRITE_SIZE counters of the traffic profiles."""
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        gr.copy(a, b)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(10):
+        gr.copy(a, b)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return 2 * nbytes / (start.elapsed_time(stop) / 10 * 1e-3) / 1e9
 
 
 def timed(fn, steps, warmup, stream):
@@ -362,6 +380,29 @@ def bench_other(which, args, dev):
                     {"workload": W["name"], "N": N, "d": d, "n": n, "r": r, "sublayers": len(ps)},
                     gr_ms_per_pass=gr_ms, f_standin_ms_per_pass=len(ps) * ms_f,
                     roofline=roofline(alg, gr_ms, "GR calls of the chain (F excluded)"))
+    if which in ("hc_mhc", "hc_tanh"):
+        # Hyper-Connections (tanh) / mHC (sigmoid, Sinkhorn 20) on the prefill
+        # shape: the fused write + read, one pass over the state
+        mode = "mhc" if which == "hc_mhc" else "hc"
+        N, n, d = 16384, 4, 4096
+        Xin = inputs.make_hc_inputs(N, n, d, mode, "bf16", seed=11000 + (mode == "mhc"),
+                                    branch_scale=(1.0, 0.5, 2.0, 1.0))
+        X, y = Xin.X.to(dev), Xin.y.to(dev)
+        p0, p1 = Xin.params[0].to(dev), Xin.params[1].to(dev)
+        _, c_in = gr.hc_read(X, p0)                     # untimed: the write's coefficients
+        u = torch.empty((N, d), dtype=X.dtype, device=dev)
+        c_out = torch.empty_like(c_in)
+        steps = args.steps if args.steps_given else 50
+        ms = timed(lambda: gr.hc_fused_write_read(X, y, c_in, p1, u=u, coeff=c_out), steps, args.warmup, stream)
+        nc = n + n * n
+        alg = N * (2 * n * d * 2 + 2 * d * 2 + 2 * nc * 4) + (n * d + d + (n + 2) * d) * 2 + (2 * n + n * n) * 4
+        log(f"{which}: {ms * 1e3:.1f} us/call, {alg / ms / 1e6:.0f} GB/s algorithmic")
+        name = "mHC" if mode == "mhc" else "HC"
+        return line(f"{name} fused write+read tokens/s (N={N}, d={d}, n={n}, bf16 state)",
+                    N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
+                    {"workload": f"hc_{mode}_prefill_bf16", "N": N, "d": d, "n": n, "mode": mode,
+                     "sinkhorn_iters": Xin.params[1].iters if mode == "mhc" else 0},
+                    roofline=roofline(alg, ms, f"gr_hc_fused_write_read ({name})", stored_traffic(f"hc_{mode}")))
     raise ValueError(which)
 
 
@@ -376,13 +417,13 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384,
                     help="tokens of the workload the CPU baseline runs (about 20 thread-seconds at 16384)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="time the copy probe beside the headline (the default; kept for older command lines)")
+                    help="time the copy probe (always beside the headline; with --workload, before it)")
     ap.add_argument("--no-copy-probe", action="store_true", help="skip the copy probe")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the decode / add+RMSNorm / chain / single-pass keys of the default line")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm",
-                             "chain", "tiny", "variants", "all"])
+                             "chain", "tiny", "variants", "hc_mhc", "hc_tanh", "all"])
     args = ap.parse_args()
     args.steps_given = "--steps" in sys.argv
 
@@ -399,8 +440,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload != "prefill":
         names = (["prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm", "chain", "tiny",
-                  "variants"]
+                  "variants", "hc_mhc", "hc_tanh"]
                  if args.workload == "all" else [args.workload])
+        if args.copy_probe:
+            log(f"copy probe: {copy_probe(gr, torch, dev, torch.cuda.current_stream(dev)):.0f} GB/s")
         for w in names:
             res = bench_other(w, args, dev)
             for one in (res if isinstance(res, list) else [res]):
@@ -467,28 +510,16 @@ def main():
                                        args.steps, stream)))
 
     if not args.no_copy_probe:
-        # context: what a plain 16-byte copy kernel moves on this machine (read + write)
-        nbytes = 1 << 30
-        a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            gr.copy(a, b)
-        start.record(stream)
-        for _ in range(10):
-            gr.copy(a, b)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        cms = start.elapsed_time(stop) / 10
-        out["copy_probe_GBps"] = 2 * nbytes / (cms * 1e-3) / 1e9
+        out["copy_probe_GBps"] = copy_probe(gr, torch, dev, stream)
         log(f"copy probe: {out['copy_probe_GBps']:.0f} GB/s (read + write of 1 GiB)")
-        del a, b
 
     if not args.no_others:
         # the other configurations of the workload set, one key each with its
         # own roofline: decode (us/call), the n = 1 fused add + RMSNorm, the
-        # 32-sublayer chain, and the single-pass kernel on this same prefill call
+        # 32-sublayer chain, mHC and HC on the prefill shape, and the single-pass
+        # kernel on this same prefill call
         others = {}
-        for w in ("decode", "addnorm", "chain"):
+        for w in ("decode", "addnorm", "chain", "hc_mhc", "hc_tanh"):
             log(f"workload {w} ...")
             res = bench_other(w, args, dev)
             keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
