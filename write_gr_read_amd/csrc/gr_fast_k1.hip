@@ -101,9 +101,25 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 
     const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
-    const int64_t tile = (b / 8 / (n * S)) * 8 + (b % 8);
-    const int br = (int)((b / 8) % (n * S)) / S;
-    const int split = (int)((b / 8) % S);
+    // blockIdx % 8 is the XCD (round-robin dispatch).  With four branches, XCD
+    // x takes branches 2 (x / 4) and 2 (x / 4) + 1 of the tiles T = x mod 4
+    // (mod 4): an XCD then streams the W' of two branches (2.5 MB at the
+    // prefill shape, within its 4 MB L2) instead of all four, and the two
+    // workgroups of a tile on it (consecutive slots) still share y in L2.
+    // Otherwise the n workgroups of a tile share an XCD.
+    int64_t tile;
+    int br, split;
+    if (n == 4) {
+        const int x = (int)(b % 8);
+        const int64_t j = b / 8;
+        split = (int)(j % S);
+        br = 2 * (x / 4) + (int)((j / S) % 2);
+        tile = (j / (2 * S)) * 4 + (x % 4);
+    } else {
+        tile = (b / 8 / (n * S)) * 8 + (b % 8);
+        br = (int)((b / 8) % (n * S)) / S;
+        split = (int)((b / 8) % S);
+    }
     if (tile >= sh.tiles) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -481,9 +497,25 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
 
     const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
-    const int64_t tile = (b / 8 / (n * S)) * 8 + (b % 8);
-    const int br = (int)((b / 8) % (n * S)) / S;
-    const int split = (int)((b / 8) % S);
+    // blockIdx % 8 is the XCD (round-robin dispatch).  With four branches, XCD
+    // x takes branches 2 (x / 4) and 2 (x / 4) + 1 of the tiles T = x mod 4
+    // (mod 4): an XCD then streams the W' of two branches (2.5 MB at the
+    // prefill shape, within its 4 MB L2) instead of all four, and the two
+    // workgroups of a tile on it (consecutive slots) still share y in L2.
+    // Otherwise the n workgroups of a tile share an XCD.
+    int64_t tile;
+    int br, split;
+    if (n == 4) {
+        const int x = (int)(b % 8);
+        const int64_t j = b / 8;
+        split = (int)(j % S);
+        br = 2 * (x / 4) + (int)((j / S) % 2);
+        tile = (j / (2 * S)) * 4 + (x % 4);
+    } else {
+        tile = (b / 8 / (n * S)) * 8 + (b % 8);
+        br = (int)((b / 8) % (n * S)) / S;
+        split = (int)((b / 8) % S);
+    }
     if (tile >= sh.tiles) return;
 
     const int tid = threadIdx.x, lane = tid & 63;

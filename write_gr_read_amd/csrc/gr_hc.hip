@@ -156,7 +156,7 @@ __device__ __forceinline__ void hc_load(HcTok<NB, K> &t, const bf16_t *__restric
 #pragma unroll
         for (int i = 0; i < NB; ++i)
             t.R[i][k] = *reinterpret_cast<const u32x4 *>(S + (tok * NB + i) * d + 8 * q);
-        if (WRITE) t.Y[k] = *reinterpret_cast<const u32x4 *>(Yp + tok * d + 8 * q);
+        if (WRITE) t.Y[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(Yp + tok * d + 8 * q));
     }
     if (WRITE) t.C = cin[tok * NC + min(ttid & 63, NC - 1)];
 }
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(kHcFastThreads, 1) k_hc_fast(HcArgs a) {
                     }
                     o[e] = pack_bf16x2(bf16_lo(wn[e]) * (xl * rx), bf16_hi(wn[e]) * (xh * rx));
                 }
-                if (live && qq < D8) *reinterpret_cast<u32x4 *>(U + tok * d + 8 * qq) = o;
+                if (live && qq < D8) __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(U + tok * d + 8 * qq));
             }
 
             // ---- H_comb and H_res: one wave of the team, one coefficient per lane
