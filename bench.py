@@ -402,7 +402,7 @@ def bench_other(which, args, dev):
                     N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
                     {"workload": f"hc_{mode}_prefill_bf16", "N": N, "d": d, "n": n, "mode": mode,
                      "sinkhorn_iters": Xin.params[1].iters if mode == "mhc" else 0},
-                    roofline=roofline(alg, ms, f"gr_hc_fused_write_read ({name})", stored_traffic(f"hc_{mode}")))
+                    roofline=roofline(alg, ms, f"gr_hc_fused_write_read ({name})", stored_traffic(which)))
     raise ValueError(which)
 
 
