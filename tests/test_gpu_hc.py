@@ -210,3 +210,31 @@ def test_hc_empty_and_argument_errors():
         gr.hc_read(Xin.X.to(DEV), bad)
     with pytest.raises(TypeError):
         gr.hc_read(Xin.X.to(DEV).to(torch.float8_e4m3fn), p)
+
+
+def test_hc_past_2_to_31_elements():
+    """N x n x d above 2^31 elements (131372 x 4 x 4096 bf16, a 4.3 GB state):
+    the one-pass kernel's token offsets pass 32 bits.  Tokens on both sides of
+    the boundary (token 131072 starts at element 2^31) are compared with the
+    oracle, which gets those rows of the same device tensors."""
+    N, n, d = 131372, 4, 4096
+    P = inputs.make_hc_inputs(1, n, d, "mhc", "bf16", seed=94, lam=(0.8, 1.3, 1.1), static="random",
+                              w_std=0.05).params
+    X, y = inputs.make_device_state(N, n, d, "bf16", seed=95, device=DEV)
+    idx = np.unique(np.concatenate([[0, 1, 65535, 131070, 131071, 131072, 131073, N - 2, N - 1],
+                                    sample_tokens(N, 24, seed=96)]))
+    ti = torch.from_numpy(idx).to(DEV)
+    Xs = X[ti].cpu()
+    _, c0 = gr.hc_read(X, P[0].to(DEV))
+    _, oc0 = orc_read(Xs, P[0], "bf16")
+    check("hc 2^31 read coeff (sampled)", c0[ti].cpu(), oc0, "bf16")
+    cs = c0[ti].cpu()
+    u1, c1 = gr.hc_fused_write_read(X, y, c0, P[1].to(DEV))
+    Xw = X[ti].cpu()
+    oRw = oracle.hc_write(Xs, y[ti].cpu(), cs, "bf16")
+    check_sum_store("hc 2^31 fused state (sampled)", Xw, oRw, write_terms(Xs, y[ti].cpu(), cs), n, "bf16")
+    ou1, oc1 = orc_read(Xw, P[1], "bf16")
+    check("hc 2^31 fused u (sampled)", u1[ti].cpu(), ou1, "bf16")
+    check("hc 2^31 fused coeff (sampled)", c1[ti].cpu(), oc1, "bf16")
+    del X, y, u1, c0, c1
+    torch.cuda.empty_cache()

@@ -499,10 +499,10 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
     const int64_t b = blockIdx.x;
     // blockIdx % 8 is the XCD (round-robin dispatch).  With four branches, XCD
     // x takes branches 2 (x / 4) and 2 (x / 4) + 1 of the tiles T = x mod 4
-    // (mod 4): an XCD then streams the W' of two branches (2.5 MB at the
-    // prefill shape, within its 4 MB L2) instead of all four, and the two
-    // workgroups of a tile on it (consecutive slots) still share y in L2.
-    // Otherwise the n workgroups of a tile share an XCD.
+    // (mod 4), as kernel 1's narrow walk does: an XCD streams the W rows of two
+    // branches instead of four, and the two workgroups of a tile on it
+    // (consecutive slots) share y in L2.  Otherwise the n workgroups of a tile
+    // share an XCD.
     int64_t tile;
     int br, split;
     if (n == 4) {
