@@ -394,6 +394,9 @@ def bench_other(which, args, dev):
         c_out = torch.empty_like(c_in)
         steps = args.steps if args.steps_given else 50
         ms = timed(lambda: gr.hc_fused_write_read(X, y, c_in, p1, u=u, coeff=c_out), steps, args.warmup, stream)
+        # the same work as two calls (write, then read): two passes over the state
+        ms_w = timed(lambda: gr.hc_write(X, y, c_in), steps, args.warmup, stream)
+        ms_r = timed(lambda: gr.hc_read(X, p1, u=u, coeff=c_out), steps, args.warmup, stream)
         nc = n + n * n
         alg = N * (2 * n * d * 2 + 2 * d * 2 + 2 * nc * 4) + (n * d + d + (n + 2) * d) * 2 + (2 * n + n * n) * 4
         log(f"{which}: {ms * 1e3:.1f} us/call, {alg / ms / 1e6:.0f} GB/s algorithmic")
@@ -402,7 +405,8 @@ def bench_other(which, args, dev):
                     N / (ms * 1e-3), "tokens/s", steps, args.warmup, ms,
                     {"workload": f"hc_{mode}_prefill_bf16", "N": N, "d": d, "n": n, "mode": mode,
                      "sinkhorn_iters": Xin.params[1].iters if mode == "mhc" else 0},
-                    roofline=roofline(alg, ms, f"gr_hc_fused_write_read ({name})", stored_traffic(which)))
+                    roofline=roofline(alg, ms, f"gr_hc_fused_write_read ({name})", stored_traffic(which)),
+                    write_only_ms=ms_w, read_only_ms=ms_r, unfused_ms=ms_w + ms_r)
     raise ValueError(which)
 
 
@@ -523,7 +527,8 @@ def main():
             log(f"workload {w} ...")
             res = bench_other(w, args, dev)
             keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
-                    "warm", "cold", "graph_replay_us_per_call", "gr_ms_per_pass", "f_standin_ms_per_pass")
+                    "warm", "cold", "graph_replay_us_per_call", "gr_ms_per_pass", "f_standin_ms_per_pass",
+                    "write_only_ms", "read_only_ms", "unfused_ms")
             others[w] = {k: res[k] for k in keep if k in res}
         os.environ["GR_KERNEL_VARIANT"] = "single"
         try:

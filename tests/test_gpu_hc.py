@@ -238,3 +238,30 @@ def test_hc_past_2_to_31_elements():
     check("hc 2^31 fused coeff (sampled)", c1[ti].cpu(), oc1, "bf16")
     del X, y, u1, c0, c1
     torch.cuda.empty_cache()
+
+
+def test_hc_two_streams():
+    """Calls queued on two streams at once (the HC kernels share no library
+    memory): every result equals the same call made alone."""
+    A = inputs.make_hc_inputs(700, 4, 4096, "mhc", "bf16", seed=81, static="random", w_std=0.05)
+    B = inputs.make_hc_inputs(300, 2, 2048, "hc", "bf16", seed=82, static="random", w_std=0.05)
+    cins = [torch.rand(700, 20) + 0.25, torch.rand(300, 6) + 0.25]
+    alone = []
+    for Xin, cin in zip((A, B), cins):
+        R = Xin.X.to(DEV)
+        u, c = gr.hc_fused_write_read(R, Xin.y.to(DEV), cin.to(DEV), Xin.params[1].to(DEV))
+        torch.cuda.synchronize()
+        alone.append((R, u, c))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for Xin, cin, st in zip((A, B), cins, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            p, y, ci = Xin.params[1].to(DEV), Xin.y.to(DEV), cin.to(DEV)
+            for _ in range(3):
+                R = Xin.X.to(DEV)
+                u, c = gr.hc_fused_write_read(R, y, ci, p)
+            outs.append((R, u, c))
+    torch.cuda.synchronize()
+    for (R1, u1, c1), (R2, u2, c2) in zip(alone, outs):
+        assert torch.equal(R1, R2) and torch.equal(u1, u2) and torch.equal(c1, c2)

@@ -10,7 +10,9 @@ If the library is missing the first call raises.
 GR ("Paper reading: Qwen3.8 Flash Next", part 2 Residual, sec. 4):
   read   u = (1/n) sum_i G_i (.) RMSNorm(R_i; gamma_i), s = 2 sigmoid(...)
   write  R_i += s_i y
-  fused  write of sublayer l, then read of sublayer l+1, one pass over R.
+  fused  write of sublayer l, then read of sublayer l+1, in one call (by
+         default two kernels over R: the write with the projections, then
+         the gated combine reading R' back).
 n = 1 fused residual add + RMSNorm: "Residual" (LLM inference), sec. 3.3.
 Hyper-Connections / mHC (same paper reading, sec. 2; "DepthBench", sec. 2.5):
   hc_read, hc_write, hc_fused_write_read with an ``HCLayer``.
