@@ -14,7 +14,8 @@
 //   S  streams its slice once: R' = R + s y (one fp32 FMA, rounded to the
 //      state dtype, stored), R' kept in LDS, partial sums of squares;
 //   M  projects its slice: P_i = W^(i) (gamma_i . R'_i) for the W_down rows
-//      and the W_write rows (MFMA, gamma . R' split into bf16 hi + lo);
+//      and the W_write rows (MFMA, gamma . R' split into bf16 hi + lo; with
+//      eight waves, two waves share a branch, each taking half its channels);
 //   Q  gathers every member's sums of squares -> rho_i, and publishes
 //      Q = sum_i rho_i P_i (one row per W_down / W_write row);
 //   R  reduces, for the token(s) it owns, the members' Q rows ->
@@ -22,12 +23,10 @@
 //   C  gathers a for the tile, forms its channels' gate logits (MFMA up
 //      projection from resident W_up rows), G = sigmoid, and
 //      u_c = (1/n) sum_i G_ic gamma_ic rho_i R'_ic from the R' still in LDS.
-// The stages of consecutive tiles are software-pipelined, iteration k
-// running S(k), R(k-1), C(k-2), M(k), Q(k): each wait on the other members
-// comes a stage or more after the values it waits for were published.  A
-// wave's memory-count waits complete in issue order, so the exchange loads
-// that R and C wait on are issued before the next tile's prefetch (then
-// waiting on them does not wait for the prefetch).
+// The stages of consecutive tiles are software-pipelined over three tiles,
+// iteration k running R(k-2), S(k), M(k-1), Q(k-1), C(k-2), so every wait on
+// the other members comes at least a stage, mostly a whole iteration, after
+// the values it waits for were published (the walk below).
 //
 // Exchange.  Values cross workgroups as 8-byte records (value bits, tag) in a
 // library-owned device array (`exchange`); a record is valid when its tag is
@@ -43,9 +42,10 @@
 // device error word is set and the call's results are not to be trusted.
 //
 // The launch must have all 32 workgroups of every cluster resident at once:
-// 256 workgroups of 256 threads with ~150 KB of LDS, one per CU, on a GPU with
-// 8 XCDs of 32 CUs; the host checks this before choosing the path, and calls
-// of this path on one GPU are serialised by the host (they share the array).
+// 256 workgroups (512 threads for 128-channel slices, 256 for 64-channel
+// ones) with ~150 KB / ~100 KB of LDS, one per CU, on a GPU with 8 XCDs of 32
+// CUs; the host checks this before choosing the path, and calls of this path
+// on one GPU are serialised by the host (they share the array).
 #include "gr_device.h"
 #include "gr_internal.h"
 
@@ -59,7 +59,10 @@ namespace grk {
 namespace cluster {
 
 constexpr int kMembers = 32;     // workgroups per cluster (CUs per XCD)
-constexpr int kThreads = 256;    // 4 waves, one per SIMD (512 registers each)
+// workgroup size: 8 waves (two per SIMD, 256 registers each) for 128-channel
+// slices, 4 waves (one per SIMD) for 64-channel slices
+constexpr int waves_of(int cw) { return cw == 128 ? 8 : 4; }
+constexpr int threads_of(int cw) { return 64 * waves_of(cw); }
 constexpr int kMaxClusters = 8;
 constexpr int kMaxNRB = 5;       // projection rows r + nw <= 80 (16-row MFMA blocks)
 constexpr int kMaxRKS = 2;       // gate rank r <= 64 (32-wide MFMA k-steps)
@@ -135,30 +138,37 @@ template <bool F8> struct St { using T = bf16_t; using V = u32x4; };
 template <> struct St<true> { using T = fp8_t; using V = u32x2; };
 
 template <int CW, bool FUSED>
-__global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
+__global__ void __launch_bounds__(threads_of(CW), 1) k_cluster(KArgs a) {
     constexpr bool F8 = false;
+    constexpr int WAVES = waves_of(CW);
+    constexpr int kThreads = threads_of(CW);
+    constexpr int WPB = WAVES / 4;         // waves per branch in the down projection
     constexpr int PCS = CW / 8;            // 8-channel pieces per (token, branch) of a slice
     constexpr int TOK = 32;                // tokens per tile
     constexpr int SJ = TOK * PCS / kThreads;  // (token, piece) pairs per thread in stage S (1 or 2)
     constexpr int KS = CW / 32;            // MFMA k-steps per branch slice
+    constexpr int KSW = KS / WPB;          // ... per wave (the wave's part of its branch's channels)
+    constexpr int CWW = CW / WAVES;        // channels per wave in the up projection and combine
     constexpr int NTG = TOK / 16;          // 16-token MFMA column groups per tile
-    constexpr int NB2 = CW / 16;           // up-projection row blocks per wave (4 branches x CW/4 channels)
+    constexpr int NB2 = CWW / 4;           // up-projection row blocks per wave (4 branches x CWW channels)
     constexpr int PR = 4 * CW * 2 + 16;    // LDS bytes per token of an R' tile (padded: conflict-free MFMA reads)
     constexpr int RKM = 64;                // act columns per token (gate rank <= 64)
     constexpr int AP = RKM * 2 + 16;       // LDS bytes per token of an act plane
     constexpr int SPX = 72;                // staging floats per (branch, token): rows (<= 68) + padding
-    constexpr int QM = 16;                 // members summed per reduction item (two items per row)
+    constexpr int QI = kThreads / 128;     // reduction items per projection row (QI rows <= kThreads)
+    constexpr int QM = kMembers / QI;      // members summed per reduction item
+    constexpr int TPT = kThreads / TOK;    // threads per token when publishing the projections
     constexpr int NSS = TOK * kMembers / kThreads;  // (token, member) sum-of-squares records per thread
     constexpr int NAI = TOK * (RKM / 2) / kThreads; // act record pairs per thread
-    static_assert(SJ >= 1 && NSS >= 1 && NAI >= 1, "tile shape");
+    static_assert(SJ >= 1 && NSS >= 1 && NAI >= 1 && KSW >= 1 && NB2 >= 1 && QI * QM == kMembers, "tile shape");
     using T = typename St<F8>::T;
     using SV = typename St<F8>::V;
 
     // ---- LDS
-    constexpr int kRBytes = 3 * TOK * PR;          // three R' tiles: current, previous, the one before
+    constexpr int kRBytes = 3 * TOK * PR;          // three R' tiles (written, projected, combined)
     constexpr int kRhoBytes = 3 * TOK * 16;
     constexpr int kStgBytes = 4 * TOK * SPX * 4;
-    constexpr int kRedBytes = 2 * SPX * 4;
+    constexpr int kRedBytes = QI * SPX * 4;
     constexpr int kActL = 2 * TOK * AP;
     static_assert(kStgBytes >= TOK * kMembers * 16, "the sums-of-squares gather shares the staging area");
     __shared__ __attribute__((aligned(16))) unsigned char
@@ -200,22 +210,23 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         *reinterpret_cast<u32x4 *>(gml + i * CW + 8 * q) =
             *reinterpret_cast<const u32x4 *>(a.gamma + (int64_t)i * d + c0 + 8 * q);
     }
-    // down projection A fragments: wave = branch bi; row j = 16 blk + l16 of
-    // (W_down ; W_write ; 0), k = channels c0 + 32 ks + 8 g .. + 7 of branch bi
-    const int bi = wave;
-    u32x4 af[kMaxNRB][KS];
+    // down projection A fragments: wave = (branch bi, part kp of its channels);
+    // row j = 16 blk + l16 of (W_down ; W_write ; 0), k = channels
+    // c0 + 32 (KSW kp + ks) + 8 g .. + 7 of branch bi
+    const int bi = wave / WPB, kp = wave % WPB;
+    u32x4 af[kMaxNRB][KSW];
 #pragma unroll
     for (int blk = 0; blk < kMaxNRB; ++blk) {
         const int j = 16 * blk + l16;
         const bf16_t *src = j < r ? a.wd + (int64_t)j * nd : (j < rows ? a.ww + (int64_t)(j - r) * nd : nullptr);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KSW; ++ks) {
             af[blk][ks] = u32x4{0u, 0u, 0u, 0u};
             if (src && blk < nrb)
-                af[blk][ks] = *reinterpret_cast<const u32x4 *>(src + (int64_t)bi * d + c0 + 32 * ks + 8 * g);
+                af[blk][ks] = *reinterpret_cast<const u32x4 *>(src + (int64_t)bi * d + c0 + 32 * (KSW * kp + ks) + 8 * g);
         }
     }
-    // up projection A fragments: wave w owns local channels w*CW/4 .. + CW/4 - 1; block b,
+    // up projection A fragments: wave w owns local channels w*CWW .. + CWW - 1; block b,
     // row 4 g' + m (g' = l16 / 4, m = l16 % 4) is (branch m, channel NB2 g' + b of the
     // wave), k = 32 ks + 8 g .. + 7 (zero at k >= r)
     u32x4 au[NB2][kMaxRKS];
@@ -223,7 +234,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         const int gp = l16 >> 2, m = l16 & 3;
 #pragma unroll
         for (int b = 0; b < NB2; ++b) {
-            const int ch = c0 + wave * (CW / 4) + NB2 * gp + b;
+            const int ch = c0 + wave * CWW + NB2 * gp + b;
             const bf16_t *src = a.wu + ((int64_t)m * d + ch) * r;
 #pragma unroll
             for (int ks = 0; ks < kMaxRKS; ++ks) {
@@ -291,7 +302,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         }
     };
 
-    // ---- stage M: down projection of branch bi for every token group of tile k
+    // ---- stage M: down projection of the wave's channels of branch bi for every
+    // token group of tile k
     f32x4 pacc[NTG][kMaxNRB];
     auto stage_M = [&](int k) __attribute__((always_inline)) {
         const unsigned char *slot = Rl + (k % 3) * TOK * PR;
@@ -301,9 +313,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
             for (int blk = 0; blk < kMaxNRB; ++blk) pacc[tgp][blk] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int t = 16 * tgp + l16;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 rv = *reinterpret_cast<const u32x4 *>(slot + t * PR + bi * CW * 2 + (32 * ks + 8 * g) * 2);
-                const u32x4 gv = *reinterpret_cast<const u32x4 *>(gml + bi * CW + 32 * ks + 8 * g);
+            for (int ks = 0; ks < KSW; ++ks) {
+                const int kg = KSW * kp + ks;
+                const u32x4 rv = *reinterpret_cast<const u32x4 *>(slot + t * PR + bi * CW * 2 + (32 * kg + 8 * g) * 2);
+                const u32x4 gv = *reinterpret_cast<const u32x4 *>(gml + bi * CW + 32 * kg + 8 * g);
                 u32x4 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -371,23 +384,38 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
             rhol[(k % 3) * TOK * 4 + e] = 1.0f / sqrtf(ss / (float)d + a.eps);
         }
         __syncthreads();
-        // scaled partials to the staging area [branch][t][row]
+        // scaled partials to the staging area [branch][t][row]; where two waves
+        // share a branch, the second writes and the first adds its own after a
+        // barrier (a + b: the same value in either order)
+        auto stage_partials = [&](bool add) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tgp = 0; tgp < NTG; ++tgp) {
-            const int t = 16 * tgp + l16;
-            const float rho = rhol[(k % 3) * TOK * 4 + t * 4 + bi];
+            for (int tgp = 0; tgp < NTG; ++tgp) {
+                const int t = 16 * tgp + l16;
+                const float rho = rhol[(k % 3) * TOK * 4 + t * 4 + bi];
 #pragma unroll
-            for (int blk = 0; blk < kMaxNRB; ++blk) {
-                const int row = 16 * blk + 4 * g;
-                if (blk < nrb && row < rows)
-                    *reinterpret_cast<f32x4 *>(stg + (bi * TOK + t) * SPX + row) = pacc[tgp][blk] * rho;
+                for (int blk = 0; blk < kMaxNRB; ++blk) {
+                    const int row = 16 * blk + 4 * g;
+                    if (blk < nrb && row < rows) {
+                        f32x4 *dst = reinterpret_cast<f32x4 *>(stg + (bi * TOK + t) * SPX + row);
+                        const f32x4 v = pacc[tgp][blk] * rho;
+                        *dst = add ? *dst + v : v;
+                    }
+                }
             }
+        };
+        if constexpr (WPB == 1) {
+            stage_partials(false);
+        } else {
+            static_assert(WPB == 2, "two waves per branch");
+            if (kp == 1) stage_partials(false);
+            __syncthreads();
+            if (kp == 0) stage_partials(true);
         }
         __syncthreads();
         // sum over branches (in order), publish as records [slot][t][member][rows]
-        static_assert(TOK * 8 == kThreads, "publish mapping: 8 threads per token");
-        const int t = tid >> 3;
-        for (int v = 2 * (tid & 7); v < rows; v += 16) {
+        static_assert(TOK * TPT == kThreads, "publish mapping: TPT threads per token");
+        const int t = tid / TPT;
+        for (int v = 2 * (tid % TPT); v < rows; v += 2 * TPT) {
             float q0 = 0.f, q1 = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -400,9 +428,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
     };
 
     // ---- stage R, first half: loads of the members' Q rows for this member's token;
-    // item tid = (half h, row v) sums members QM h .. QM h + QM - 1 (2 rows items <= kThreads)
+    // item tid = (part h, row v) sums members QM h .. QM h + QM - 1 (QI rows items <= kThreads)
     u32x2 qv[QM];
-    const int nqi = 2 * rows;
+    const int nqi = QI * rows;
     const int qi_v = tid < nqi ? tid % rows : 0, qi_h = tid < nqi ? tid / rows : 0;   // once per launch
     const uint32_t qi_base = (uint32_t)(((member * kMembers + QM * qi_h) * rows + qi_v) * 8);
     const uint32_t qi_mstride = (uint32_t)(rows * 8);
@@ -434,7 +462,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         const int64_t tok = tok0_of(k) + member;
         if (tid < rows) {
             const int v = tid;
-            const float q = red[v] + red[SPX + v];
+            float q = red[v];
+#pragma unroll
+            for (int h = 1; h < QI; ++h) q += red[h * SPX + v];
             if (v < r) {
                 const float av = -kLog2e * silu_f(q * inv_n);
                 const uint32_t off = act_off + (uint32_t)((((k & 1) * TOK + member) * RKM + v) * 8);
@@ -479,7 +509,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         __syncthreads();
         const unsigned char *slot = Rl + (k % 3) * TOK * PR;
         const int64_t tok0 = tok0_of(k);
-        const int cl = wave * (CW / 4) + NB2 * g;     // this lane's first local channel
+        const int cl = wave * CWW + NB2 * g;          // this lane's first local channel
 #pragma unroll
         for (int tgp = 0; tgp < NTG; ++tgp) {
             const int t = 16 * tgp + l16;
@@ -545,27 +575,29 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
         }
     };
 
-    // ---- the walk.  Iteration k: the loads of Q(k-1)'s records go out, then
-    // S(k), the loads of tile k+1, R(k-1), the loads of ss(k) and a(k-1), M(k),
-    // Q(k), C(k-1).  A wave's memory-count waits complete in issue order, so R
-    // waits only for loads issued before the next tile's; the stage flags are
-    // compile-time constants in the steady state, so the counts are exact.
-    auto iterate = [&](int k, auto doS, auto doR) __attribute__((always_inline)) {
-        if constexpr (doR.value) issue_q(k - 1);
-        if constexpr (doS.value) {
-            stage_S(k);
-            __syncthreads();
-            prefetch(k + 1 < K ? k + 1 : k);
+    // ---- the walk: a three-tile software pipeline.  Iteration k: the loads of
+    // ss(k-1) go out, R(k-2), S(k), M(k-1) and Q(k-1), the loads of a(k-2), the
+    // loads of tile k+1, C(k-2), then the loads of Q(k-1)'s records.  Every
+    // exchange is read at least a stage after it was written, most of them an
+    // iteration after: ss(k) is published in iteration k and gathered in k+1,
+    // Q(k) in k+1 and reduced at the start of k+2, a(k) at the start of k+2 and
+    // gathered at its end.  A wave's memory-count waits complete in issue
+    // order, so each wait on exchange loads covers only what was issued before
+    // them (the loads of tile k+1 come after those of a(k-2)); the stage flags
+    // are compile-time constants, so the counts are exact.
+    auto iterate = [&](int k, auto doS, auto doMQ, auto doRC) __attribute__((always_inline)) {
+        if constexpr (doMQ.value) issue_ss(k - 1);
+        if constexpr (doRC.value) stage_R(k - 2);
+        if constexpr (doS.value) stage_S(k);
+        if constexpr (doMQ.value) {
+            stage_M(k - 1);
+            stage_Q(k - 1);
         }
-        if constexpr (doR.value) { stage_R(k - 1); __syncthreads(); }
-        if constexpr (doS.value) issue_ss(k);
-        if constexpr (doR.value) issue_act(k - 1);
-        if constexpr (doS.value) {
-            stage_M(k);
-            stage_Q(k);
-            __syncthreads();
-        }
-        if constexpr (doR.value) { stage_C(k - 1); __syncthreads(); }
+        if constexpr (doRC.value) issue_act(k - 2);
+        if constexpr (doS.value) prefetch(k + 1 < K ? k + 1 : k);
+        if constexpr (doRC.value) stage_C(k - 2);
+        __syncthreads();
+        if constexpr (doMQ.value) issue_q(k - 1);
     };
     using T1 = std::integral_constant<bool, true>;
     using F0 = std::integral_constant<bool, false>;
@@ -573,9 +605,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_cluster(KArgs a) {
     __syncthreads();
     if (K > 0) {
         prefetch(0);
-        iterate(0, T1{}, F0{});
-        for (int k = 1; k < K; ++k) iterate(k, T1{}, T1{});   // steady state
-        iterate(K, F0{}, T1{});
+        iterate(0, T1{}, F0{}, F0{});
+        if (K >= 2) iterate(1, T1{}, T1{}, F0{});
+        else iterate(1, F0{}, T1{}, F0{});
+        for (int k = 2; k < K; ++k) iterate(k, T1{}, T1{}, T1{});   // steady state
+        if (K >= 2) iterate(K, F0{}, T1{}, T1{});
+        iterate(K + 1, F0{}, F0{}, T1{});
     }
     // the last member of the cluster to finish advances its epoch
     if (tid == 0) {
@@ -614,9 +649,9 @@ DevState g_dev[kMaxDevices];
 
 template <int CW, bool FUSED> void *kernel_ptr() { return reinterpret_cast<void *>(&k_cluster<CW, FUSED>); }
 
-bool occupancy_ok(void *fn) {
+bool occupancy_ok(void *fn, int threads) {
     int nb = 0;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) == hipSuccess && nb >= 1;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, 0) == hipSuccess && nb >= 1;
 }
 
 void init_device(int dev, DevState &s) {
@@ -624,9 +659,9 @@ void init_device(int dev, DevState &s) {
     if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
     if (strncmp(p.gcnArchName, "gfx950", 6) != 0) return;
     if (p.multiProcessorCount != kMembers * kMaxClusters) return;   // 8 XCDs of 32 CUs
-    void *fns[] = {kernel_ptr<128, true>(), kernel_ptr<128, false>(), kernel_ptr<64, true>(), kernel_ptr<64, false>()};
-    for (void *f : fns)
-        if (!occupancy_ok(f)) return;
+    if (!occupancy_ok(kernel_ptr<128, true>(), threads_of(128)) || !occupancy_ok(kernel_ptr<128, false>(), threads_of(128)) ||
+        !occupancy_ok(kernel_ptr<64, true>(), threads_of(64)) || !occupancy_ok(kernel_ptr<64, false>(), threads_of(64)))
+        return;
     void *ptr = nullptr;
     if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(exchange)) != hipSuccess || !ptr) return;
     if (hipEventCreateWithFlags(&s.last, hipEventDisableTiming) != hipSuccess) return;
@@ -654,7 +689,7 @@ int slice_width(const ReadArgs &a) {
 
 template <int CW, bool FUSED>
 hipError_t launch_t(const KArgs &k, int ncl, hipStream_t st) {
-    hipLaunchKernelGGL((k_cluster<CW, FUSED>), dim3(kMembers * ncl), dim3(kThreads), 0, st, k);
+    hipLaunchKernelGGL((k_cluster<CW, FUSED>), dim3(kMembers * ncl), dim3(threads_of(CW)), 0, st, k);
     return hipGetLastError();
 }
 
