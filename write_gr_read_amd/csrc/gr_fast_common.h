@@ -17,47 +17,21 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16 * kWaves;        // tokens per workgroup
 constexpr int kChunk = 32;                // channels per MFMA k-step
 
-#ifndef GR_K1_DEPTH
-#define GR_K1_DEPTH 0
-#endif
 constexpr int kIter = 64;                 // channels per W' chunk of kernel 1 (a round is two)
-constexpr int kDepth = GR_K1_DEPTH;       // kernel 1: rounds of state / y loads in flight ahead
-#ifndef GR_K1_TG
-#define GR_K1_TG 1
-#endif
-constexpr int kTG = GR_K1_TG;             // 16-token MFMA column groups per kernel-1 wave
-#ifndef GR_K2_WAVES_PER_SIMD
-#define GR_K2_WAVES_PER_SIMD 3
-#endif
-#ifndef GR_K2_WAVES
-#define GR_K2_WAVES 4
-#endif
-constexpr int kK2WavesPerSimd = GR_K2_WAVES_PER_SIMD;  // occupancy target of kernel 2
-constexpr int kK2Waves = GR_K2_WAVES;                  // waves per kernel-2 workgroup
+constexpr int kK1WavesPerSimd = 4;        // occupancy target of kernel 1 (narrow gate)
+constexpr int kK2WavesPerSimd = 3;        // occupancy target of the few-token kernel 2
+constexpr int kK2Waves = 4;               // waves per few-token kernel-2 workgroup
 constexpr int kK2Threads = 64 * kK2Waves;
-constexpr int kK2Tile = 16 * kK2Waves;                 // tokens per kernel-2 workgroup
-#ifndef GR_K2_SUB
-#define GR_K2_SUB 1
-#endif
-constexpr int kK2Sub = GR_K2_SUB;  // 32-channel chunks per kernel-2 iteration (whole 128-byte lines)
+constexpr int kK2Tile = 16 * kK2Waves;    // tokens per few-token kernel-2 workgroup
 constexpr int kMaxRowBlocks = 8;          // (r + n) padded to 16, at most 128 (narrow gate)
 constexpr int kMaxWideRowBlocks = 21;     // wide gate (kernel 1 wide form): r + n up to 336
 constexpr int kMaxWideRKS = 10;           // wide gate: r up to 320 (k-steps of 32 of the up projection)
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
-#ifndef GR_SPLIT_TARGET
-#define GR_SPLIT_TARGET 256
-#endif
-constexpr int kSplitTarget = GR_SPLIT_TARGET;  // kernel-1 workgroups wanted before splitting channels
+constexpr int kSplitTarget = 256;         // kernel-1 workgroups wanted before splitting channels
 constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power of two)
-#ifndef GR_SMALL_BELOW
-#define GR_SMALL_BELOW 32
-#endif
-constexpr int kSmallBelow = GR_SMALL_BELOW;  // few-token kernel 1 while (token tiles) x n is below this
+constexpr int kSmallBelow = 32;           // few-token kernel 1 while (token tiles) x n is below this
 constexpr int kSmallBelowWide = 16;          // ... for a wide gate
-#ifndef GR_SMALL_TARGET
-#define GR_SMALL_TARGET 256
-#endif
-constexpr int kSmallTarget = GR_SMALL_TARGET;  // few-token kernel 1: workgroups wanted before splitting
+constexpr int kSmallTarget = 256;         // few-token kernel 1: workgroups wanted before splitting
 constexpr int kSmallWaves = 8;            // waves per few-token kernel-1 workgroup
 
 struct FastShape {

@@ -41,9 +41,6 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
 }
 
 // ---------------------------------------------------------------------------
-#ifndef GR_K1_WAVES_PER_SIMD
-#define GR_K1_WAVES_PER_SIMD 4
-#endif
 // Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
 // the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
 // that XCD's L2) and consecutive dispatch slots.
@@ -63,20 +60,19 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
 // once for the call (every token tile would otherwise redo the same split).
 // It is staged in a double-buffered LDS slot per chunk: the chunk after next
 // is loaded into registers while a chunk is used, with one barrier per chunk.
-// DEPTH > 0: DEPTH rounds of state / y loads are in flight ahead of the round
-// in use.  DEPTH = 0: the next round's state loads are issued as soon as the
-// element phase has freed their registers, so they fly during the MFMA phase
-// at no register cost; y (mostly an L2 hit: the n workgroups of a tile share
-// it) is loaded at the start of its round.
-template <bool FUSED, int NRB, int DEPTH, int TG, bool F8>
-__global__ void __launch_bounds__(64 * (kWaves / TG), (NRB <= 5 && TG == 1) ? GR_K1_WAVES_PER_SIMD : 2)
+// The next round's state loads are issued as soon as the element phase has
+// freed their registers, so they fly during the MFMA phase at no register
+// cost; y (mostly an L2 hit: the n workgroups of a tile share it) is loaded at
+// the start of its round.
+template <bool FUSED, int NRB, bool F8>
+__global__ void __launch_bounds__(kThreads, NRB <= 5 ? kK1WavesPerSimd : 2)
 k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
               const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
               const bf16_t *__restrict__ wd, const bf16_t *__restrict__ ww, Workspace ws,
               FastShape sh) {
-    constexpr int WAVES = kWaves / TG;                 // each wave carries TG groups of 16 tokens
+    constexpr int WAVES = kWaves;                      // each wave carries 16 tokens
     constexpr int THREADS = 64 * WAVES;
-    constexpr int NQ = 4 * TG;                         // load instructions per round (4 tokens each)
+    constexpr int NQ = 4;                              // load instructions per round (4 tokens each)
     constexpr int RC = 2 * kIter;                      // channels per round
     constexpr int PCS = RC / 8;                        // 16-byte pieces per token row and round
     constexpr int KS = kIter / kChunk;                 // MFMA k-steps per W' chunk
@@ -90,14 +86,13 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     static_assert(kIter / 8 == 8, "the W' swizzle permutes eight 16-byte pieces per row");
     constexpr int NV = NRB * 16 * (kIter / 8);         // 16-byte vectors of W' per chunk (per plane)
     constexpr int WV = (2 * NV + THREADS - 1) / THREADS;  // hi and lo planes
-    constexpr int NSLOT = DEPTH + 1;
     using T = typename StateT<F8>::type;
     using SV = typename StateT<F8>::vec8;              // 8 channels of the state
     static_assert(PCS == 16, "a round is 16 pieces of 8 channels per token");
     // [buffer][hi/lo][row][k]
     __shared__ __attribute__((aligned(16))) bf16_t lds_w[2][2][NRB * 16 * kPitch];
     constexpr int RP = PCS + 1;                        // LDS tile pitch in pieces (odd: no bank conflicts)
-    __shared__ __attribute__((aligned(16))) u32x4 lds_r[WAVES][16 * TG * RP];
+    __shared__ __attribute__((aligned(16))) u32x4 lds_r[WAVES][16 * RP];
 
     const int n = sh.n, d = sh.d, S = sh.ksplit;
     const int64_t b = blockIdx.x;
@@ -125,7 +120,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, m16 = lane & 15;
-    const int64_t t0 = tile * kTile + wave * 16 * TG;   // first token of this wave
+    const int64_t t0 = tile * kTile + wave * 16;        // first token of this wave
     const int64_t nd = (int64_t)n * d;
     const int chan = sh.ksplit_chan;                    // channels of this split (multiple of kIter)
     const int nit = chan / kIter;                       // W' chunks
@@ -188,44 +183,40 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
     const uint32_t soff = (uint32_t)(g * nd + 8 * m16), yoff = (uint32_t)(g * d + 8 * m16);
     const int64_t qstride = 4 * nd, qystride = 4 * (int64_t)d;
 
-    SV rr[NSLOT][NQ];
-    u32x4 yy[NSLOT][NQ];
-    // load round `ar` of the split (valid: the walk has such a step)
-    auto load_round = [&](int ar, bool valid, int slot, bool ds = true, bool dy = true) {
+    SV rr[NQ];
+    u32x4 yy[NQ];
+    // load round `ar` of the split (valid: the walk has such a step): its
+    // state (ds) and / or its y (dy)
+    auto load_round = [&](int ar, bool valid, bool ds, bool dy) {
         const bool in = valid && ar * RC + 8 * m16 < chan;
         const T *const rs = sbase + ar * RC;                   // wave-uniform
         const bf16_t *const ry = FUSED ? ybase + ar * RC : nullptr;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            if (ds) rr[slot][q] = SV{};
-            if (dy) yy[slot][q] = u32x4{0u, 0u, 0u, 0u};
+            if (ds) rr[q] = SV{};
+            if (dy) yy[q] = u32x4{0u, 0u, 0u, 0u};
             if (vq[q] && in) {
-                if (ds) rr[slot][q] = *reinterpret_cast<const SV *>(rs + q * qstride + soff);
-                if (FUSED && dy) yy[slot][q] = *reinterpret_cast<const u32x4 *>(ry + q * qystride + yoff);
+                if (ds) rr[q] = *reinterpret_cast<const SV *>(rs + q * qstride + soff);
+                if (FUSED && dy) yy[q] = *reinterpret_cast<const u32x4 *>(ry + q * qystride + yoff);
             }
         }
     };
 
-    f32x4 acc[TG][NRB];
+    f32x4 acc[NRB];
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg)
-#pragma unroll
-        for (int k = 0; k < NRB; ++k) acc[tg][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 *my_r = lds_r[wave];
 
     load_w(0);
     store_w(0);
     load_w(1);
-#pragma unroll
-    for (int q = 0; q < DEPTH; ++q) load_round(q < nround ? rnd(q) : 0, q < nround, q);
-    if (DEPTH == 0) load_round(rot, true, 0, true, false);
+    load_round(rot, true, true, false);
     __syncthreads();
     int it = 0;                                         // W' chunks of the walk used so far
     int ar = rot;                                       // round of the split at walk step rd
     for (int rd = 0; rd < nround; ++rd) {
         const int an = ar + 1 == nround ? 0 : ar + 1;   // ... at step rd + 1
-        if (DEPTH > 0) load_round(rd + DEPTH < nround ? rnd(rd + DEPTH) : 0, rd + DEPTH < nround, DEPTH);
-        else load_round(ar, true, 0, false, true);
+        load_round(ar, true, false, true);
         // eq:write in the load layout: store, sum of squares, LDS tile
         const bool in = ar * RC + 8 * m16 < chan;
         T *const ws_ = sbase + ar * RC;                          // wave-uniform
@@ -233,16 +224,16 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
         for (int q = 0; q < NQ; ++q) {
             u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
             if constexpr (F8) {
-                u32x2 o = rr[0][q];
+                u32x2 o = rr[q];
                 if (FUSED) {
-                    o = write8_fp8(sq[q], yy[0][q], rr[0][q]);
+                    o = write8_fp8(sq[q], yy[q], rr[q]);
                     if (vq[q] && in) *reinterpret_cast<u32x2 *>(ws_ + q * qstride + soff) = o;
                 }
                 w = widen8_fp8_bf16(o);
             } else {
-                w = rr[0][q];
+                w = rr[q];
                 if (FUSED) {
-                    w = write8_bf16(sq[q], yy[0][q], rr[0][q]);
+                    w = write8_bf16(sq[q], yy[q], rr[q]);
                     if (vq[q] && in) *reinterpret_cast<u32x4 *>(ws_ + q * qstride + soff) = w;
                 }
             }
@@ -254,7 +245,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
         // instructions of a wave execute in order); keep the phases apart so
         // the element work and the MFMA operands are not live together
         __builtin_amdgcn_sched_barrier(0);
-        if (DEPTH == 0) load_round(an, rd + 1 < nround, 0, true, false);
+        load_round(an, rd + 1 < nround, true, false);
 #pragma unroll
         for (int h = 0; h < RC / kIter; ++h) {
             if (ar * (RC / kIter) + h < nit) {               // chunk h of this round exists
@@ -262,10 +253,7 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int pc = (h * kIter + ks * kChunk) / 8 + g;   // piece of this lane group
-                    bf16x8 bop[TG];
-#pragma unroll
-                    for (int tg = 0; tg < TG; ++tg)
-                        bop[tg] = as_bf16x8(my_r[(16 * tg + m16) * RP + pc]);
+                    const bf16x8 bop = as_bf16x8(my_r[m16 * RP + pc]);
                     const int pw = ((ks * kChunk / 8 + g) ^ swz(m16)) * 8;   // swizzled piece
                     const bf16_t *wh = &lds_w[cur][0][m16 * kPitch + pw];
                     const bf16_t *wl = &lds_w[cur][1][m16 * kPitch + pw];
@@ -273,11 +261,8 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                     for (int k = 0; k < NRB; ++k) {
                         const u32x4 ah = *reinterpret_cast<const u32x4 *>(wh + k * 16 * kPitch);
                         const u32x4 al = *reinterpret_cast<const u32x4 *>(wl + k * 16 * kPitch);
-#pragma unroll
-                        for (int tg = 0; tg < TG; ++tg) {
-                            acc[tg][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop[tg], acc[tg][k], 0, 0, 0);
-                            acc[tg][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop[tg], acc[tg][k], 0, 0, 0);
-                        }
+                        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), bop, acc[k], 0, 0, 0);
+                        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), bop, acc[k], 0, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -287,13 +272,6 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
                 ++it;
             }
         }
-#pragma unroll
-        for (int q = 0; q < DEPTH; ++q)
-#pragma unroll
-            for (int e = 0; e < NQ; ++e) {
-                rr[q][e] = rr[q + 1][e];
-                yy[q][e] = yy[q + 1][e];
-            }
         ar = an;
     }
 
@@ -307,13 +285,12 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
         if (m16 == 0 && vq[q])
             ws.partial[((t0 + 4 * q + g) * n + br) * S * (int64_t)sh.pstride + split * (int64_t)sh.pstride] = ss[q];
     }
-#pragma unroll
-    for (int tg = 0; tg < TG; ++tg) {
-        const int64_t t = t0 + 16 * tg + m16;  // MFMA column of this lane
+    {
+        const int64_t t = t0 + m16;  // MFMA column of this lane
         if (t < sh.N) {
             float *rec = ws.partial + ((t * n + br) * S + split) * (int64_t)sh.pstride;
 #pragma unroll
-            for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[tg][k];
+            for (int k = 0; k < NRB; ++k) *reinterpret_cast<f32x4 *>(rec + 4 + 16 * k + 4 * g) = acc[k];
         }
     }
 }
@@ -686,7 +663,7 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     }
 #define GR_K1(NRB)                                                                          \
     case NRB:                                                                               \
-        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, kDepth, kTG, F8>), dim3(grid), dim3(64 * (kWaves / kTG)), 0, st, \
+        hipLaunchKernelGGL((k_stream_proj<FUSED, NRB, F8>), dim3(grid), dim3(kThreads), 0, st, \
                            (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,                \
                            (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
         break;

@@ -118,8 +118,7 @@ __global__ void __launch_bounds__(kK2Threads, kK2WavesPerSimd)
 k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
                int ranges) {
-    constexpr int SUB = kK2Sub;                        // 32-channel chunks per iteration
-    constexpr int KC = SUB * kChunk;                   // channels per iteration
+    constexpr int KC = kChunk;                         // channels per iteration
     constexpr int RK = RKS * 32;
     constexpr int kPitch = RK + 8;                     // bf16 per staged W_up row
     constexpr int NV = NB * KC * (RK / 8);             // 16-byte vectors of W_up per iteration
@@ -138,8 +137,7 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     const bool valid = t < sh.N;
     const int c_begin = range * sh.k2_chan;
     const int c_end = (c_begin + sh.k2_chan) < d ? (c_begin + sh.k2_chan) : d;
-    const int nch = (c_end - c_begin) / kChunk;        // 32-channel chunks of this range
-    const int nit = (nch + SUB - 1) / SUB;
+    const int nit = (c_end - c_begin) / kChunk;        // 32-channel chunks of this range
     const float inv_n = 1.0f / (float)NB;
 
     // W_up rows (branch i, channel c) of one iteration; row index i * KC + cc
@@ -166,15 +164,15 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
             }
         }
     };
-    // LDS row of (branch i, channel cc): chunk cc/32, then MFMA row order within it
+    // LDS row of (branch i, channel cc of the chunk): MFMA row order
     auto store_w = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kK2Threads;
             if (v < NV) {
                 const int row = v / (RK / 8), kv = v % (RK / 8);
-                const int i = row / KC, cc = row % KC, c32 = cc % kChunk;
-                const int pos = (i * SUB + cc / kChunk) * kChunk + 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+                const int i = row / KC, cc = row % KC;
+                const int pos = i * kChunk + 16 * ((cc >> 2) & 1) + 4 * (cc >> 3) + (cc & 3);
                 *reinterpret_cast<u32x4 *>(&lds_u[buf][pos * kPitch + kv * 8]) = wreg[q];
             }
         }
@@ -205,17 +203,15 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     bf16_t *urow = u + t * (int64_t)d + 8 * g;
     const int m16 = lane & 15;  // A row this lane feeds
 
-    u32x4 s0[SUB][NB], s1[SUB][NB];
-    auto load_state = [&](int it, u32x4 (&sv)[SUB][NB]) {
+    u32x4 s0[NB], s1[NB];
+    auto load_state = [&](int it, u32x4 (&sv)[NB]) {
 #pragma unroll
-        for (int sc = 0; sc < SUB; ++sc)
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                const int c0 = c_begin + it * KC + sc * kChunk;
-                sv[sc][i] = u32x4{0u, 0u, 0u, 0u};
-                if (valid && it < nit && c0 < c_end)
-                    sv[sc][i] = load8_as_bf16<F8>(srow + (int64_t)i * d + c0);
-            }
+        for (int i = 0; i < NB; ++i) {
+            const int c0 = c_begin + it * KC;
+            sv[i] = u32x4{0u, 0u, 0u, 0u};
+            if (valid && it < nit && c0 < c_end)
+                sv[i] = load8_as_bf16<F8>(srow + (int64_t)i * d + c0);
+        }
     };
 
     load_w(0);
@@ -226,9 +222,8 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     for (int it = 0; it < nit; ++it) {
         const int cur = it & 1;
         load_state(it + 1, s1);
-#pragma unroll
-        for (int sc = 0; sc < SUB; ++sc) {
-            const int c0 = c_begin + it * KC + sc * kChunk;
+        {
+            const int c0 = c_begin + it * KC;
             float uacc[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
@@ -237,7 +232,7 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     f32x4 tl = {0.f, 0.f, 0.f, 0.f};
-                    const bf16_t *ap = &lds_u[cur][((i * SUB + sc) * kChunk + 16 * h + m16) * kPitch + 8 * g];
+                    const bf16_t *ap = &lds_u[cur][(i * kChunk + 16 * h + m16) * kPitch + 8 * g];
 #pragma unroll
                     for (int ks = 0; ks < RKS; ++ks) {
                         const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
@@ -248,8 +243,7 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const int e = 4 * h + m;
-                        const float bterm = dot2_bf16(s0[sc][i][e >> 1],
-                                                      lds_g[cur][i * KC + sc * kChunk + 8 * g + e], 0.f);
+                        const float bterm = dot2_bf16(s0[i][e >> 1], lds_g[cur][i * KC + 8 * g + e], 0.f);
                         const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
                         uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
                     }
@@ -269,9 +263,7 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
         load_w(it + 2);
         __syncthreads();
 #pragma unroll
-        for (int sc = 0; sc < SUB; ++sc)
-#pragma unroll
-            for (int i = 0; i < NB; ++i) s0[sc][i] = s1[sc][i];
+        for (int i = 0; i < NB; ++i) s0[i] = s1[i];
     }
 }
 
@@ -316,19 +308,14 @@ template <int RKS> struct ResidentCfg {
     static constexpr int SC = CH >= 64 ? 2 : 1;
 };
 
-#ifndef GR_K2R_WAVES
-#define GR_K2R_WAVES 8
-#endif
-#ifndef GR_K2R_WAVES_PER_SIMD
-#define GR_K2R_WAVES_PER_SIMD 4
-#endif
-constexpr int kResWaves = GR_K2R_WAVES;
+constexpr int kResWaves = 8;
+constexpr int kResWavesPerSimd = 4;              // occupancy target (narrow gate)
 constexpr int kResThreads = 64 * kResWaves;
 constexpr int kResTile = 16 * kResWaves;         // tokens per tile
 constexpr int kResWgsTarget = 512;               // workgroups wanted (two per CU)
 
 template <int NB, int RKS, int CH, int SC>
-__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? GR_K2R_WAVES_PER_SIMD : 2)
+__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? kResWavesPerSimd : 2)
 k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                         const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
                         FastShape sh, int ranges, int P) {
@@ -653,7 +640,7 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
 constexpr int kF8Unit = 64;
 
 template <int NB, int RKS, int CH>
-__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? GR_K2R_WAVES_PER_SIMD : 2)
+__global__ void __launch_bounds__(kResThreads, RKS <= 2 ? kResWavesPerSimd : 2)
 k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__restrict__ gamma,
                             const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws,
                             FastShape sh, int ranges, int P) {

@@ -392,14 +392,11 @@ hipError_t launch_write(void *state, const void *y, const float *s, bool bf16, b
     return hipGetLastError();
 }
 
-#ifndef GR_ADDNORM_WALK
-#define GR_ADDNORM_WALK 1
-#endif
 template <typename T, int KPT>
 static void add_rmsnorm_k(void *x, const void *y, const void *w, float eps, void *out,
                           int64_t N, int d, hipStream_t st) {
     if constexpr (KPT > 0) {
-        if (GR_ADDNORM_WALK && N > 1024) {
+        if (N > 1024) {
             hipLaunchKernelGGL((k_add_rmsnorm_walk<T, KPT>), dim3(1024), dim3(256), 0, st, (T *)x,
                                (const T *)y, (const T *)w, eps, (T *)out, d, N);
             return;
