@@ -152,5 +152,27 @@ __device__ __forceinline__ float block_sum(float v, float *scratch) {
     for (int w = 0; w < nw; ++w) t += scratch[w];
     return t;
 }
+// K sums over the whole workgroup with one exchange: v[q] becomes the sum of
+// every thread's v[q] (each the same as block_sum(v[q]) would give).
+// `scratch` holds at least K * blockDim.x / 64 floats.
+template <int K>
+__device__ __forceinline__ void block_sum_many(float (&v)[K], float *scratch) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
+#pragma unroll
+    for (int q = 0; q < K; ++q) v[q] = wave_sum(v[q]);
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) scratch[q * nw + wave] = v[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+        float t = 0.f;
+        for (int w = 0; w < nw; ++w) t += scratch[q * nw + w];
+        v[q] = t;
+    }
+}
 
 }  // namespace grk

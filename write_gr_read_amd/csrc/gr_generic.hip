@@ -15,7 +15,7 @@
 namespace grk {
 
 constexpr int kGenThreads = 256;
-constexpr int kRowsPerPass = 8;  // projection rows accumulated per sweep
+constexpr int kRowsPerPass = 16;  // projection rows accumulated per sweep (one reduction each)
 
 // ---------------------------------------------------------------------------
 // GR read (optionally preceded by the write of the previous sublayer), one
@@ -31,7 +31,7 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
                int n, int d, int r, float eps, const W *__restrict__ gamma,
                const W *__restrict__ wd, const W *__restrict__ wu, const W *__restrict__ ww,
                W *__restrict__ u, float *__restrict__ s_out) {
-    __shared__ float red[kGenThreads / 64];
+    __shared__ float red[kRowsPerPass * (kGenThreads / 64)];
     __shared__ float rho[8];
     __shared__ float proj[512 + 8];  // z (then SiLU) for k < r, write logits after
     const int64_t t = blockIdx.x;
@@ -39,21 +39,28 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
     const int64_t nd = (int64_t)n * d;
     T *Rt = state + t * nd;
 
-    // eq:write (FUSED) and the per-branch sum of squares of eq:rms.
-    for (int i = 0; i < n; ++i) {
-        float ss = 0.f;
-        const float si = FUSED ? s_in[t * n + i] : 0.f;
-        for (int c = tid; c < d; c += kGenThreads) {
-            float v = Store<T>::load(Rt + (int64_t)i * d + c);
-            if (FUSED) {
-                v = Store<T>::write(si, Store<W>::load(y + t * d + c), v);
-                Store<T>::store(Rt + (int64_t)i * d + c, v);
+    // eq:write (FUSED) and the per-branch sum of squares of eq:rms (n <= 8),
+    // reduced together.
+    float ss[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ss[i] = 0.f;
+        if (i < n) {
+            const float si = FUSED ? s_in[t * n + i] : 0.f;
+            for (int c = tid; c < d; c += kGenThreads) {
+                float v = Store<T>::load(Rt + (int64_t)i * d + c);
+                if (FUSED) {
+                    v = Store<T>::write(si, Store<W>::load(y + t * d + c), v);
+                    Store<T>::store(Rt + (int64_t)i * d + c, v);
+                }
+                ss[i] = fmaf(v, v, ss[i]);
             }
-            ss = fmaf(v, v, ss);
         }
-        ss = block_sum(ss, red);
-        if (tid == 0) rho[i] = 1.0f / sqrtf(ss / (float)d + eps);
     }
+    block_sum_many(ss, red);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (tid == i && i < n) rho[i] = 1.0f / sqrtf(ss[i] / (float)d + eps);
     __syncthreads();
 
     // eq:gate down projection and eq:s logits: rows k < r of W_down, then the
@@ -78,11 +85,10 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
                 }
             }
         }
+        block_sum_many(acc, red);
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q) {
-            const float tot = block_sum(acc[q], red);
-            if (tid == 0 && k0 + q < rows) proj[k0 + q] = tot / (float)n;
-        }
+        for (int q = 0; q < kRowsPerPass; ++q)
+            if (tid == q && k0 + q < rows) proj[k0 + q] = acc[q] / (float)n;
     }
     __syncthreads();
     for (int k = tid; k < r; k += kGenThreads) proj[k] = silu_f(proj[k]);
@@ -95,9 +101,17 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
             const int64_t j = (int64_t)i * d + c;
             float g = 1.0f;
             if (r > 0) {
+                // sixteen weights per batch: independent loads, one round trip
                 float l = 0.f;
                 const W *wrow = wu + j * r;
-                for (int k = 0; k < r; ++k) l = fmaf(Store<W>::load(wrow + k), proj[k], l);
+                for (int k0 = 0; k0 < r; k0 += 16) {
+                    float wv[16];
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) wv[q] = k0 + q < r ? Store<W>::load(wrow + k0 + q) : 0.f;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        if (k0 + q < r) l = fmaf(wv[q], proj[k0 + q], l);
+                }
                 g = sigmoid_f(l);
             }
             const float v = Store<W>::load(gamma + j) * Store<T>::load(Rt + j) * rho[i];
@@ -106,6 +120,103 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
         Store<W>::store(u + t * d + c, acc_u / (float)n);
     }
     if (s_out && tid < n) s_out[t * n + tid] = ww ? 2.0f * sigmoid_f(proj[r + tid]) : 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// The same read (and fused write + read) for small fp32 rows: n = 4,
+// d = 256 EPT, r = 16 RB (RB = 1, 2, 4).  With every trip count known at
+// compile time each phase is straight-line code, so a thread's loads of all
+// four branches (and of all projection rows) go out together instead of one
+// loop iteration's round trip after another; every reduction hands all its
+// sums to every thread (z, SiLU(z) and the write logits stay in registers).
+// Same arithmetic and order of operations per element as k_read_generic.
+template <bool FUSED, int EPT, int RB>
+__global__ void __launch_bounds__(kGenThreads)
+k_read_small(float *__restrict__ state, const float *__restrict__ y, const float *__restrict__ s_in,
+             float eps, const float *__restrict__ gamma, const float *__restrict__ wd,
+             const float *__restrict__ wu, const float *__restrict__ ww, float *__restrict__ u,
+             float *__restrict__ s_out) {
+    constexpr int NB = 4, D = kGenThreads * EPT, ND = NB * D, R = 16 * RB;
+    constexpr int PASSES = RB + 1;                   // 16 projection rows each; the last one the write rows
+    __shared__ float red[16 * (kGenThreads / 64)];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    float *Rt = state + t * ND;
+    const bool haw = ww != nullptr;
+
+    // eq:write (FUSED) and the sums of squares of eq:rms
+    float rv[NB][EPT], gv[NB][EPT], ss[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const float si = FUSED ? s_in[t * NB + i] : 0.f;
+        ss[i] = 0.f;
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+            const int c = tid + kGenThreads * q;
+            float v = Rt[i * D + c];
+            if (FUSED) {
+                v = fmaf(si, y[t * D + c], v);
+                Rt[i * D + c] = v;
+            }
+            rv[i][q] = v;
+            gv[i][q] = gamma[i * D + c];
+            ss[i] = fmaf(v, v, ss[i]);
+        }
+    }
+    block_sum_many(ss, red);
+    float rho[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) rho[i] = 1.0f / sqrtf(ss[i] / (float)D + eps);
+    // v = vec(R-hat) for this thread's elements
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) gv[i][q] = gv[i][q] * rv[i][q] * rho[i];
+
+    // eq:gate down projection (rows k < R) and eq:s logits (the n rows of W_write)
+    float proj[16 * PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        float acc[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            acc[k] = 0.f;
+            const int row = 16 * p + k;
+            const bool on = p < RB || (haw && k < NB);
+            if (on) {
+                const float *wrow = p < RB ? wd + (int64_t)row * ND : ww + (int64_t)k * ND;
+#pragma unroll
+                for (int i = 0; i < NB; ++i)
+#pragma unroll
+                    for (int q = 0; q < EPT; ++q)
+                        acc[k] = fmaf(wrow[i * D + tid + kGenThreads * q], gv[i][q], acc[k]);
+            }
+        }
+        block_sum_many(acc, red);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) proj[16 * p + k] = acc[k] / (float)NB;
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) proj[k] = silu_f(proj[k]);
+
+    // eq:gate up projection + sigmoid, eq:use_gate combine
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int c = tid + kGenThreads * q;
+        float acc_u = 0.f;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const float *wrow = wu + (int64_t)(i * D + c) * R;
+            float l = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k) l = fmaf(wrow[k], proj[k], l);
+            acc_u = fmaf(sigmoid_f(l), gv[i][q], acc_u);
+        }
+        u[t * D + c] = acc_u / (float)NB;
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        if (s_out && tid == i) s_out[t * NB + i] = haw ? 2.0f * sigmoid_f(proj[16 * RB + i]) : 1.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -350,9 +461,41 @@ static unsigned grid_for(int64_t items, int64_t per_block, int64_t cap = 1 << 16
     return (unsigned)g;
 }
 
+template <bool FUSED, int EPT>
+static void read_small_rb(const ReadArgs &a, hipStream_t st) {
+    const int rb = a.r / 16;
+#define GR_SMALL(RB)                                                                                   \
+    hipLaunchKernelGGL((k_read_small<FUSED, EPT, RB>), dim3((unsigned)a.N), dim3(kGenThreads), 0, st, \
+                       (float *)a.state, (const float *)a.y, a.s_in, a.eps, (const float *)a.gamma,    \
+                       (const float *)a.wd, (const float *)a.wu, (const float *)a.ww, (float *)a.u,     \
+                       a.s_out)
+    if (rb == 1) GR_SMALL(1);
+    else if (rb == 2) GR_SMALL(2);
+    else GR_SMALL(4);
+#undef GR_SMALL
+}
+
+// fp32, n = 4, d in {256, 512, 1024}, r in {16, 32, 64}: k_read_small
+static bool small_shape(const ReadArgs &a) {
+    return !a.bf16 && !a.fp8 && a.n == 4 && (a.d == 256 || a.d == 512 || a.d == 1024) &&
+           (a.r == 16 || a.r == 32 || a.r == 64);
+}
+
+template <bool FUSED>
+static void read_small(const ReadArgs &a, hipStream_t st) {
+    if (a.d == 256) read_small_rb<FUSED, 1>(a, st);
+    else if (a.d == 512) read_small_rb<FUSED, 2>(a, st);
+    else read_small_rb<FUSED, 4>(a, st);
+}
+
 template <typename T, typename W>
 static hipError_t read_generic_t(const ReadArgs &a, hipStream_t st) {
     T *state = (T *)a.state;
+    if (small_shape(a)) {
+        if (a.fused) read_small<true>(a, st);
+        else read_small<false>(a, st);
+        return hipGetLastError();
+    }
     if (a.fused)
         hipLaunchKernelGGL((k_read_generic<T, W, true>), dim3((unsigned)a.N), dim3(kGenThreads), 0,
                            st, state, (const W *)a.y, a.s_in, a.n, a.d, a.r, a.eps,
