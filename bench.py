@@ -424,7 +424,7 @@ def main():
                     help="time the copy probe (always beside the headline; with --workload, before it)")
     ap.add_argument("--no-copy-probe", action="store_true", help="skip the copy probe")
     ap.add_argument("--no-others", action="store_true",
-                    help="skip the decode / add+RMSNorm / chain / single-pass keys of the default line")
+                    help="skip the tiny / decode / add+RMSNorm / chain / HC / single-pass keys of the default line")
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm",
                              "chain", "tiny", "variants", "hc_mhc", "hc_tanh", "all"])
@@ -519,11 +519,11 @@ def main():
 
     if not args.no_others:
         # the other configurations of the workload set, one key each with its
-        # own roofline: decode (us/call), the n = 1 fused add + RMSNorm, the
-        # 32-sublayer chain, mHC and HC on the prefill shape, and the single-pass
-        # kernel on this same prefill call
+        # own roofline: the tiny fp32 call and decode (us/call), the n = 1 fused
+        # add + RMSNorm, the 32-sublayer chain, mHC and HC on the prefill shape,
+        # and the single-pass kernel on this same prefill call
         others = {}
-        for w in ("decode", "addnorm", "chain", "hc_mhc", "hc_tanh"):
+        for w in ("tiny", "decode", "addnorm", "chain", "hc_mhc", "hc_tanh"):
             log(f"workload {w} ...")
             res = bench_other(w, args, dev)
             keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
