@@ -290,6 +290,28 @@ def test_zero_write_projection_gives_exactly_one():
     assert torch.all(s == 1.0)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "fp8"])
+def test_empty_inputs(dt):
+    """N = 0 on every GR call through the binding: no error, empty outputs."""
+    X = inputs.make_gr_inputs(1, 4, 256, 16, "f32" if dt == "f32" else "bf16", seed=3)
+    p = X.params[0].to(DEV)
+    sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dt]
+    pdt = torch.float32 if dt == "f32" else torch.bfloat16
+    S = torch.empty((0, 4, 256), dtype=sdt, device=DEV)
+    y = torch.empty((0, 256), dtype=pdt, device=DEV)
+    s = torch.empty((0, 4), dtype=torch.float32, device=DEV)
+    u, s1 = gr.read(S, p)
+    assert u.shape == (0, 256) and s1.shape == (0, 4)
+    assert gr.write(S, y, s).shape == (0, 4, 256)
+    u, s1 = gr.fused_write_read(S, y, s, p)
+    assert u.shape == (0, 256) and s1.shape == (0, 4)
+    if dt != "fp8":
+        x = torch.empty((0, 256), dtype=pdt, device=DEV)
+        w = torch.ones(256, dtype=pdt, device=DEV)
+        assert gr.residual_add_rmsnorm(x, x.clone(), w).shape == (0, 256)
+    torch.cuda.synchronize()
+
+
 def test_zero_strength_and_zero_output_are_identities():
     X = inputs.make_gr_inputs(50, 4, 512, 16, "bf16", seed=43)
     R = X.X.to(DEV)
