@@ -572,6 +572,41 @@ def test_chain_workload_subset():
     assert dev_gpu <= 1.1 * dev_orc, (dev_gpu, dev_orc)
 
 
+def test_chain_closed_form_with_gpu_strengths():
+    """P8, eq:rcv: after the 32-sublayer chain the state is R^(0) + sum_l s^(l) y^(l),
+    formed here in fp64 from the GPU's own strengths and sublayer outputs, up to
+    the 32 stores.  Each write rounds R + s y once to fp32 (one FMA) and once to
+    bf16 (at most half an ulp, 2^-8 of the value), so element by element
+    |g - closed| <= 1.01 (2^-8 + 2^-23) sum_l |R^(l)| with R^(l) the partial sums
+    (the 1 % covers the earlier errors carried into each rounded value)."""
+    Xin = inputs.workload(5, N=256)
+    X = Xin.X.to(DEV)
+    ps = [dev_params(p) for p in Xin.params]
+    writes = []
+    u, s = gr.read(X, ps[0])
+    y = gr.tanh_standin(u)
+    for p in ps[1:]:
+        writes.append((s.clone(), y.clone()))
+        u, s = gr.fused_write_read(X, y, s, p)
+        y = gr.tanh_standin(u)
+    writes.append((s.clone(), y.clone()))
+    gr.write(X, y, s)
+    torch.cuda.synchronize()
+    assert len(writes) == 32
+    part = to64(Xin.X)
+    total = np.zeros_like(part)
+    for sl, yl in writes:
+        part = part + to64(sl)[:, :, None] * to64(yl)[:, None, :]
+        total += np.abs(part)
+    err = np.abs(to64(X) - part)
+    bound = 1.01 * (2.0 ** -8 + 2.0 ** -23) * total
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} elements past the rounding bound; worst ratio "
+                           f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+    # the bound is not vacuous: the rounding errors are there, and well inside it
+    assert 0 < float(err.max()) and float((err / np.maximum(bound, 1e-300)).max()) < 1
+
+
 def test_chain_workload_full_sampled():
     """Workload 5 at full size (N=32768): the oracle runs the chain on 32
     sampled tokens."""
