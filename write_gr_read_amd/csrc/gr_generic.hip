@@ -444,6 +444,21 @@ k_tanh_standin(const T *__restrict__ u, T *__restrict__ y, int64_t count) {
          q += (int64_t)gridDim.x * blockDim.x)
         Store<T>::store(y + q, 0.1f * tanh_f(Store<T>::load(u + q)));
 }
+// the same over 16-byte vectors (u and y are 16-byte aligned, as the ABI
+// requires); elements past the last whole vector are left to k_tanh_standin
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_tanh_standin_vec(const T *__restrict__ u, T *__restrict__ y, int64_t vecs) {
+    constexpr int VEC = 16 / sizeof(T);
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < vecs;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        T in[VEC], out[VEC];
+        *reinterpret_cast<u32x4 *>(in) = *reinterpret_cast<const u32x4 *>(u + q * VEC);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) Store<T>::store(out + e, 0.1f * tanh_f(Store<T>::load(in + e)));
+        *reinterpret_cast<u32x4 *>(y + q * VEC) = *reinterpret_cast<const u32x4 *>(out);
+    }
+}
 
 __global__ void __launch_bounds__(256)
 k_copy(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int64_t vecs) {
@@ -567,14 +582,20 @@ hipError_t launch_add_rmsnorm(void *x, const void *y, const void *w, float eps, 
     return hipGetLastError();
 }
 
+template <typename T>
+static void tanh_standin_t(const T *u, T *y, int64_t count, hipStream_t st) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int64_t vecs = count / VEC, done = vecs * VEC;
+    if (vecs > 0)
+        hipLaunchKernelGGL(k_tanh_standin_vec<T>, dim3(grid_for(vecs, 256, 256 * 64)), dim3(256), 0, st, u, y, vecs);
+    if (done < count)
+        hipLaunchKernelGGL(k_tanh_standin<T>, dim3(grid_for(count - done, 256, 256 * 64)), dim3(256), 0, st,
+                           u + done, y + done, count - done);
+}
+
 hipError_t launch_tanh_standin(const void *u, void *y, bool bf16, int64_t count, hipStream_t st) {
-    const unsigned g = grid_for(count, 256, 256 * 64);
-    if (bf16)
-        hipLaunchKernelGGL(k_tanh_standin<bf16_t>, dim3(g), dim3(256), 0, st, (const bf16_t *)u,
-                           (bf16_t *)y, count);
-    else
-        hipLaunchKernelGGL(k_tanh_standin<float>, dim3(g), dim3(256), 0, st, (const float *)u,
-                           (float *)y, count);
+    if (bf16) tanh_standin_t((const bf16_t *)u, (bf16_t *)y, count, st);
+    else tanh_standin_t((const float *)u, (float *)y, count, st);
     return hipGetLastError();
 }
 
