@@ -312,7 +312,11 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // NRB W fragments per k-step take 4 NRB VGPRs)
 template <int NRB> constexpr int small_kb() { return NRB <= kMaxRowBlocks ? 4 : 1; }
 constexpr int kSmallPass = kMaxRowBlocks;  // row blocks per pass of the LDS reduction
-template <bool FUSED, int NRB, bool F8>
+// ONE: the wave's slice is one batch (kpw <= kSmallKB, decode-sized calls):
+// straight-line code, so the compiler counts the loads in flight instead of
+// waiting for all of them before the first element, and does not wait for the
+// stores before the reduction (a loop, or a join with one, makes it do both).
+template <bool FUSED, int NRB, bool F8, bool ONE>
 __global__ void __launch_bounds__(64 * kSmallWaves, 2)
 k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
                     const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
@@ -346,32 +350,38 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
 #pragma unroll
     for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
-    for (int kb = 0; kb < kpw; kb += kSmallKB) {
+    // one batch of kSmallKB k-steps starting at k-step kb of the wave's slice
+    auto batch = [&](int kb) {
         SV rr[kSmallKB];
         u32x4 yy[kSmallKB], gm[kSmallKB], wv[kSmallKB][NRB];
         bool kin[kSmallKB];
+        // Every load is issued unconditionally (a masked one reads the start of
+        // its tensor) and its value zeroed after: with the loads under
+        // branches the compiler waits for all of them before the first use.
+        constexpr u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int ks = 0; ks < kSmallKB; ++ks) {
             const int c0 = c_wave + (kb + ks) * kChunk;   // whole 32-channel chunk in or out (d % 32 == 0)
             kin[ks] = kb + ks < kpw && c0 < d;
             const int c = c0 + 8 * g;
-            rr[ks] = SV{};
-            yy[ks] = gm[ks] = u32x4{0u, 0u, 0u, 0u};
+            const bool okr = kin[ks] && valid;
+            const SV rv = *reinterpret_cast<const SV *>(okr ? srow + c : state);
+            rr[ks] = okr ? rv : SV{};
+            if (FUSED) {
+                const u32x4 yv = *reinterpret_cast<const u32x4 *>(okr ? yrow + c : y);
+                yy[ks] = okr ? yv : z4;
+            } else {
+                yy[ks] = z4;
+            }
+            const u32x4 gv = *reinterpret_cast<const u32x4 *>(kin[ks] ? gamma + (int64_t)br * d + c : gamma);
+            gm[ks] = kin[ks] ? gv : z4;
 #pragma unroll
-            for (int k = 0; k < NRB; ++k) wv[ks][k] = u32x4{0u, 0u, 0u, 0u};
-            if (kin[ks]) {
-                if (valid) {
-                    rr[ks] = *reinterpret_cast<const SV *>(srow + c);
-                    if (FUSED) yy[ks] = *reinterpret_cast<const u32x4 *>(yrow + c);
-                }
-                gm[ks] = *reinterpret_cast<const u32x4 *>(gamma + (int64_t)br * d + c);
-#pragma unroll
-                for (int k = 0; k < NRB; ++k) {
-                    const int row = 16 * k + m16;
-                    const bf16_t *src = row < sh.r ? wd + (int64_t)row * nd
-                                      : (row < sh.rows ? ww + (int64_t)(row - sh.r) * nd : nullptr);
-                    if (src) wv[ks][k] = *reinterpret_cast<const u32x4 *>(src + (int64_t)br * d + c);
-                }
+            for (int k = 0; k < NRB; ++k) {
+                const int row = 16 * k + m16;
+                const bool okw = kin[ks] && row < sh.rows;
+                const bf16_t *src = row < sh.r ? wd + (int64_t)row * nd : ww + (int64_t)(row - sh.r) * nd;
+                const u32x4 wvv = *reinterpret_cast<const u32x4 *>(okw ? src + (int64_t)br * d + c : wd);
+                wv[ks][k] = okw ? wvv : z4;
             }
         }
 #pragma unroll
@@ -405,6 +415,11 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
                 acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bl), acc[k], 0, 0, 0);
             }
         }
+    };
+    if constexpr (ONE) {
+        batch(0);
+    } else {
+        for (int kb = 0; kb < kpw; kb += kSmallKB) batch(kb);
     }
     // this wave's share of ss per token: the four lane groups hold its channels
     ss += __shfl_xor(ss, 16, 64);
@@ -671,9 +686,16 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
         const unsigned sgrid = (unsigned)(((sh.N + 15) / 16) * sh.n * sh.ksplit);
 #define GR_K1S(NRB)                                                                         \
     case NRB:                                                                               \
-        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8>), dim3(sgrid), dim3(64 * kSmallWaves), 0, st, \
-                           (T *)a.state, y, a.s_in, (const bf16_t *)a.gamma,                \
-                           (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
+        if (sh.small_kpw <= small_kb<NRB>())                                                \
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, true>), dim3(sgrid),    \
+                               dim3(64 * kSmallWaves), 0, st, (T *)a.state, y, a.s_in,      \
+                               (const bf16_t *)a.gamma, (const bf16_t *)a.wd,               \
+                               (const bf16_t *)a.ww, w, sh);                                \
+        else                                                                                \
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, false>), dim3(sgrid),   \
+                               dim3(64 * kSmallWaves), 0, st, (T *)a.state, y, a.s_in,      \
+                               (const bf16_t *)a.gamma, (const bf16_t *)a.wd,               \
+                               (const bf16_t *)a.ww, w, sh);                                \
         break;
         switch (sh.row_blocks) {
             GR_K1S(1) GR_K1S(2) GR_K1S(3) GR_K1S(4) GR_K1S(5) GR_K1S(6) GR_K1S(7) GR_K1S(8)

@@ -112,8 +112,9 @@ k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float ep
 // words (exact for n = 4) masked to one half, so v_dot2 forms (gamma/n) R'
 // straight from the packed state.  Pipeline: the state of the chunk two ahead
 // and the W_up rows of the chunk after it are in flight while a chunk is
-// combined.
-template <int NB, int RKS, bool F8>
+// combined.  ONE: every range is one chunk (decode-sized calls): all loads go
+// out at once, with no prefetch and no loop.
+template <int NB, int RKS, bool F8, bool ONE>
 __global__ void __launch_bounds__(kK2Threads, kK2WavesPerSimd)
 k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ gamma,
                const bf16_t *__restrict__ wu, bf16_t *__restrict__ u, Workspace ws, FastShape sh,
@@ -137,31 +138,39 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     const bool valid = t < sh.N;
     const int c_begin = range * sh.k2_chan;
     const int c_end = (c_begin + sh.k2_chan) < d ? (c_begin + sh.k2_chan) : d;
-    const int nit = (c_end - c_begin) / kChunk;        // 32-channel chunks of this range
+    const int nit = (c_end - c_begin) / kChunk;        // 32-channel chunks of this range (>= 1)
     const float inv_n = 1.0f / (float)NB;
+    // Loads are issued without conditions (with conditions the compiler waits
+    // for every load in flight before the first use, which at one or two chunks
+    // per workgroup is the whole kernel): a token past the end of a ragged tile
+    // reads the last token (its u is never stored), a prefetch past the last
+    // chunk re-reads that chunk (never used), and W_up / gamma entries outside
+    // the range or past r read the start of their tensor and are zeroed.
+    const int64_t tl_ = valid ? t : sh.N - 1;          // token whose data this lane loads
+    constexpr u32x4 z4 = {0u, 0u, 0u, 0u};
 
     // W_up rows (branch i, channel c) of one iteration; row index i * KC + cc
     u32x4 wreg[WV];
     uint32_t greg[NG];
     auto load_w = [&](int it) {
-        const int c0 = c_begin + it * KC;
+        const int c0 = c_begin + (it < nit ? it : nit - 1) * KC;
 #pragma unroll
         for (int q = 0; q < WV; ++q) {
             const int v = tid + q * kK2Threads;
             const int row = v / (RK / 8), kv = v % (RK / 8);
             const int i = row / KC, cc = row % KC;
-            wreg[q] = u32x4{0u, 0u, 0u, 0u};
-            if (v < NV && it < nit && c0 + cc < c_end && kv * 8 < r)
-                wreg[q] = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c0 + cc) * r + kv * 8);
+            const bool ok = v < NV && c0 + cc < c_end && kv * 8 < r;
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(ok ? wu + ((int64_t)i * d + c0 + cc) * r + kv * 8 : wu);
+            wreg[q] = ok ? wv : z4;
         }
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
             const int v = tid + q * kK2Threads;
-            greg[q] = 0u;
-            if (v < NB * KC && it < nit && c0 + v % KC < c_end) {
-                const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)(v / KC) * d + c0 + v % KC]) * inv_n);
-                greg[q] = (v & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
-            }
+            const bool ok = v < NB * KC && c0 + v % KC < c_end;
+            const bf16_t gr = gamma[ok ? (int64_t)(v / KC) * d + c0 + v % KC : 0];
+            const bf16_t gk = f32_to_bf16(bf16_to_f32(gr) * inv_n);
+            const uint32_t gw = (v & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+            greg[q] = ok ? gw : 0u;
         }
     };
     // LDS row of (branch i, channel cc of the chunk): MFMA row order
@@ -188,40 +197,26 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
     float rms[NB];
 #pragma unroll
     for (int ks = 0; ks < RKS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
-        if (valid) {
-            v = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK + ks * 32 + 8 * g);
-            vl = *reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK + ks * 32 + 8 * g);
-        }
-        bop[ks] = as_bf16x8(v);
-        bopl[ks] = as_bf16x8(vl);
+        bop[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (tl_ * 2) * RK + ks * 32 + 8 * g));
+        bopl[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (tl_ * 2 + 1) * RK + ks * 32 + 8 * g));
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) rms[i] = valid ? ws.rms[t * NB + i] : 1.0f;
+    for (int i = 0; i < NB; ++i) rms[i] = ws.rms[tl_ * NB + i];
 
-    const typename StateT<F8>::type *srow = state + t * (int64_t)NB * d + 8 * g;
+    const typename StateT<F8>::type *srow = state + tl_ * (int64_t)NB * d + 8 * g;
     bf16_t *urow = u + t * (int64_t)d + 8 * g;
     const int m16 = lane & 15;  // A row this lane feeds
 
     u32x4 s0[NB], s1[NB];
     auto load_state = [&](int it, u32x4 (&sv)[NB]) {
+        const int c0 = c_begin + (it < nit ? it : nit - 1) * KC;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int c0 = c_begin + it * KC;
-            sv[i] = u32x4{0u, 0u, 0u, 0u};
-            if (valid && it < nit && c0 < c_end)
-                sv[i] = load8_as_bf16<F8>(srow + (int64_t)i * d + c0);
-        }
+        for (int i = 0; i < NB; ++i) sv[i] = load8_as_bf16<F8>(srow + (int64_t)i * d + c0);
     };
 
-    load_w(0);
-    store_w(0);
-    load_w(1);
-    load_state(0, s0);
-    __syncthreads();
-    for (int it = 0; it < nit; ++it) {
+    // gate and combine chunk `it` (W_up in LDS buffer it & 1, its state in s0)
+    auto combine = [&](int it) {
         const int cur = it & 1;
-        load_state(it + 1, s1);
         {
             const int c0 = c_begin + it * KC;
             float uacc[8];
@@ -259,7 +254,25 @@ k_gate_combine(const typename StateT<F8>::type *__restrict__ state, const bf16_t
                 *reinterpret_cast<u32x4 *>(urow + c0) = o;
             }
         }
-        if (it + 1 < nit) store_w(cur ^ 1);
+    };
+
+    if constexpr (ONE) {
+        load_state(0, s0);
+        load_w(0);
+        store_w(0);
+        __syncthreads();
+        combine(0);
+        return;
+    }
+    load_w(0);
+    store_w(0);
+    load_w(1);
+    load_state(0, s0);
+    __syncthreads();
+    for (int it = 0; it < nit; ++it) {
+        load_state(it + 1, s1);
+        combine(it);
+        if (it + 1 < nit) store_w((it & 1) ^ 1);
         load_w(it + 2);
         __syncthreads();
 #pragma unroll
@@ -771,9 +784,14 @@ hipError_t launch_k2(const ReadArgs &a, const FastShape &sh, const Workspace &w,
     const unsigned grid = (unsigned)(((sh.N + kK2Tile - 1) / kK2Tile) * ranges);
 #define GR_K2(RKS)                                                                          \
     case RKS:                                                                               \
-        hipLaunchKernelGGL((k_gate_combine<NB, RKS, F8>), dim3(grid), dim3(kK2Threads), 0, st, \
-                           (const typename StateT<F8>::type *)a.state, (const bf16_t *)a.gamma, \
-                           (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);             \
+        if (sh.k2_chan == kChunk)                                                           \
+            hipLaunchKernelGGL((k_gate_combine<NB, RKS, F8, true>), dim3(grid), dim3(kK2Threads), 0, st, \
+                               (const typename StateT<F8>::type *)a.state, (const bf16_t *)a.gamma, \
+                               (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);         \
+        else                                                                                \
+            hipLaunchKernelGGL((k_gate_combine<NB, RKS, F8, false>), dim3(grid), dim3(kK2Threads), 0, st, \
+                               (const typename StateT<F8>::type *)a.state, (const bf16_t *)a.gamma, \
+                               (const bf16_t *)a.wu, (bf16_t *)a.u, w, sh, ranges);         \
         break;
     switch (sh.rk / 32) {
         GR_K2(1) GR_K2(2) GR_K2(3) GR_K2(4)
