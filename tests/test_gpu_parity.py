@@ -274,12 +274,19 @@ def test_wide_gate_without_write_projection():
     check("wide no-write u", u, ou, "bf16")
 
 
-def test_no_write_projection_gives_unit_strength():
-    X = inputs.make_gr_inputs(40, 4, 256, 16, "bf16", seed=41, with_write=False)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_no_write_projection_gives_unit_strength(dt):
+    """No W_write: s == 1 (the fp32 case takes the small-row kernel, whose
+    one-batch form loads W_down rows in place of the missing write rows)."""
+    X = inputs.make_gr_inputs(40, 4, 256, 16, dt, seed=41, with_write=False)
     u, s = gr.read(X.X.to(DEV), dev_params(X.params[0]))
     assert torch.all(s == 1.0)
-    ou, _, A = orc_read(X.X, X.params[0], "bf16")
-    check("no-write u", u, ou, "bf16")
+    ou, _, A = orc_read(X.X, X.params[0], dt)
+    check("no-write u", u, ou, dt)
+    if dt == "f32":
+        S = X.X.to(DEV)
+        u2, s2 = gr.fused_write_read(S, X.y.to(DEV), s.clone(), dev_params(X.params[0]))
+        assert torch.all(s2 == 1.0)
 
 
 def test_zero_write_projection_gives_exactly_one():

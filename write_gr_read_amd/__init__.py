@@ -20,6 +20,7 @@ Hyper-Connections / mHC (same paper reading, sec. 2; "DepthBench", sec. 2.5):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -135,6 +136,10 @@ def _pdt(state: torch.Tensor) -> torch.dtype:
 
 
 def _dev(t: torch.Tensor, name: str, shape, dtype, device) -> int:
+    # one combined test for the usual case; the checks below name what is wrong
+    if (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.shape == shape
+            and (device is None or t.device == device) and t.is_contiguous()):
+        return t.data_ptr()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
@@ -167,14 +172,22 @@ def _layer(layer, n: int, d: int, dtype, device, eps: float) -> _Layer:
     return _Layer(n, d, r, float(eps), g, wd, wu, ww)
 
 
+# The current HIP stream of a device as a raw pointer; torch's accessor that
+# skips building a Stream object (about 0.2 instead of 1.8 us per call) where
+# this torch has it.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device) -> int:
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
     return torch.cuda.current_stream(device).cuda_stream
 
 
 _workspaces = {}
 
 
-def _workspace(device, nbytes: int) -> Tuple[int, int]:
+def _workspace(device, nbytes: int, stream: Optional[int] = None) -> Tuple[int, int]:
     """Scratch buffer per (device, stream), grown on demand: calls on one
     stream are ordered, so they may share it; calls on different streams get
     their own.  The library needs no initialisation of it.  (Under graph
@@ -182,7 +195,7 @@ def _workspace(device, nbytes: int) -> Tuple[int, int]:
     the capture.)"""
     if nbytes == 0:
         return 0, 0
-    key = (device, _stream(device))
+    key = (device, _stream(device) if stream is None else stream)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -190,13 +203,22 @@ def _workspace(device, nbytes: int) -> Tuple[int, int]:
     return buf.data_ptr(), buf.numel()
 
 
-def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
-                   has_write: bool = True) -> int:
+@functools.lru_cache(maxsize=512)
+def _workspace_size(op: int, code: int, N: int, n: int, d: int, r: int, has_write: bool,
+                    variant: Optional[str]) -> int:
     L = _Layer(n, d, r, 1e-6, None, None, None, 16 if has_write else None)
     out = ctypes.c_size_t(0)
-    code = {torch.bfloat16: GR_BF16, torch.float8_e4m3fn: GR_FP8_E4M3}.get(dtype, GR_F32)
     _call("gr_workspace_size", op, code, N, ctypes.byref(L), ctypes.byref(out))
     return out.value
+
+
+def workspace_size(op: int, dtype: torch.dtype, N: int, n: int, d: int, r: int,
+                   has_write: bool = True) -> int:
+    """Workspace bytes of a call (a pure function of its shape and of the
+    GR_KERNEL_VARIANT setting, so remembered per distinct argument set)."""
+    code = {torch.bfloat16: GR_BF16, torch.float8_e4m3fn: GR_FP8_E4M3}.get(dtype, GR_F32)
+    return _workspace_size(int(op), code, int(N), int(n), int(d), int(r), bool(has_write),
+                           os.environ.get("GR_KERNEL_VARIANT"))
 
 
 # ------------------------------------------------------------------ public API
@@ -224,8 +246,9 @@ def read(state: torch.Tensor, layer, eps: float = 1e-6, u: Optional[torch.Tensor
     up = _dev(u, "u", (N, d), dt, dev)
     spo = _dev(s, "s", (N, n), torch.float32, dev)
     need = workspace_size(GR_OP_READ, state.dtype, N, n, d, L.r, layer.w_write is not None)
-    wp, wn = _workspace(dev, need)
-    _call("gr_read", sp, _dt(state), N, ctypes.byref(L), up, spo, wp, wn, _stream(dev))
+    st = _stream(dev)
+    wp, wn = _workspace(dev, need, st)
+    _call("gr_read", sp, _dt(state), N, ctypes.byref(L), up, spo, wp, wn, st)
     return u, s
 
 
@@ -259,9 +282,9 @@ def fused_write_read(state: torch.Tensor, y: torch.Tensor, s_in: torch.Tensor, l
     up = _dev(u, "u_next", (N, d), dt, dev)
     spo = _dev(s, "s_next", (N, n), torch.float32, dev)
     need = workspace_size(GR_OP_FUSED_WRITE_READ, state.dtype, N, n, d, L.r, layer.w_write is not None)
-    wp, wn = _workspace(dev, need)
-    _call("gr_fused_write_read", sp, yp, sip, _dt(state), N, ctypes.byref(L), up, spo, wp, wn,
-          _stream(dev))
+    st = _stream(dev)
+    wp, wn = _workspace(dev, need, st)
+    _call("gr_fused_write_read", sp, yp, sip, _dt(state), N, ctypes.byref(L), up, spo, wp, wn, st)
     return u, s
 
 

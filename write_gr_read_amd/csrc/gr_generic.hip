@@ -129,6 +129,10 @@ k_read_generic(T *__restrict__ state, const W *__restrict__ y, const float *__re
 // four branches (and of all projection rows) go out together instead of one
 // loop iteration's round trip after another; every reduction hands all its
 // sums to every thread (z, SiLU(z) and the write logits stay in registers).
+// ONE (the weights a thread needs fit in registers: d = 256 with r = 16): the
+// W_down / W_write rows and the W_up rows are loaded with the state, so the
+// whole call is one memory round trip followed by two block reductions;
+// otherwise the projection rows come 16 at a time, one round trip per pass.
 // Same arithmetic and order of operations per element as k_read_generic.
 template <bool FUSED, int EPT, int RB>
 __global__ void __launch_bounds__(kGenThreads)
@@ -138,11 +142,43 @@ k_read_small(float *__restrict__ state, const float *__restrict__ y, const float
              float *__restrict__ s_out) {
     constexpr int NB = 4, D = kGenThreads * EPT, ND = NB * D, R = 16 * RB;
     constexpr int PASSES = RB + 1;                   // 16 projection rows each; the last one the write rows
-    __shared__ float red[16 * (kGenThreads / 64)];
+    constexpr int ROWS = R + NB;                     // down rows, then the write rows
+    constexpr bool ONE = NB * EPT * ROWS <= 96 && NB * EPT * R <= 64;
+    constexpr int KR = ONE ? ROWS : 16;              // sums per projection reduction
+    __shared__ float red[(KR > NB ? KR : NB) * (kGenThreads / 64)];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     float *Rt = state + t * ND;
     const bool haw = ww != nullptr;
+
+    // ONE: every weight this thread uses, issued before the state is touched
+    // (a missing W_write reads W_down's rows instead; their sums are unused)
+    float wv[ONE ? ROWS : 1][NB][EPT];
+    float wuv[ONE ? NB : 1][EPT][ONE ? R : 1];
+    if constexpr (ONE) {
+#pragma unroll
+        for (int k = 0; k < ROWS; ++k) {
+            const float *wrow = k < R ? wd + (int64_t)k * ND : (haw ? ww + (int64_t)(k - R) * ND : wd);
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int q = 0; q < EPT; ++q) wv[k][i][q] = wrow[i * D + tid + kGenThreads * q];
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                const float4 *wrow = reinterpret_cast<const float4 *>(wu + (int64_t)(i * D + tid + kGenThreads * q) * R);
+#pragma unroll
+                for (int k4 = 0; k4 < R / 4; ++k4) {
+                    const float4 w4 = wrow[k4];
+                    wuv[i][q][4 * k4] = w4.x;
+                    wuv[i][q][4 * k4 + 1] = w4.y;
+                    wuv[i][q][4 * k4 + 2] = w4.z;
+                    wuv[i][q][4 * k4 + 3] = w4.w;
+                }
+            }
+    }
 
     // eq:write (FUSED) and the sums of squares of eq:rms
     float rv[NB][EPT], gv[NB][EPT], ss[NB];
@@ -175,26 +211,41 @@ k_read_small(float *__restrict__ state, const float *__restrict__ y, const float
 
     // eq:gate down projection (rows k < R) and eq:s logits (the n rows of W_write)
     float proj[16 * PASSES];
+    if constexpr (ONE) {
+        float acc[ROWS];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        float acc[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < ROWS; ++k) {
             acc[k] = 0.f;
-            const int row = 16 * p + k;
-            const bool on = p < RB || (haw && k < NB);
-            if (on) {
-                const float *wrow = p < RB ? wd + (int64_t)row * ND : ww + (int64_t)k * ND;
 #pragma unroll
-                for (int i = 0; i < NB; ++i)
+            for (int i = 0; i < NB; ++i)
 #pragma unroll
-                    for (int q = 0; q < EPT; ++q)
-                        acc[k] = fmaf(wrow[i * D + tid + kGenThreads * q], gv[i][q], acc[k]);
-            }
+                for (int q = 0; q < EPT; ++q) acc[k] = fmaf(wv[k][i][q], gv[i][q], acc[k]);
         }
         block_sum_many(acc, red);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) proj[16 * p + k] = acc[k] / (float)NB;
+        for (int k = 0; k < ROWS; ++k) proj[k] = acc[k] / (float)NB;
+    } else {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            float acc[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                acc[k] = 0.f;
+                const int row = 16 * p + k;
+                const bool on = p < RB || (haw && k < NB);
+                if (on) {
+                    const float *wrow = p < RB ? wd + (int64_t)row * ND : ww + (int64_t)k * ND;
+#pragma unroll
+                    for (int i = 0; i < NB; ++i)
+#pragma unroll
+                        for (int q = 0; q < EPT; ++q)
+                            acc[k] = fmaf(wrow[i * D + tid + kGenThreads * q], gv[i][q], acc[k]);
+                }
+            }
+            block_sum_many(acc, red);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) proj[16 * p + k] = acc[k] / (float)NB;
+        }
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) proj[k] = silu_f(proj[k]);
@@ -206,10 +257,15 @@ k_read_small(float *__restrict__ state, const float *__restrict__ y, const float
         float acc_u = 0.f;
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const float *wrow = wu + (int64_t)(i * D + c) * R;
             float l = 0.f;
+            if constexpr (ONE) {
 #pragma unroll
-            for (int k = 0; k < R; ++k) l = fmaf(wrow[k], proj[k], l);
+                for (int k = 0; k < R; ++k) l = fmaf(wuv[i][q][k], proj[k], l);
+            } else {
+                const float *wrow = wu + (int64_t)(i * D + c) * R;
+#pragma unroll
+                for (int k = 0; k < R; ++k) l = fmaf(wrow[k], proj[k], l);
+            }
             acc_u = fmaf(sigmoid_f(l), gv[i][q], acc_u);
         }
         u[t * D + c] = acc_u / (float)NB;
