@@ -313,6 +313,67 @@ __device__ __forceinline__ void load_act_rms(const Workspace &ws, const FastShap
 // that branch: the prefetch costs no registers beyond one step's state.  The
 // activations and rms of the next tile are loaded before the state of its
 // first step, so waiting for them never waits for that state.
+// Stage the W_up rows of a channel range (every branch, NC 32-channel chunks,
+// MFMA row order: LDS row (i NC + chunk) 32 + 16h + m holds channel
+// 8(m/4) + 4h + m%4 of the chunk) and gamma/n of the range (bf16 in the half word
+// of the channel's parity).  A thread's loads go out BATCH at a time before
+// their LDS stores, one round trip per batch (as a loop of load-then-store,
+// one per vector).  Channels past nchan and k past r stage zeros.
+template <int NB, int CH, int RK, int THREADS, int BATCH>
+__device__ __forceinline__ void stage_wup(bf16_t *lds_u, uint32_t *lds_g, const bf16_t *__restrict__ wu,
+                                          const bf16_t *__restrict__ gamma, int d, int r, int c_begin,
+                                          int nchan, float inv_n, int tid) {
+    constexpr int NC = CH / kChunk;
+    constexpr int kPitch = RK + 8;
+    constexpr int NVEC = NB * CH * (RK / 8);
+    constexpr int PER = (NVEC + THREADS - 1) / THREADS;
+    constexpr int GPER = (NB * CH + THREADS - 1) / THREADS;
+    constexpr u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += BATCH) {
+        u32x4 w[BATCH];
+        uint32_t gw[GPER];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int v = tid + (b0 + j) * THREADS;
+            const int row = v / (RK / 8), kv = v % (RK / 8);
+            const int i = row / CH, cc = row % CH;
+            const bool ok = b0 + j < PER && v < NVEC && cc < nchan && kv * 8 < r;
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(ok ? wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8 : wu);
+            w[j] = ok ? wv : z4;
+        }
+        if (b0 == 0) {
+#pragma unroll
+            for (int j = 0; j < GPER; ++j) {
+                const int v = tid + j * THREADS;
+                const int i = v / CH, cc = v % CH;
+                const bool ok = v < NB * CH && cc < nchan;
+                const bf16_t gr = gamma[ok ? (int64_t)i * d + c_begin + cc : 0];
+                const bf16_t gk = f32_to_bf16(bf16_to_f32(gr) * inv_n);
+                const uint32_t gv = (cc & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
+                gw[j] = ok ? gv : 0u;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int v = tid + (b0 + j) * THREADS;
+            if (b0 + j < PER && v < NVEC) {
+                const int row = v / (RK / 8), kv = v % (RK / 8);
+                const int i = row / CH, cc = row % CH, c32 = cc % kChunk;
+                const int pos = (i * NC + cc / kChunk) * kChunk + 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+                *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w[j];
+            }
+        }
+        if (b0 == 0) {
+#pragma unroll
+            for (int j = 0; j < GPER; ++j) {
+                const int v = tid + j * THREADS;
+                if (v < NB * CH) lds_g[v] = gw[j];
+            }
+        }
+    }
+}
+
 template <int RKS> struct ResidentCfg {
     // channels per workgroup: keeps the staged W_up near 72 KiB (two per CU);
     // a wide gate (RKS > 4) gets 32 channels, ~84 KiB (one per CU)
@@ -377,24 +438,7 @@ k_gate_combine_resident(const bf16_t *__restrict__ state, const bf16_t *__restri
     for (int i = 0; i < NB; ++i) load_state(T, 0, i, sv[i]);
 
     // stage W_up rows (branch i, channel cc of the range) and gamma/n
-    for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
-        const int row = v / (RK / 8), kv = v % (RK / 8);
-        const int i = row / CH, cc = row % CH, c32 = cc % kChunk;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (cc < nchan && kv * 8 < r)
-            w = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8);
-        const int pos = (i * NC + cc / kChunk) * kChunk + 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
-        *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w;
-    }
-    for (int v = tid; v < NB * CH; v += kResThreads) {
-        const int i = v / CH, cc = v % CH;
-        uint32_t gw = 0u;
-        if (cc < nchan) {
-            const bf16_t gk = f32_to_bf16(bf16_to_f32(gamma[(int64_t)i * d + c_begin + cc]) * inv_n);
-            gw = (cc & 1) ? ((uint32_t)gk << 16) : (uint32_t)gk;
-        }
-        lds_g[v] = gw;
-    }
+    stage_wup<NB, CH, RK, kResThreads, 8>(lds_u, lds_g, wu, gamma, d, r, c_begin, nchan, inv_n, tid);
     __syncthreads();
 
     for (;;) {
@@ -540,6 +584,8 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
         return *reinterpret_cast<const SV *>(state + t * (int64_t)NB * d + (int64_t)i * d + rg * CH + 8 * g);
     };
     // W_up rows (branch i, channel cc of range rg) in MFMA row order, and gamma/n
+    // (a loop of load-then-store; issuing a batch of loads before the stores, as
+    // the resident forms do, made this kernel slower: 312 -> 343 us at r = 320)
     auto stage = [&](int rg) {
         const int c_begin = rg * CH;
         for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
@@ -698,20 +744,47 @@ k_gate_combine_resident_fp8(const fp8_t *__restrict__ state, const bf16_t *__res
 #pragma unroll
     for (int i = 0; i < NB; ++i) sv[i] = load_state(T, 0, i);
 
-    // stage W_up rows (branch i, channel cc of the range) and gamma/n
-    for (int v = tid; v < NB * CH * (RK / 8); v += kResThreads) {
-        const int row = v / (RK / 8), kv = v % (RK / 8);
-        const int i = row / CH, cc = row % CH, c64 = cc % kF8Unit;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (cc < nchan && kv * 8 < r)
-            w = *reinterpret_cast<const u32x4 *>(wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8);
-        const int pos = (i * NU + cc / kF8Unit) * kF8Unit + 16 * ((c64 >> 2) & 3) + 4 * (c64 >> 4) + (c64 & 3);
-        *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w;
-    }
-    for (int v = tid; v < NB * CH; v += kResThreads) {
-        const int i = v / CH, cc = v % CH;
-        lds_g[v] = cc < nchan ? bf16_to_f32(f32_to_bf16(bf16_to_f32(gamma[(int64_t)i * d + c_begin + cc]) * inv_n))
-                              : 0.f;
+    // stage W_up rows (branch i, channel cc of the range) and gamma/n: a thread's
+    // loads all go out before its LDS stores (one round trip, not one per vector)
+    {
+        constexpr int NVEC = NB * CH * (RK / 8);
+        constexpr int PER = (NVEC + kResThreads - 1) / kResThreads;
+        constexpr int GPER = (NB * CH + kResThreads - 1) / kResThreads;
+        u32x4 w[PER];
+        float gq[GPER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int v = tid + j * kResThreads;
+            const int row = v / (RK / 8), kv = v % (RK / 8);
+            const int i = row / CH, cc = row % CH;
+            const bool ok = v < NVEC && cc < nchan && kv * 8 < r;
+            const u32x4 wv = *reinterpret_cast<const u32x4 *>(ok ? wu + ((int64_t)i * d + c_begin + cc) * r + kv * 8 : wu);
+            w[j] = ok ? wv : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < GPER; ++j) {
+            const int v = tid + j * kResThreads;
+            const int i = v / CH, cc = v % CH;
+            const bool ok = v < NB * CH && cc < nchan;
+            const bf16_t gr = gamma[ok ? (int64_t)i * d + c_begin + cc : 0];
+            const float gv = bf16_to_f32(f32_to_bf16(bf16_to_f32(gr) * inv_n));
+            gq[j] = ok ? gv : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int v = tid + j * kResThreads;
+            if (v < NVEC) {
+                const int row = v / (RK / 8), kv = v % (RK / 8);
+                const int i = row / CH, cc = row % CH, c64 = cc % kF8Unit;
+                const int pos = (i * NU + cc / kF8Unit) * kF8Unit + 16 * ((c64 >> 2) & 3) + 4 * (c64 >> 4) + (c64 & 3);
+                *reinterpret_cast<u32x4 *>(&lds_u[pos * kPitch + kv * 8]) = w[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GPER; ++j) {
+            const int v = tid + j * kResThreads;
+            if (v < NB * CH) lds_g[v] = gq[j];
+        }
     }
     __syncthreads();
 
