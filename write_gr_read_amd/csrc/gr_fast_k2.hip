@@ -574,9 +574,6 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
     auto unit_tile = [&](int64_t q) { return tile0 + 8 * (q % ntx); };
     auto unit_range = [&](int64_t q) { return GS * (rg0 + rgstep * (int)(q / ntx)) + side; };
     auto token = [&](int64_t T) { return T * kResTile + wave * 16 + m16; };
-    auto load_act = [&](int64_t T, bf16x8 (&hi)[RKS], bf16x8 (&lo)[RKS], float (&rm)[NB]) {
-        load_act_rms<NB, RKS>(ws, sh, token(T), g, hi, lo, rm);
-    };
     // state of branch i, range rg of tile T: 8 channels per lane
     auto load_state = [&](int64_t T, int rg, int i) {
         const int64_t t = token(T);
@@ -604,13 +601,39 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
         }
     };
 
-    bf16x8 bop[RKS], bopl[RKS], nbop[RKS], nbopl[RKS];
+    // The activations (B operand) of a unit come in two halves of the k-steps,
+    // K0 and RKS - K0: the second half of the current unit is loaded while the
+    // first half's MFMAs run, and the next unit's first half into the registers
+    // the first half frees -- 80 instead of 160 VGPRs of activations in flight,
+    // which leaves the compiler room to keep more W_up fragment reads ahead of
+    // the MFMAs.  Each gate still accumulates its k-steps 0 .. RKS-1 in order.
+    constexpr int K0 = (RKS + 1) / 2, K1 = RKS - K0;
+    constexpr int RK_ = RKS * 32;
+    auto load_half = [&](int64_t T, int kb, int kn, bf16x8 *hi, bf16x8 *lo) {
+        int64_t t = token(T);
+        if (t >= sh.N) t = sh.N - 1;
+#pragma unroll
+        for (int k = 0; k < K0; ++k) {
+            if (k < kn) {
+                hi[k] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (t * 2) * RK_ + (kb + k) * 32 + 8 * g));
+                lo[k] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ws.act + (t * 2 + 1) * RK_ + (kb + k) * 32 + 8 * g));
+            }
+        }
+    };
+    auto load_rms = [&](int64_t T, float (&rm)[NB]) {
+        int64_t t = token(T);
+        if (t >= sh.N) t = sh.N - 1;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rm[i] = ws.rms[t * NB + i];
+    };
+    bf16x8 bA[K0], bAl[K0], bB[K0], bBl[K0];
     float rms[NB], nrms[NB];
     SV sv[NB];
     int64_t q = u0;
     int64_t T = unit_tile(q);
     int rg = unit_range(q);
-    load_act(T, bop, bopl, rms);
+    load_half(T, 0, K0, bA, bAl);
+    load_rms(T, rms);
 #pragma unroll
     for (int i = 0; i < NB; ++i) sv[i] = load_state(T, rg, i);
     stage(rg);
@@ -620,24 +643,56 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
         const bool more = q + 1 < u1;
         const int64_t Tn = more ? unit_tile(q + 1) : T;
         const int rn = more ? unit_range(q + 1) : rg;
-        if (more) load_act(Tn, nbop, nbopl, nrms);
+        load_half(T, K0, K1, bB, bBl);                // this unit's second half
+
+        f32x4 tl[NB][2];
+        // W_up fragments of chain c = (i, h), k-steps kb .. kb + K0 - 1, read one
+        // chain ahead of the MFMAs that use them
+        bf16x8 fa[2][K0];
+        auto read_frags = [&](int c, int kb, int kn, bf16x8 (&f)[K0]) {
+            const bf16_t *ap = &lds_u[((c >> 1) * CH + 16 * (c & 1) + m16) * kPitch + 8 * g];
+#pragma unroll
+            for (int k = 0; k < K0; ++k)
+                if (k < kn) f[k] = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + (kb + k) * 32));
+        };
+        read_frags(0, 0, K0, fa[0]);
+#pragma unroll
+        for (int c = 0; c < 2 * NB; ++c) {
+            if (c + 1 < 2 * NB) read_frags(c + 1, 0, K0, fa[(c + 1) & 1]);
+            else read_frags(0, K0, K1, fa[(c + 1) & 1]);   // the second half's first chain
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < K0; ++ks) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[c & 1][ks], bA[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[c & 1][ks], bAl[ks], acc, 0, 0, 0);
+            }
+            tl[c >> 1][c & 1] = acc;
+        }
+        if (more) {                                    // the next unit's first half, into the freed registers
+            load_half(Tn, 0, K0, bA, bAl);
+            load_rms(Tn, nrms);
+        }
 
         float uacc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) uacc[e] = 0.f;
+        constexpr int F0 = (2 * NB) & 1;                // buffer holding the second half's chain 0
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                f32x4 tl = {0.f, 0.f, 0.f, 0.f};
-                const bf16_t *ap = &lds_u[(i * CH + 16 * h + m16) * kPitch + 8 * g];
+                const int c = 2 * i + h;
+                const int cur = (F0 + c) & 1;
+                if (c + 1 < 2 * NB) read_frags(c + 1, K0, K1, fa[cur ^ 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < RKS; ++ks) {
-                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4 *>(ap + ks * 32));
-                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bop[ks], tl, 0, 0, 0);
-                    tl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bopl[ks], tl, 0, 0, 0);
+                for (int ks = 0; ks < K1; ++ks) {
+                    tl[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][ks], bB[ks], tl[i][h], 0, 0, 0);
+                    tl[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][ks], bBl[ks], tl[i][h], 0, 0, 0);
                 }
-                // tl[m] = -log2(e) * l for channel 8g + 4h + m of the range, branch i
+                const f32x4 tv = tl[i][h];
+                // tv[m] = -log2(e) * l for channel 8g + 4h + m of the range, branch i
                 const uint32_t *gp = &lds_g[i * CH + 8 * g + 4 * h];
                 float xe[4];                              // e4m3: elements 4h .. 4h+3 of the lane's 8
                 if constexpr (F8) {
@@ -652,7 +707,7 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
                         bterm = xe[m] * ((m & 1) ? bf16_hi(gp[m]) : bf16_lo(gp[m]));
                     else
                         bterm = dot2_bf16(sv[i][e >> 1], gp[m], 0.f);
-                    const float den = fmaf(__builtin_amdgcn_exp2f(tl[m]), rms[i], rms[i]);
+                    const float den = fmaf(__builtin_amdgcn_exp2f(tv[m]), rms[i], rms[i]);
                     uacc[e] = fmaf(bterm, __builtin_amdgcn_rcpf(den), uacc[e]);
                 }
             }
@@ -675,8 +730,6 @@ k_gate_combine_wide(const typename StateT<F8>::type *__restrict__ state, const b
             stage(rn);
             __syncthreads();
         }
-#pragma unroll
-        for (int ks = 0; ks < RKS; ++ks) { bop[ks] = nbop[ks]; bopl[ks] = nbopl[ks]; }
 #pragma unroll
         for (int i = 0; i < NB; ++i) rms[i] = nrms[i];
         T = Tn;
