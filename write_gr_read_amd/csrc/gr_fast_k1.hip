@@ -312,11 +312,13 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // NRB W fragments per k-step take 4 NRB VGPRs)
 template <int NRB> constexpr int small_kb() { return NRB <= kMaxRowBlocks ? 4 : 1; }
 constexpr int kSmallPass = kMaxRowBlocks;  // row blocks per pass of the LDS reduction
-// ONE: the wave's slice is one batch (kpw <= kSmallKB, decode-sized calls):
-// straight-line code, so the compiler counts the loads in flight instead of
-// waiting for all of them before the first element, and does not wait for the
-// stores before the reduction (a loop, or a join with one, makes it do both).
-template <bool FUSED, int NRB, bool F8, bool ONE>
+// ONEKB > 0: the wave's slice is one batch of at most ONEKB k-steps
+// (decode-sized calls; ONEKB = 1, 2 or 4 as the slice needs, so that no
+// k-step is loaded for nothing): straight-line code, so the compiler counts the
+// loads in flight instead of waiting for all of them before the first element,
+// and does not wait for the stores before the reduction (a loop, or a join
+// with one, makes it do both).  ONEKB = 0: the slice in batches of small_kb.
+template <bool FUSED, int NRB, bool F8, int ONEKB>
 __global__ void __launch_bounds__(64 * kSmallWaves, 2)
 k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
                     const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
@@ -324,7 +326,7 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
                     FastShape sh) {
     using T = typename StateT<F8>::type;
     using SV = typename StateT<F8>::vec8;
-    constexpr int kSmallKB = small_kb<NRB>();
+    constexpr int kSmallKB = ONEKB > 0 ? ONEKB : small_kb<NRB>();
     constexpr int PB = NRB < kSmallPass ? NRB : kSmallPass;   // row blocks per reduction pass
     constexpr int NPASS = (NRB + PB - 1) / PB;
     __shared__ float lds_p[kSmallWaves][4 * PB + 1][64];  // per wave: a pass's accumulators, then ss
@@ -416,7 +418,7 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
             }
         }
     };
-    if constexpr (ONE) {
+    if constexpr (ONEKB > 0) {
         batch(0);
     } else {
         for (int kb = 0; kb < kpw; kb += kSmallKB) batch(kb);
@@ -662,6 +664,35 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
     }
 }
 
+// The few-token kernel 1 at the batch size its slice needs (see k_stream_proj_small).
+template <bool FUSED, int NRB, bool F8>
+void launch_small(const ReadArgs &a, const FastShape &sh, const Workspace &w, unsigned sgrid, hipStream_t st) {
+    using T = typename StateT<F8>::type;
+    constexpr int KB = small_kb<NRB>();
+    const dim3 block(64 * kSmallWaves);
+    const bf16_t *y = (const bf16_t *)a.y, *gm = (const bf16_t *)a.gamma;
+    const bf16_t *wd = (const bf16_t *)a.wd, *ww = (const bf16_t *)a.ww;
+    if (sh.small_kpw <= 1) {
+        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 1>), dim3(sgrid), block, 0, st,
+                           (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
+        return;
+    }
+    if constexpr (KB >= 4) {
+        if (sh.small_kpw <= 2)
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 2>), dim3(sgrid), block, 0, st,
+                               (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
+        else if (sh.small_kpw <= 4)
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 4>), dim3(sgrid), block, 0, st,
+                               (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
+        else
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0>), dim3(sgrid), block, 0, st,
+                               (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
+    } else {
+        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0>), dim3(sgrid), block, 0, st,
+                           (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
+    }
+}
+
 template <bool FUSED, bool F8>
 hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     using T = typename StateT<F8>::type;
@@ -686,16 +717,7 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
         const unsigned sgrid = (unsigned)(((sh.N + 15) / 16) * sh.n * sh.ksplit);
 #define GR_K1S(NRB)                                                                         \
     case NRB:                                                                               \
-        if (sh.small_kpw <= small_kb<NRB>())                                                \
-            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, true>), dim3(sgrid),    \
-                               dim3(64 * kSmallWaves), 0, st, (T *)a.state, y, a.s_in,      \
-                               (const bf16_t *)a.gamma, (const bf16_t *)a.wd,               \
-                               (const bf16_t *)a.ww, w, sh);                                \
-        else                                                                                \
-            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, false>), dim3(sgrid),   \
-                               dim3(64 * kSmallWaves), 0, st, (T *)a.state, y, a.s_in,      \
-                               (const bf16_t *)a.gamma, (const bf16_t *)a.wd,               \
-                               (const bf16_t *)a.ww, w, sh);                                \
+        launch_small<FUSED, NRB, F8>(a, sh, w, sgrid, st);                                  \
         break;
         switch (sh.row_blocks) {
             GR_K1S(1) GR_K1S(2) GR_K1S(3) GR_K1S(4) GR_K1S(5) GR_K1S(6) GR_K1S(7) GR_K1S(8)
