@@ -79,11 +79,14 @@ def test_tiny_fp32_workload():
 @pytest.mark.parametrize("N,n,d,r", [
     (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (9, 2, 128, 1), (17, 3, 64, 5),
     (3, 8, 32, 2), (70, 4, 512, 32), (130, 4, 1024, 48), (33, 4, 2048, 32), (64, 4, 256, 0),
+    (200, 4, 4096, 64),
 ])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_shapes(N, n, d, r, dtype):
     """Off-workload shapes: several tiles, ragged token tails, n in 1..8,
-    r in {0, 1, 2, 5, ...}; both storage dtypes."""
+    r in {0, 1, 2, 5, ...}; both storage dtypes.  With a bf16 state the few-token
+    kernel 1 takes its one-batch forms at 1 (N <= 64 at d = 4096), 2 (N = 200) and
+    4 k-steps (the decode workload) and its batch loop (N = 512, below)."""
     X = inputs.make_gr_inputs(N, n, d, r, dtype, seed=N * 131 + n * 17 + d + r, w_std=0.05,
                               branch_scale=None)
     run_read_write_fused(X, f"N{N}-n{n}-d{d}-r{r}-{dtype}")
