@@ -381,7 +381,8 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
             for (int k = 0; k < NRB; ++k) {
                 const int row = 16 * k + m16;
                 const bool okw = kin[ks] && row < sh.rows;
-                const bf16_t *src = row < sh.r ? wd + (int64_t)row * nd : ww + (int64_t)(row - sh.r) * nd;
+                const bf16_t *src = row < sh.r ? wd + (int64_t)row * nd
+                                  : (okw ? ww + (int64_t)(row - sh.r) * nd : wd);
                 const u32x4 wvv = *reinterpret_cast<const u32x4 *>(okw ? src + (int64_t)br * d + c : wd);
                 wv[ks][k] = okw ? wvv : z4;
             }
