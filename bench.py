@@ -20,6 +20,11 @@ shape, one line each; decode: us per
 call with the state warm in cache, back to back; addnorm:
 the n = 1 fused residual add + RMSNorm; chain: 32 sublayers of read -> F ->
 fused write+read -> ... -> write with the elementwise F stand-in).
+
+Every timed region starts after about 100 ms of untimed streaming copies
+(--no-burn-in skips them) so that the GPU's power management has settled; the
+default line measures the copy probe and the other workloads first and times
+the headline last.
 """
 import argparse
 import hashlib
@@ -133,6 +138,7 @@ def copy_probe(gr, torch, dev, stream):
     nbytes = 1 << 30
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1)
     b = torch.empty_like(a)
+    burn_in()
     for _ in range(3):
         gr.copy(a, b)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -144,9 +150,41 @@ def copy_probe(gr, torch, dev, stream):
     return 2 * nbytes / (start.elapsed_time(stop) / 10 * 1e-3) / 1e9
 
 
-def timed(fn, steps, warmup, stream):
-    """Average ms per call of fn over `steps` calls after `warmup` calls."""
+BURN_IN_MS = 100.0   # 0 (--no-burn-in): measure without settling the GPU first
+_burn_buf = {}
+
+
+def burn_in():
+    """Untimed streaming copies (256 MiB each way) for about BURN_IN_MS ms right
+    before a timed region, so that the GPU's clocks have settled: a GPU that
+    was idle (e.g. while inputs were generated on the host) boosts, then slows
+    down for some tens of milliseconds while its power management settles
+    (calls 6-25 of the prefill call take ~470 us from idle, ~430 us once
+    settled).  Returns (copies, elapsed ms)."""
+    if BURN_IN_MS <= 0:
+        return 0, 0.0
     import torch
+    import write_gr_read_amd as gr
+    if "a" not in _burn_buf:
+        _burn_buf["a"] = torch.empty(1 << 28, dtype=torch.uint8, device="cuda:0")
+        _burn_buf["b"] = torch.empty_like(_burn_buf["a"])
+    a, b = _burn_buf["a"], _burn_buf["b"]
+    gr.copy(a, b)              # the library's first launch is not GPU time
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < BURN_IN_MS:
+        for _ in range(20):
+            gr.copy(a, b)
+        torch.cuda.synchronize()
+        n += 20
+    return n, (time.perf_counter() - t0) * 1e3
+
+
+def timed(fn, steps, warmup, stream):
+    """Average ms per call of fn over `steps` calls after `warmup` calls (after
+    the burn-in)."""
+    import torch
+    burn_in()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -423,6 +461,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="time the copy probe (always beside the headline; with --workload, before it)")
     ap.add_argument("--no-copy-probe", action="store_true", help="skip the copy probe")
+    ap.add_argument("--no-burn-in", action="store_true",
+                    help="skip the untimed burn-in copies at the start (profiling runs, whose "
+                         "summaries separate the call's kernels from the copy probe's)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the tiny / decode / add+RMSNorm / chain / HC / single-pass keys of the default line")
     ap.add_argument("--workload", default="prefill",
@@ -442,6 +483,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    global BURN_IN_MS
+    if args.no_burn_in:
+        BURN_IN_MS = 0.0
     if args.workload != "prefill":
         names = (["prefill_fp8", "prefill_r320", "prefill_fp8_r320", "decode", "addnorm", "chain", "tiny",
                   "variants", "hc_mhc", "hc_tanh"]
@@ -465,12 +509,46 @@ def main():
     s_next = torch.empty((N, n), dtype=torch.float32, device=dev)
     _, s_in = gr.read(X, p0)  # untimed: write strengths of the previous sublayer
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    alg = algorithmic_bytes(N, n, d, r)
 
+    # The copy probe and the other workloads' lines run before the headline is
+    # timed, and every timed region starts after a burn-in (see burn_in), so
+    # the headline is measured at the GPU's steady state.  The timed region is
+    # the warmup calls, then exactly the timed steps.
+    copy_gbps = None
+    if not args.no_copy_probe:
+        copy_gbps = copy_probe(gr, torch, dev, stream)
+        log(f"copy probe: {copy_gbps:.0f} GB/s (read + write of 1 GiB)")
+    others = None
+    if not args.no_others:
+        # the other configurations of the workload set, one key each with its
+        # own roofline: the tiny fp32 call and decode (us/call), the n = 1 fused
+        # add + RMSNorm, the 32-sublayer chain, mHC and HC on the prefill shape,
+        # and the single-pass kernel on this same prefill call
+        others = {}
+        for w in ("tiny", "decode", "addnorm", "chain", "hc_mhc", "hc_tanh"):
+            log(f"workload {w} ...")
+            res = bench_other(w, args, dev)
+            keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
+                    "warm", "cold", "graph_replay_us_per_call", "gr_ms_per_pass", "f_standin_ms_per_pass",
+                    "write_only_ms", "read_only_ms", "unfused_ms")
+            others[w] = {k: res[k] for k in keep if k in res}
+        os.environ["GR_KERNEL_VARIANT"] = "single"
+        try:
+            ms1 = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next), args.steps, args.warmup, stream)
+        finally:
+            del os.environ["GR_KERNEL_VARIANT"]
+        others["prefill_single_pass"] = {"value": N / (ms1 * 1e-3), "unit": "tokens/s", "ms_per_step": ms1,
+                                         "roofline": roofline(alg, ms1, "gr_fused_write_read (GR_KERNEL_VARIANT=single)")}
+        log(f"single-pass kernel on the prefill call: {ms1 * 1e3:.1f} us/call")
+
+    nb, msb = burn_in()
+    log(f"burn-in: {nb} untimed 256 MiB copies over {msb:.0f} ms (GPU clocks settle)")
     log(f"warmup {args.warmup} ...")
     for _ in range(args.warmup):
         gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"timing {args.steps} steps ...")
     t0 = time.perf_counter()
@@ -482,7 +560,6 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / args.steps
     tokens_per_s = N / (ms * 1e-3)
-    alg = algorithmic_bytes(N, n, d, r)
     gbps = alg / (ms * 1e-3) / 1e9
     log(f"fused write+read: {ms * 1e3:.1f} us/call, {tokens_per_s / 1e6:.2f} M tok/s, "
         f"{gbps:.0f} GB/s algorithmic ({gbps / PEAK_HBM_GBPS:.1%} of peak); wall {wall:.2f}s")
@@ -513,31 +590,9 @@ def main():
     out.update(percentiles(per_call_ms(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next),
                                        args.steps, stream)))
 
-    if not args.no_copy_probe:
-        out["copy_probe_GBps"] = copy_probe(gr, torch, dev, stream)
-        log(f"copy probe: {out['copy_probe_GBps']:.0f} GB/s (read + write of 1 GiB)")
-
-    if not args.no_others:
-        # the other configurations of the workload set, one key each with its
-        # own roofline: the tiny fp32 call and decode (us/call), the n = 1 fused
-        # add + RMSNorm, the 32-sublayer chain, mHC and HC on the prefill shape,
-        # and the single-pass kernel on this same prefill call
-        others = {}
-        for w in ("tiny", "decode", "addnorm", "chain", "hc_mhc", "hc_tanh"):
-            log(f"workload {w} ...")
-            res = bench_other(w, args, dev)
-            keep = ("metric", "value", "unit", "ms_per_step", "steps", "config", "roofline", "tokens_per_s",
-                    "warm", "cold", "graph_replay_us_per_call", "gr_ms_per_pass", "f_standin_ms_per_pass",
-                    "write_only_ms", "read_only_ms", "unfused_ms")
-            others[w] = {k: res[k] for k in keep if k in res}
-        os.environ["GR_KERNEL_VARIANT"] = "single"
-        try:
-            ms1 = timed(lambda: gr.fused_write_read(X, y, s_in, p1, u=u, s=s_next), args.steps, args.warmup, stream)
-        finally:
-            del os.environ["GR_KERNEL_VARIANT"]
-        others["prefill_single_pass"] = {"value": N / (ms1 * 1e-3), "unit": "tokens/s", "ms_per_step": ms1,
-                                         "roofline": roofline(alg, ms1, "gr_fused_write_read (GR_KERNEL_VARIANT=single)")}
-        log(f"single-pass kernel on the prefill call: {ms1 * 1e3:.1f} us/call")
+    if copy_gbps is not None:
+        out["copy_probe_GBps"] = copy_gbps
+    if others is not None:
         out["other_workloads"] = others
 
     if not args.no_cpu:
