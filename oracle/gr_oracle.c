@@ -3,7 +3,7 @@
  *
  * A plain, slow, single-threaded fp64 evaluation of the Gated Residual (GR)
  * read and write, of the fused write+read, and of the n = 1 fused residual
- * add + RMSNorm.  It exists to judge the HIP path; only the tests, the smoke
+ * add + RMSNorm.  It exists to check the HIP path; only the tests, the smoke
  * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
  * header, table or helper with the HIP library.
  *
