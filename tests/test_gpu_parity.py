@@ -79,14 +79,15 @@ def test_tiny_fp32_workload():
 @pytest.mark.parametrize("N,n,d,r", [
     (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (9, 2, 128, 1), (17, 3, 64, 5),
     (3, 8, 32, 2), (70, 4, 512, 32), (130, 4, 1024, 48), (33, 4, 2048, 32), (64, 4, 256, 0),
-    (200, 4, 4096, 64),
+    (200, 4, 4096, 64), (264, 4, 4096, 64),
 ])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_shapes(N, n, d, r, dtype):
     """Off-workload shapes: several tiles, ragged token tails, n in 1..8,
     r in {0, 1, 2, 5, ...}; both storage dtypes.  With a bf16 state the few-token
-    kernel 1 takes its one-batch forms at 1 (N <= 64 at d = 4096), 2 (N = 200) and
-    4 k-steps (the decode workload) and its batch loop (N = 512, below)."""
+    kernel 1 takes its one-batch forms at 1 (N <= 64 at d = 4096), 2 (N = 200,
+    264) and 4 k-steps (the decode workload); at N = 264 (two 16-token groups per
+    wave) the last workgroup's second group is empty."""
     X = inputs.make_gr_inputs(N, n, d, r, dtype, seed=N * 131 + n * 17 + d + r, w_std=0.05,
                               branch_scale=None)
     run_read_write_fused(X, f"N{N}-n{n}-d{d}-r{r}-{dtype}")
@@ -189,13 +190,17 @@ def test_saturating_gate(N, d, r, w_std):
     run_read_write_fused(X, f"saturating-N{N}-d{d}-r{r}")
 
 
-@pytest.mark.parametrize("N,d,r", [(511, 1024, 48), (512, 4096, 64), (896, 1024, 32), (897, 1024, 32),
+@pytest.mark.parametrize("N,d,r", [(100, 4096, 64), (511, 1024, 48), (512, 4096, 64), (600, 8192, 64),
+                                   (512, 4096, 96), (896, 1024, 32), (897, 1024, 32),
                                    (1000, 1024, 32), (1024, 2048, 64), (2065, 1024, 16), (3000, 4096, 64)])
 def test_kernel1_forms_by_token_count(N, d, r):
     """Kernel 1 takes its few-token form with fewer than 8 tiles of 128 tokens
     (N <= 896, n = 4) and the tile walk with channel splits from there, until
     the grid is full; both sides of each switch, ragged tails, every token
-    compared."""
+    compared.  The few-token form takes one 16-token group per wave below 256
+    tokens (N = 100) or with more than 5 row blocks (r = 96), two from there
+    (sharing each W fragment), with its batch loop at N = 600, d = 8192 (two
+    groups) and N = 512, r = 96 (one group)."""
     X = inputs.make_gr_inputs(N, 4, d, r, "bf16", seed=7 * N + d + r, w_std=0.2,
                               branch_scale=(1.0, 0.5, 2.0, 1.0))
     run_read_write_fused(X, f"k1-forms-N{N}-d{d}-r{r}")

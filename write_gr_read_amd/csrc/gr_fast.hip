@@ -78,12 +78,16 @@ FastShape shape_of(const ReadArgs &a) {
     s.k2_chan = c2;
     s.wide = s.row_blocks > kMaxRowBlocks;
     // Few tokens: kernel 1's few-token form (narrow or wide gate), whose workgroups are
-    // (16 tokens, branch, split); splits (a power of two, at most kMaxSplit)
+    // (16 or 32 tokens, branch, split); splits (a power of two, at most kMaxSplit)
     // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
     s.small = 0;
     s.small_kpw = 0;
+    s.small_tg = 1;
     if (s.tiles * s.n < (s.wide ? kSmallBelowWide : kSmallBelow)) {
-        const int64_t groups = (s.N + 15) / 16;
+        // from kSmallTg2From tokens a wave takes two 16-token groups: each W
+        // fragment it loads then serves 32 tokens (half the W reads from L2)
+        s.small_tg = (s.N >= kSmallTg2From && s.row_blocks <= kSmallTg2MaxRB) ? 2 : 1;
+        const int64_t groups = (s.N + 16 * s.small_tg - 1) / (16 * s.small_tg);
         int sp = 1;
         while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
         const int per = kSmallWaves * kChunk * sp;   // channels covered per k-step of every wave

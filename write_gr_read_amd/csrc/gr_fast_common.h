@@ -33,6 +33,8 @@ constexpr int kSmallBelow = 32;           // few-token kernel 1 while (token til
 constexpr int kSmallBelowWide = 16;          // ... for a wide gate
 constexpr int kSmallTarget = 256;         // few-token kernel 1: workgroups wanted before splitting
 constexpr int kSmallWaves = 8;            // waves per few-token kernel-1 workgroup
+constexpr int kSmallTg2From = 256;        // few-token kernel 1: two 16-token groups per wave from this many tokens
+constexpr int kSmallTg2MaxRB = 5;         // ... for gates of at most this many 16-row blocks
 
 struct FastShape {
     int n, d, r, nw;     // nw = n if W_write given, else 0
@@ -50,6 +52,7 @@ struct FastShape {
     int wide;            // r + n beyond 128: kernel 1's wide form (gamma on the state side, no W')
     int small;           // few tokens: kernel 1's few-token form (k_stream_proj_small)
     int small_kpw;       // ... its k-steps (32 channels) per wave
+    int small_tg;        // ... its 16-token groups per wave (1 or 2; they share each W fragment)
     int64_t N, tiles;
 };
 

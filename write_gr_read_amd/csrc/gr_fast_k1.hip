@@ -297,9 +297,11 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 
 // Kernel 1, few-token form.  With few tokens the tile walk above has too few
 // (tile, branch) units to fill the GPU, and each unit is a chain of rounds.
-// Here a workgroup takes 16 tokens of one branch and a split of the channels,
-// one slice of kpw k-steps (32 channels each) per wave, so a wave makes one
-// short pass.  A lane loads its state words straight in the MFMA B layout
+// Here a workgroup takes 16 TG tokens of one branch and a split of the
+// channels, one slice of kpw k-steps (32 channels each) per wave, so a wave
+// makes one short pass.  With TG = 2 (two 16-token groups) every W fragment a
+// wave loads feeds the MFMAs of both groups: half the W reads per token, at
+// twice the splits for the same number of workgroups.  A lane loads its state words straight in the MFMA B layout
 // (token = lane % 16, 8 channels of lane group lane / 16): eq:write, its store
 // and the sum of squares run there, with no LDS tile.  As in the wide form the
 // contraction is P_i = W^{(i)} (gamma_i . R'_i): the raw W_down / W_write rows
@@ -311,14 +313,19 @@ k_stream_proj(typename StateT<F8>::type *__restrict__ state, const bf16_t *__res
 // k-steps loaded together (one batch): four, or one for a wide gate (its
 // NRB W fragments per k-step take 4 NRB VGPRs)
 template <int NRB> constexpr int small_kb() { return NRB <= kMaxRowBlocks ? 4 : 1; }
+// ... in the batch loop, where the loop's state takes registers too: two
+// from 7 row blocks and with two token groups, so that nothing spills
+template <int NRB, int TG> constexpr int small_loop_kb() {
+    return NRB > kMaxRowBlocks ? 1 : (NRB >= 7 || TG > 1 ? 2 : 4);
+}
 constexpr int kSmallPass = kMaxRowBlocks;  // row blocks per pass of the LDS reduction
 // ONEKB > 0: the wave's slice is one batch of at most ONEKB k-steps
 // (decode-sized calls; ONEKB = 1, 2 or 4 as the slice needs, so that no
 // k-step is loaded for nothing): straight-line code, so the compiler counts the
 // loads in flight instead of waiting for all of them before the first element,
 // and does not wait for the stores before the reduction (a loop, or a join
-// with one, makes it do both).  ONEKB = 0: the slice in batches of small_kb.
-template <bool FUSED, int NRB, bool F8, int ONEKB>
+// with one, makes it do both).  ONEKB = 0: the slice in batches of small_loop_kb.
+template <bool FUSED, int NRB, bool F8, int ONEKB, int TG>
 __global__ void __launch_bounds__(64 * kSmallWaves, 2)
 k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t *__restrict__ y,
                     const float *__restrict__ s_in, const bf16_t *__restrict__ gamma,
@@ -326,10 +333,13 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
                     FastShape sh) {
     using T = typename StateT<F8>::type;
     using SV = typename StateT<F8>::vec8;
-    constexpr int kSmallKB = ONEKB > 0 ? ONEKB : small_kb<NRB>();
+    constexpr int kSmallKB = ONEKB > 0 ? ONEKB : small_loop_kb<NRB, TG>();
     constexpr int PB = NRB < kSmallPass ? NRB : kSmallPass;   // row blocks per reduction pass
     constexpr int NPASS = (NRB + PB - 1) / PB;
-    __shared__ float lds_p[kSmallWaves][4 * PB + 1][64];  // per wave: a pass's accumulators, then ss
+    constexpr int ACC = 4 * PB;                                // words per lane, group and pass
+    constexpr int TOKW = 16 * TG;                              // tokens of a workgroup (and of each wave)
+    // per wave: a pass's accumulators of each token group, then the groups' ss
+    __shared__ float lds_p[kSmallWaves][TG * ACC + TG][64];
     const int n = sh.n, d = sh.d, S = sh.ksplit, kpw = sh.small_kpw;
     // blockIdx -> (token group, branch, split) with (branch, split) fastest, so
     // the workgroups reading one slice of W sit on one XCD when n S % 8 == 0
@@ -340,22 +350,34 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, m16 = lane & 15;
-    const int64_t t = tg * 16 + m16;                      // this lane's token (MFMA column)
-    const bool valid = t < sh.N;
     const int64_t nd = (int64_t)n * d;
     const int c_wave = (split * kSmallWaves + wave) * kpw * kChunk;
-    const float sv = (FUSED && valid) ? s_in[t * n + br] : 0.f;
-    T *const srow = state + (t * n + br) * (int64_t)d;
-    const bf16_t *const yrow = FUSED ? y + t * (int64_t)d : nullptr;
-
-    f32x4 acc[NRB];
+    // token group j of the wave: this lane's token (MFMA column) tg TOKW + 16 j + m16
+    bool valid[TG];
+    float sv[TG];
+    T *srow[TG];
+    const bf16_t *yrow[TG];
 #pragma unroll
-    for (int k = 0; k < NRB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
+    for (int j = 0; j < TG; ++j) {
+        const int64_t t = tg * TOKW + 16 * j + m16;
+        valid[j] = t < sh.N;
+        sv[j] = (FUSED && valid[j]) ? s_in[t * n + br] : 0.f;
+        srow[j] = state + (t * n + br) * (int64_t)d;
+        yrow[j] = FUSED ? y + t * (int64_t)d : nullptr;
+    }
+
+    f32x4 acc[TG][NRB];
+    float ss[TG];
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+        ss[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < NRB; ++k) acc[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     // one batch of kSmallKB k-steps starting at k-step kb of the wave's slice
     auto batch = [&](int kb) {
-        SV rr[kSmallKB];
-        u32x4 yy[kSmallKB], gm[kSmallKB], wv[kSmallKB][NRB];
+        SV rr[TG][kSmallKB];
+        u32x4 yy[TG][kSmallKB], gm[kSmallKB], wv[kSmallKB][NRB];
         bool kin[kSmallKB];
         // Every load is issued unconditionally (a masked one reads the start of
         // its tensor) and its value zeroed after: with the loads under
@@ -366,14 +388,17 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
             const int c0 = c_wave + (kb + ks) * kChunk;   // whole 32-channel chunk in or out (d % 32 == 0)
             kin[ks] = kb + ks < kpw && c0 < d;
             const int c = c0 + 8 * g;
-            const bool okr = kin[ks] && valid;
-            const SV rv = *reinterpret_cast<const SV *>(okr ? srow + c : state);
-            rr[ks] = okr ? rv : SV{};
-            if (FUSED) {
-                const u32x4 yv = *reinterpret_cast<const u32x4 *>(okr ? yrow + c : y);
-                yy[ks] = okr ? yv : z4;
-            } else {
-                yy[ks] = z4;
+#pragma unroll
+            for (int j = 0; j < TG; ++j) {
+                const bool okr = kin[ks] && valid[j];
+                const SV rv = *reinterpret_cast<const SV *>(okr ? srow[j] + c : state);
+                rr[j][ks] = okr ? rv : SV{};
+                if (FUSED) {
+                    const u32x4 yv = *reinterpret_cast<const u32x4 *>(okr ? yrow[j] + c : y);
+                    yy[j][ks] = okr ? yv : z4;
+                } else {
+                    yy[j][ks] = z4;
+                }
             }
             const u32x4 gv = *reinterpret_cast<const u32x4 *>(kin[ks] ? gamma + (int64_t)br * d + c : gamma);
             gm[ks] = kin[ks] ? gv : z4;
@@ -390,32 +415,35 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
 #pragma unroll
         for (int ks = 0; ks < kSmallKB; ++ks) {
             const int c = c_wave + (kb + ks) * kChunk + 8 * g;
-            u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
-            if constexpr (F8) {
-                u32x2 o = rr[ks];
-                if (FUSED) {
-                    o = write8_fp8(sv, yy[ks], rr[ks]);
-                    if (valid && kin[ks]) *reinterpret_cast<u32x2 *>(srow + c) = o;
-                }
-                w = widen8_fp8_bf16(o);
-            } else {
-                w = rr[ks];
-                if (FUSED) {
-                    w = write8_bf16(sv, yy[ks], rr[ks]);
-                    if (valid && kin[ks]) *reinterpret_cast<u32x4 *>(srow + c) = w;
-                }
-            }
-            // masked lanes and chunks hold zeros: they add nothing below
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ss = dot2_bf16(w[e], w[e], ss);
-            // B = gamma . R' as bf16 hi + lo (exact fp32 product split once per
-            // k-step); A = the raw W rows
-            u32x4 bh, bl;
-            split_product(w, gm[ks], bh, bl);
+            for (int j = 0; j < TG; ++j) {
+                u32x4 w;  // the 8 stored values as bf16 (exact for an e4m3 state)
+                if constexpr (F8) {
+                    u32x2 o = rr[j][ks];
+                    if (FUSED) {
+                        o = write8_fp8(sv[j], yy[j][ks], rr[j][ks]);
+                        if (valid[j] && kin[ks]) *reinterpret_cast<u32x2 *>(srow[j] + c) = o;
+                    }
+                    w = widen8_fp8_bf16(o);
+                } else {
+                    w = rr[j][ks];
+                    if (FUSED) {
+                        w = write8_bf16(sv[j], yy[j][ks], rr[j][ks]);
+                        if (valid[j] && kin[ks]) *reinterpret_cast<u32x4 *>(srow[j] + c) = w;
+                    }
+                }
+                // masked lanes and chunks hold zeros: they add nothing below
 #pragma unroll
-            for (int k = 0; k < NRB; ++k) {
-                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bh), acc[k], 0, 0, 0);
-                acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bl), acc[k], 0, 0, 0);
+                for (int e = 0; e < 4; ++e) ss[j] = dot2_bf16(w[e], w[e], ss[j]);
+                // B = gamma . R' as bf16 hi + lo (exact fp32 product split once per
+                // k-step); A = the raw W rows, shared by the TG token groups
+                u32x4 bh, bl;
+                split_product(w, gm[ks], bh, bl);
+#pragma unroll
+                for (int k = 0; k < NRB; ++k) {
+                    acc[j][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bh), acc[j][k], 0, 0, 0);
+                    acc[j][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[ks][k]), as_bf16x8(bl), acc[j][k], 0, 0, 0);
+                }
             }
         }
     };
@@ -425,33 +453,40 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
         for (int kb = 0; kb < kpw; kb += kSmallKB) batch(kb);
     }
     // this wave's share of ss per token: the four lane groups hold its channels
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+        ss[j] += __shfl_xor(ss[j], 16, 64);
+        ss[j] += __shfl_xor(ss[j], 32, 64);
+    }
     // add the waves' accumulators in LDS, PB row blocks per pass (ss with the first)
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-        constexpr int ACC = 4 * PB;                       // words per lane and pass
         if (ps > 0) __syncthreads();                      // the previous pass is read
 #pragma unroll
-        for (int k = 0; k < PB; ++k)
+        for (int j = 0; j < TG; ++j) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                if (ps * PB + k < NRB) lds_p[wave][4 * k + m][lane] = acc[ps * PB + k][m];
-        if (ps == 0) lds_p[wave][ACC][lane] = ss;
+            for (int k = 0; k < PB; ++k)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (ps * PB + k < NRB) lds_p[wave][j * ACC + 4 * k + m][lane] = acc[j][ps * PB + k][m];
+            if (ps == 0) lds_p[wave][TG * ACC + j][lane] = ss[j];
+        }
         __syncthreads();
-        // word j of lane l: P row 16(ps PB + j/4) + 4(l/16) + j%4 of token l%16
-        // (j < ACC), ss (j = ACC, first pass)
+        // word j*ACC + q of lane l: P row 16(ps PB + q/4) + 4(l/16) + q%4 of token
+        // 16 j + l%16 (q < ACC); word TG ACC + j: ss of token 16 j + l%16 (first pass)
         const int words = 4 * (ps * PB + PB <= NRB ? PB : NRB - ps * PB);   // P words of this pass
-        for (int v = tid; v < (ACC + 1) * 64; v += 64 * kSmallWaves) {
-            const int j = v >> 6, l = v & 63;
-            const int64_t tt = tg * 16 + (l & 15);
-            const bool is_ss = j == ACC;
-            if (tt >= sh.N || (is_ss ? (ps != 0 || l >= 16) : j >= words)) continue;
+        for (int v = tid; v < (TG * ACC + TG) * 64; v += 64 * kSmallWaves) {
+            const int wi = v >> 6, l = v & 63;
+            const bool is_ss = wi >= TG * ACC;
+            const int jg = is_ss ? wi - TG * ACC : wi / ACC;
+            const int q = wi - jg * ACC;                          // word of the group (P words)
+            const int64_t tt = tg * TOKW + 16 * jg + (l & 15);
+            if (tt >= sh.N || (is_ss ? (ps != 0 || l >= 16) : q >= words)) continue;
             float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][j][l];
+            for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][wi][l];
             float *rec = ws.partial + ((tt * n + br) * S + split) * (int64_t)sh.pstride;
-            rec[is_ss ? 0 : 4 + 16 * (ps * PB + (j >> 2)) + 4 * (l >> 4) + (j & 3)] = sum;
+            rec[is_ss ? 0 : 4 + 16 * (ps * PB + (q >> 2)) + 4 * (l >> 4) + (q & 3)] = sum;
         }
     }
 }
@@ -665,33 +700,46 @@ k_stream_proj_wide(typename StateT<F8>::type *__restrict__ state, const bf16_t *
     }
 }
 
-// The few-token kernel 1 at the batch size its slice needs (see k_stream_proj_small).
-template <bool FUSED, int NRB, bool F8>
-void launch_small(const ReadArgs &a, const FastShape &sh, const Workspace &w, unsigned sgrid, hipStream_t st) {
+// The few-token kernel 1 at the batch size its slice needs and the token
+// groups per wave the shape asks for (see k_stream_proj_small).
+template <bool FUSED, int NRB, bool F8, int TG>
+void launch_small_tg(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
     using T = typename StateT<F8>::type;
     constexpr int KB = small_kb<NRB>();
+    const unsigned sgrid = (unsigned)(((sh.N + 16 * TG - 1) / (16 * TG)) * sh.n * sh.ksplit);
     const dim3 block(64 * kSmallWaves);
     const bf16_t *y = (const bf16_t *)a.y, *gm = (const bf16_t *)a.gamma;
     const bf16_t *wd = (const bf16_t *)a.wd, *ww = (const bf16_t *)a.ww;
     if (sh.small_kpw <= 1) {
-        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 1>), dim3(sgrid), block, 0, st,
+        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 1, TG>), dim3(sgrid), block, 0, st,
                            (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
         return;
     }
     if constexpr (KB >= 4) {
         if (sh.small_kpw <= 2)
-            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 2>), dim3(sgrid), block, 0, st,
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 2, TG>), dim3(sgrid), block, 0, st,
                                (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
         else if (sh.small_kpw <= 4)
-            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 4>), dim3(sgrid), block, 0, st,
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 4, TG>), dim3(sgrid), block, 0, st,
                                (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
         else
-            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0>), dim3(sgrid), block, 0, st,
+            hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0, TG>), dim3(sgrid), block, 0, st,
                                (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
     } else {
-        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0>), dim3(sgrid), block, 0, st,
+        hipLaunchKernelGGL((k_stream_proj_small<FUSED, NRB, F8, 0, TG>), dim3(sgrid), block, 0, st,
                            (T *)a.state, y, a.s_in, gm, wd, ww, w, sh);
     }
+}
+
+template <bool FUSED, int NRB, bool F8>
+void launch_small(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    if constexpr (NRB <= kSmallTg2MaxRB) {
+        if (sh.small_tg == 2) {
+            launch_small_tg<FUSED, NRB, F8, 2>(a, sh, w, st);
+            return;
+        }
+    }
+    launch_small_tg<FUSED, NRB, F8, 1>(a, sh, w, st);
 }
 
 template <bool FUSED, bool F8>
@@ -715,10 +763,9 @@ hipError_t launch_k1(const ReadArgs &a, const FastShape &sh, const Workspace &w,
                            (const bf16_t *)a.wd, (const bf16_t *)a.ww, w, sh);              \
         break;
     if (sh.small) {
-        const unsigned sgrid = (unsigned)(((sh.N + 15) / 16) * sh.n * sh.ksplit);
 #define GR_K1S(NRB)                                                                         \
     case NRB:                                                                               \
-        launch_small<FUSED, NRB, F8>(a, sh, w, sgrid, st);                                  \
+        launch_small<FUSED, NRB, F8>(a, sh, w, st);                                         \
         break;
         switch (sh.row_blocks) {
             GR_K1S(1) GR_K1S(2) GR_K1S(3) GR_K1S(4) GR_K1S(5) GR_K1S(6) GR_K1S(7) GR_K1S(8)
