@@ -14,7 +14,7 @@ namespace fast {
 namespace {
 
 // Kernel 1b: combine the partial records written by kernel 1.  One wave per
-// token, four tokens per workgroup: lanes 0..NB-1 sum the squares over the
+// token, RW tokens per workgroup: lanes 0..NB-1 sum the squares over the
 // splits (rho_i, rms_i; shared by shuffles), and each lane owns outputs
 // j = lane, lane + 64, ...: the split sums of P_i[j] for every branch (lanes
 // read consecutive j: coalesced), rho applied, summed over branches in order.
@@ -24,12 +24,13 @@ namespace {
 //   j < r        z = (1/n) sum_i rho_i P_i[j]  ->  -log2(e) SiLU(z) as (hi, lo)
 //   r <= j < rk  zero padding of the up projection's k-steps
 //   rk + i       s_i = 2 sigmoid((1/n) sum_i' rho_i' P_i'[r + i])  (1 without W_write)
-constexpr int kRedWaves = 4;
-template <int NB, int S, int JO>
-__global__ void __launch_bounds__(64 * kRedWaves)
+// RW waves (tokens) per workgroup: four, or one for few tokens, whose
+// workgroups then spread over all CUs.
+template <int NB, int S, int JO, int RW>
+__global__ void __launch_bounds__(64 * RW)
 k_reduce_records(float *__restrict__ s_out, Workspace ws, FastShape sh, float eps) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * kRedWaves + (threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * RW + (threadIdx.x >> 6);
     if (t >= sh.N) return;  // whole wave
     const int ps = sh.pstride;
     const float inv_n = 1.0f / (float)NB;
@@ -1035,26 +1036,35 @@ constexpr int64_t kWideXcdMinTokens = 8 * 4 * kResTile;
 
 }  // namespace
 
-hipError_t launch_reduce(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
-    const dim3 rgrid((unsigned)((sh.N + kRedWaves - 1) / kRedWaves)), rblock(64 * kRedWaves);
-    // a wide gate's records (more than 128 outputs) with one or two splits: all
-    // of a lane's outputs in one round of loads
-    const bool wide = sh.rk + 4 > 128;
+// one wave per workgroup up to this many tokens (the grid then reaches every CU)
+constexpr int64_t kRedOneWaveBelow = 512;
+
+template <int RW>
+hipError_t launch_reduce_rw(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st, bool wide) {
+    const dim3 rgrid((unsigned)((sh.N + RW - 1) / RW)), rblock(64 * RW);
     switch (sh.ksplit) {
     case 1:
-        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 1, 6>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
-        else hipLaunchKernelGGL((k_reduce_records<4, 1, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 1, 6, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        else hipLaunchKernelGGL((k_reduce_records<4, 1, 2, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
         break;
     case 2:
-        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 2, 6>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
-        else hipLaunchKernelGGL((k_reduce_records<4, 2, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        if (wide) hipLaunchKernelGGL((k_reduce_records<4, 2, 6, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
+        else hipLaunchKernelGGL((k_reduce_records<4, 2, 2, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps);
         break;
-    case 4: hipLaunchKernelGGL((k_reduce_records<4, 4, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 8: hipLaunchKernelGGL((k_reduce_records<4, 8, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
-    case 16: hipLaunchKernelGGL((k_reduce_records<4, 16, 2>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 4: hipLaunchKernelGGL((k_reduce_records<4, 4, 2, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 8: hipLaunchKernelGGL((k_reduce_records<4, 8, 2, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
+    case 16: hipLaunchKernelGGL((k_reduce_records<4, 16, 2, RW>), rgrid, rblock, 0, st, a.s_out, w, sh, a.eps); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
+    // a wide gate's records (more than 128 outputs) with one or two splits: all
+    // of a lane's outputs in one round of loads
+    const bool wide = sh.rk + 4 > 128;
+    if (sh.N <= kRedOneWaveBelow) return launch_reduce_rw<1>(a, sh, w, st, wide);
+    return launch_reduce_rw<4>(a, sh, w, st, wide);
 }
 
 hipError_t launch_kernel2(const ReadArgs &a, const FastShape &sh, const Workspace &w, hipStream_t st) {
