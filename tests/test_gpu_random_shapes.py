@@ -1,0 +1,53 @@
+"""GPU parity on seeded random shapes: read, write and fused write+read of the
+HIP path against the fp64 oracle, whole tensors, through the C ABI.
+
+Seventy per cent of the cases take the fast path's shape class (n = 4, bf16 or
+e4m3 state, d a multiple of 64, r a multiple of 16 up to the wide gate's 320),
+the rest any shape the library accepts (n in 1..8, r from 0, fp32 or bf16
+state).  Token counts sit on and around the kernels' switch points (16-token
+groups, 128-token tiles, the few-token limit at 896), capped so that the oracle
+finishes each case in well under a second; gate weights up to N(0, 0.5), so the
+gate covers its whole range; a quarter of the cases without W_write.  The shape
+list is drawn once, at collection, from a fixed seed: every run checks the same
+cases, and each case's test id names its shape.
+"""
+import random
+
+import pytest
+
+from write_gr_read_amd import inputs
+from test_gpu_parity import gpu_and_library, run_read_write_fused  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+_TOKENS = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 512,
+           513, 767, 896, 897, 1023, 1024, 1500, 2049, 3000]
+
+
+def _cases(seed: int = 20261202, count: int = 60):
+    rng = random.Random(seed)
+    out = []
+    for c in range(count):
+        if rng.random() < 0.7:
+            n = 4
+            d = rng.choice([64, 128, 192, 256, 320, 512, 640, 1024, 1536, 2048, 2560, 4096])
+            r = rng.choice([16, 32, 48, 64, 80, 96, 112, 128, 160, 192, 256, 320])
+            dt = rng.choice(["bf16", "bf16", "fp8"])
+        else:
+            n = rng.choice([1, 2, 3, 4, 5, 8])
+            d = rng.choice([8, 32, 40, 64, 96, 256, 320, 1024])
+            r = rng.choice([0, 1, 2, 5, 16, 33, 64])
+            dt = rng.choice(["bf16", "f32"])
+        N = min(rng.choice(_TOKENS), max(1, min(3000, 6_000_000 // (n * d))))
+        w_std = rng.choice([0.02, 0.05, 0.2, 0.5])
+        with_write = rng.random() < 0.75
+        out.append(pytest.param(c, N, n, d, r, dt, w_std, with_write,
+                                id=f"N{N}-n{n}-d{d}-r{r}-{dt}-w{w_std}-{'write' if with_write else 'nowrite'}"))
+    return out
+
+
+@pytest.mark.parametrize("c,N,n,d,r,dtype,w_std,with_write", _cases())
+def test_random_shape(c, N, n, d, r, dtype, w_std, with_write):
+    X = inputs.make_gr_inputs(N, n, d, r, dtype, seed=5000 + c, w_std=w_std, with_write=with_write,
+                              branch_scale=(1.0, 0.5, 2.0, 1.0) if n == 4 else None)
+    run_read_write_fused(X, f"random case {c}: N={N} n={n} d={d} r={r} {dtype}")
