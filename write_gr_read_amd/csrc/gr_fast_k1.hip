@@ -472,21 +472,33 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
             if (ps == 0) lds_p[wave][TG * ACC + j][lane] = ss[j];
         }
         __syncthreads();
-        // word j*ACC + q of lane l: P row 16(ps PB + q/4) + 4(l/16) + q%4 of token
-        // 16 j + l%16 (q < ACC); word TG ACC + j: ss of token 16 j + l%16 (first pass)
-        const int words = 4 * (ps * PB + PB <= NRB ? PB : NRB - ps * PB);   // P words of this pass
-        for (int v = tid; v < (TG * ACC + TG) * 64; v += 64 * kSmallWaves) {
-            const int wi = v >> 6, l = v & 63;
-            const bool is_ss = wi >= TG * ACC;
-            const int jg = is_ss ? wi - TG * ACC : wi / ACC;
-            const int q = wi - jg * ACC;                          // word of the group (P words)
+        // words j ACC + 4 k + m (m < 4) of lane l: P rows 16(ps PB + k) + 4(l/16) + m
+        // of token 16 j + l%16, consecutive in its record, so a thread sums the
+        // four (waves in order) and stores them as one 16-byte vector; word
+        // TG ACC + j: ss of token 16 j + l%16 (first pass)
+        const int blocks = ps * PB + PB <= NRB ? PB : NRB - ps * PB;   // row blocks of this pass
+        for (int v = tid; v < TG * PB * 64; v += 64 * kSmallWaves) {
+            const int qi = v >> 6, l = v & 63;
+            const int jg = qi / PB, k = qi - jg * PB;
             const int64_t tt = tg * TOKW + 16 * jg + (l & 15);
-            if (tt >= sh.N || (is_ss ? (ps != 0 || l >= 16) : q >= words)) continue;
-            float sum = 0.f;
+            if (tt >= sh.N || k >= blocks) continue;
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][wi][l];
+            for (int w = 0; w < kSmallWaves; ++w)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) sum[m] += lds_p[w][jg * ACC + 4 * k + m][l];
             float *rec = ws.partial + ((tt * n + br) * S + split) * (int64_t)sh.pstride;
-            rec[is_ss ? 0 : 4 + 16 * (ps * PB + (q >> 2)) + 4 * (l >> 4) + (q & 3)] = sum;
+            *reinterpret_cast<f32x4 *>(rec + 4 + 16 * (ps * PB + k) + 4 * (l >> 4)) = sum;
+        }
+        if (ps == 0 && tid < 16 * TG) {
+            const int jg = tid >> 4, l = tid & 15;
+            const int64_t tt = tg * TOKW + 16 * jg + l;
+            if (tt < sh.N) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < kSmallWaves; ++w) sum += lds_p[w][TG * ACC + jg][l];
+                ws.partial[((tt * n + br) * S + split) * (int64_t)sh.pstride] = sum;
+            }
         }
     }
 }
