@@ -80,6 +80,9 @@ FastShape shape_of(const ReadArgs &a) {
     // Few tokens: kernel 1's few-token form (narrow or wide gate), whose workgroups are
     // (16 or 32 tokens, branch, split); splits (a power of two, at most kMaxSplit)
     // until the grid has kSmallTarget workgroups or a wave's slice is one k-step.
+    // With two token groups per wave (86 KB of LDS at 5 row blocks: one
+    // workgroup per CU) the grid stays within kSmallTarget, one round of
+    // workgroups: at 600-896 tokens a second, partial round cost 2-3 us.
     s.small = 0;
     s.small_kpw = 0;
     s.small_tg = 1;
@@ -89,7 +92,12 @@ FastShape shape_of(const ReadArgs &a) {
         s.small_tg = (s.N >= kSmallTg2From && s.row_blocks <= kSmallTg2MaxRB) ? 2 : 1;
         const int64_t groups = (s.N + 16 * s.small_tg - 1) / (16 * s.small_tg);
         int sp = 1;
-        while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
+        if (s.small_tg == 2) {
+            while (groups * s.n * sp * 2 <= kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk)
+                sp *= 2;
+        } else {
+            while (groups * s.n * sp < kSmallTarget && sp < kMaxSplit && s.d / (2 * sp) >= kSmallWaves * kChunk) sp *= 2;
+        }
         const int per = kSmallWaves * kChunk * sp;   // channels covered per k-step of every wave
         s.small = 1;
         s.ksplit = sp;

@@ -362,8 +362,10 @@ k_stream_proj_small(typename StateT<F8>::type *__restrict__ state, const bf16_t 
         const int64_t t = tg * TOKW + 16 * j + m16;
         valid[j] = t < sh.N;
         sv[j] = (FUSED && valid[j]) ? s_in[t * n + br] : 0.f;
-        srow[j] = state + (t * n + br) * (int64_t)d;
-        yrow[j] = FUSED ? y + t * (int64_t)d : nullptr;
+        // rows of a token past the end are never read or written: point at token 0
+        const int64_t tv = valid[j] ? t : 0;
+        srow[j] = state + (tv * n + br) * (int64_t)d;
+        yrow[j] = FUSED ? y + tv * (int64_t)d : nullptr;
     }
 
     f32x4 acc[TG][NRB];
