@@ -41,9 +41,10 @@ k_prep_wprime(const bf16_t *__restrict__ gamma, const bf16_t *__restrict__ wd,
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1.  blockIdx -> (tile, branch) so that the n workgroups of a tile get
-// the same blockIdx % 8 (same XCD under round-robin dispatch: y is shared in
-// that XCD's L2) and consecutive dispatch slots.
+// Kernel 1.  blockIdx -> (tile, branch, split), XCD-aware (blockIdx % 8 is the
+// XCD under round-robin dispatch): the workgroups of a tile that share an XCD
+// share y in its L2, and with four branches an XCD streams the W' of two of
+// them (the mapping is spelled out in the kernel).
 //
 // Memory side: a round covers RC = 128 channels of the wave's 16 tokens.  One
 // load instruction takes 4 tokens x 256 contiguous bytes (16 lanes per token
