@@ -191,11 +191,11 @@ def test_saturating_gate(N, d, r, w_std):
 
 
 @pytest.mark.parametrize("N,d,r", [(100, 4096, 64), (511, 1024, 48), (512, 4096, 64), (600, 8192, 64),
-                                   (512, 4096, 96), (896, 1024, 32), (897, 1024, 32),
+                                   (512, 4096, 96), (896, 1024, 32), (897, 1024, 32), (1025, 1024, 32),
                                    (1000, 1024, 32), (1024, 2048, 64), (2065, 1024, 16), (3000, 4096, 64)])
 def test_kernel1_forms_by_token_count(N, d, r):
     """Kernel 1 takes its few-token form with fewer than 8 tiles of 128 tokens
-    (N <= 896, n = 4) and the tile walk with channel splits from there, until
+    (N <= 1024, n = 4) and the tile walk with channel splits from there, until
     the grid is full; both sides of each switch, ragged tails, every token
     compared.  The few-token form takes one 16-token group per wave below 256
     tokens (N = 100) or with more than 5 row blocks (r = 96), two from there

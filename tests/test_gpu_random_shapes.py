@@ -5,7 +5,7 @@ Seventy per cent of the cases take the fast path's shape class (n = 4, bf16 or
 e4m3 state, d a multiple of 64, r a multiple of 16 up to the wide gate's 320),
 the rest any shape the library accepts (n in 1..8, r from 0, fp32 or bf16
 state).  Token counts sit on and around the kernels' switch points (16-token
-groups, 128-token tiles, the few-token limit at 896), capped so that the oracle
+groups, 128-token tiles, the few-token limit at 1024), capped so that the oracle
 finishes each case in well under a second; gate weights up to N(0, 0.5), so the
 gate covers its whole range; a quarter of the cases without W_write.  The shape
 list is drawn once, at collection, from a fixed seed: every run checks the same

@@ -29,7 +29,7 @@ constexpr int kMaxWideRKS = 10;           // wide gate: r up to 320 (k-steps of 
 constexpr int kChanPerWg = 256;           // channels per k_gate_combine workgroup
 constexpr int kSplitTarget = 256;         // kernel-1 workgroups wanted before splitting channels
 constexpr int kMaxSplit = 16;             // channel splits of kernel 1 (a power of two)
-constexpr int kSmallBelow = 32;           // few-token kernel 1 while (token tiles) x n is below this
+constexpr int kSmallBelow = 36;           // few-token kernel 1 while (token tiles) x n is below this (n = 4: N <= 1024)
 constexpr int kSmallBelowWide = 16;          // ... for a wide gate
 constexpr int kSmallTarget = 256;         // few-token kernel 1: workgroups wanted before splitting
 constexpr int kSmallWaves = 8;            // waves per few-token kernel-1 workgroup
