@@ -96,7 +96,7 @@ def test_shapes(N, n, d, r, dtype):
 @pytest.mark.parametrize("N,n,d,r", [
     (37, 4, 256, 16), (1, 4, 4096, 64), (5, 1, 64, 0), (17, 3, 64, 5), (70, 4, 512, 32),
     (130, 4, 1024, 48), (300, 4, 192, 32), (129, 4, 384, 96), (257, 4, 320, 128), (64, 4, 256, 0),
-    (256, 4, 4096, 64),
+    (256, 4, 4096, 64), (1024, 4, 4096, 64),
 ])
 @pytest.mark.parametrize("path", ["default", "generic"])
 def test_fp8_state_shapes(N, n, d, r, path, monkeypatch):
@@ -105,7 +105,8 @@ def test_fp8_state_shapes(N, n, d, r, path, monkeypatch):
     u at the bf16 tolerance).  "default" takes the MFMA kernels wherever the
     shape allows (n = 4, r a multiple of 16, d a multiple of 64), including a
     last channel range of one 64-channel unit (d = 192, 320), every k-step
-    count of the up projection and the few-token kernel 1;
+    count of the up projection and the few-token kernel 1 (at N = 1024, its
+    largest size, ahead of the resident kernel 2);
     "generic" forces the shape-generic kernels on the same shapes."""
     if path == "generic":
         monkeypatch.setenv("GR_KERNEL_VARIANT", "generic")
